@@ -1,0 +1,309 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself.
+
+Sources: page "MiniMax-01: Scaling Foundation Models with Lightning Attention |
+Summary", section 2.2 (reordered Q(K^T V) form, causal cumulative state,
+tiles = intra masked term + inter state term, no normalisation/SiLU/gating)
+and section 3.2 (LASP+: local prefix summaries combined into global
+prefixes).  The pages print no worked numbers, so the pins are a hand-worked
+example, closed forms, textbook routines (cumulative sum, a first-order IIR
+filter), identities and brute force -- chosen so that a dropped term, a wrong
+exponent, a transposed state or a read-before-update fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny():
+    w = synth.WORKLOADS["tiny"]
+    q = synth.generate(synth.Q, w.seed, w.d, nh=w.heads, nt=w.n)
+    k = synth.generate(synth.K, w.seed, w.d, nh=w.heads, nt=w.n)
+    v = synth.generate(synth.V, w.seed, w.d, nh=w.heads, nt=w.n)
+    return q, k, v, w.slopes().astype(np.float64)
+
+
+def _rel(a, b):
+    return np.abs(a - b).max() / max(np.abs(b).max(), 1e-300)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_splitmix64_published_sequence():
+    # SplitMix64 seeded with 0 (Steele, Lea & Flood 2014) -- its first four outputs, as published
+    # with the reference xoshiro seeding code.
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+    gamma = 0x9E3779B97F4A7C15
+    got = [synth.splitmix64_next((i * gamma) % 2**64) for i in range(4)]
+    assert got == want
+
+
+def test_generator_moments_and_slices():
+    z = synth.generate(synth.V, 11, 128, nh=4, nt=4096)
+    x = synth.generate(synth.Q, 11, 128, nh=4, nt=4096)
+    assert abs(z.mean()) < 0.01 and abs(z.var() - 1.0) < 0.01
+    # E[SiLU(z)] = 0.2066, E[SiLU(z)^2] = 0.3558 for z ~ N(0,1) (numerical integration below)
+    t = np.linspace(-12, 12, 200001)
+    pdf = np.exp(-t * t / 2) / math.sqrt(2 * math.pi)
+    silu = t / (1 + np.exp(-t))
+    m1 = np.trapezoid(silu * pdf, t)
+    m2 = np.trapezoid(silu * silu * pdf, t)
+    assert abs(x.mean() - m1) < 0.005 and abs((x.astype(np.float64) ** 2).mean() - m2) < 0.005
+    # counter-based: any slice regenerates exactly
+    part = synth.generate(synth.Q, 11, 128, h0=2, nh=1, t0=1000, nt=77)
+    assert np.array_equal(part[0, 0], x[0, 2, 1000:1077])
+    # bf16 bits are the RNE rounding of the float32 values
+    xb = synth.generate(synth.Q, 11, 128, nh=4, nt=64, dtype="bf16")
+    assert np.array_equal(xb, synth.f32_to_bf16_bits(x[:, :, :64]))
+
+
+def test_bf16_rounding_rule():
+    vals = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-9, -2.5, 0.0], dtype=np.float32)
+    bits = synth.f32_to_bf16_bits(vals)
+    back = synth.bf16_bits_to_f32(bits)
+    # 1+2^-8 is a tie between 1 and 1+2^-7 -> even (1); 1+3*2^-8 ties to 1+2^-6 (even mantissa)
+    assert back.tolist() == [1.0, 1.0, 1.0 + 2**-6, 1.0, -2.5, 0.0]
+
+
+# ---------------------------------------------------------------- hand-worked example
+
+def test_hand_worked_example_all_forms():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_d2_n3.json")))
+    q = np.array(g["q"], dtype=np.float32)[None, None]
+    k = np.array(g["k"], dtype=np.float32)[None, None]
+    v = np.array(g["v"], dtype=np.float32)[None, None]
+    s = np.array([g["slope"]])
+    kv_in = np.array(g["kv_in"], dtype=np.float64)[None, None]
+    for kin, o_want, kv_want in ((None, g["o_zero_state"], g["kv_zero_state"]),
+                                 (kv_in, g["o_with_state"], g["kv_with_state"])):
+        o_r, kv_r, _ = oracle.recurrent(q, k, v, s, kv_in=kin)
+        o_q, kv_q = oracle.quadratic(q, k, v, s, kv_in=kin)
+        np.testing.assert_allclose(o_r[0, 0], o_want, atol=1e-12)
+        np.testing.assert_allclose(kv_r[0, 0], kv_want, atol=1e-12)
+        np.testing.assert_allclose(o_q[0, 0], o_want, atol=1e-12)
+        np.testing.assert_allclose(kv_q[0, 0], kv_want, atol=1e-12)
+        for blk in (1, 2, 3, 5):
+            o_b, kv_b = oracle.blocked(q, k, v, s, blk, kv_in=kin)
+            np.testing.assert_allclose(o_b[0, 0], o_want, atol=1e-12)
+            np.testing.assert_allclose(kv_b[0, 0], kv_want, atol=1e-12)
+        kv = np.zeros((1, 1, 2, 2)) if kin is None else kin.copy()
+        for t in range(3):
+            o_t = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], s, kv)
+            np.testing.assert_allclose(o_t[0, 0], o_want[t], atol=1e-12)
+        np.testing.assert_allclose(kv[0, 0], kv_want, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P1: forms agree
+
+@pytest.mark.parametrize("block", [1, 7, 64, 256, 512])
+def test_p1_recurrent_quadratic_blocked_agree(block):
+    q, k, v, s = _tiny()
+    o_r, kv_r, _ = oracle.recurrent(q, k, v, s)
+    o_q, kv_q = oracle.quadratic(q, k, v, s)
+    o_b, kv_b = oracle.blocked(q, k, v, s, block)
+    assert _rel(o_q, o_r) < 1e-12 and _rel(kv_q, kv_r) < 1e-12
+    assert _rel(o_b, o_r) < 1e-12 and _rel(kv_b, kv_r) < 1e-12
+
+
+def test_p1_with_incoming_state_and_ragged_tail():
+    q, k, v, s = _tiny()
+    N = 301  # not a multiple of any block below
+    q, k, v = q[:, :, :N], k[:, :, :N], v[:, :, :N]
+    rng = np.random.default_rng(7)
+    kv_in = rng.standard_normal((1, 2, 64, 64))
+    o_r, kv_r, _ = oracle.recurrent(q, k, v, s, kv_in=kv_in)
+    o_q, kv_q = oracle.quadratic(q, k, v, s, kv_in=kv_in)
+    assert _rel(o_q, o_r) < 1e-12 and _rel(kv_q, kv_r) < 1e-12
+    for block in (7, 64, 256):
+        o_b, kv_b = oracle.blocked(q, k, v, s, block, kv_in=kv_in)
+        assert _rel(o_b, o_r) < 1e-12 and _rel(kv_b, kv_r) < 1e-12
+
+
+# ---------------------------------------------------------------- P2: no decay = cumulative sum
+
+def test_p2_no_decay_is_cumulative_sum_attention():
+    q, k, v, _ = _tiny()
+    q, k, v = q[:, :1, :200], k[:, :1, :200], v[:, :1, :200]
+    s = np.array([0.0])
+    o, kv, _ = oracle.recurrent(q, k, v, s)
+    outer = np.einsum("ti,tj->tij", k[0, 0].astype(np.float64), v[0, 0].astype(np.float64))
+    states = np.cumsum(outer, axis=0)
+    want = np.einsum("ti,tij->tj", q[0, 0].astype(np.float64), states)
+    assert _rel(o[0, 0], want) < 1e-12
+    assert _rel(kv[0, 0], states[-1]) < 1e-12
+
+
+# ---------------------------------------------------------------- P3: d = 1 is a first-order IIR filter
+
+def test_p3_scalar_case_is_first_order_filter():
+    rng = np.random.default_rng(3)
+    N = 1000
+    q = rng.standard_normal((1, 1, N, 1)).astype(np.float32)
+    k = rng.standard_normal((1, 1, N, 1)).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, 1)).astype(np.float32)
+    s = 0.01
+    lam = math.exp(-s)
+    o, kv, _ = oracle.recurrent(q, k, v, np.array([s]))
+    y = scipy.signal.lfilter([1.0], [1.0, -lam], (k.astype(np.float64) * v.astype(np.float64)).ravel())
+    want = q.astype(np.float64).ravel() * y
+    assert _rel(o.ravel(), want) < 1e-12
+    assert abs(kv.ravel()[0] - y[-1]) <= 1e-12 * abs(y[-1])
+
+
+# ---------------------------------------------------------------- P4: impulse
+
+def test_p4_impulse_response():
+    rng = np.random.default_rng(4)
+    N, d, src = 300, 16, 37
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    k = np.zeros((1, 1, N, d), dtype=np.float32)
+    v = np.zeros((1, 1, N, d), dtype=np.float32)
+    k[0, 0, src] = rng.standard_normal(d)
+    v[0, 0, src] = rng.standard_normal(d)
+    s = 0.05
+    o, kv, _ = oracle.recurrent(q, k, v, np.array([s]))
+    t = np.arange(N)
+    qk = q[0, 0].astype(np.float64) @ k[0, 0, src].astype(np.float64)
+    want = np.where(t >= src, np.exp(-s * np.maximum(t - src, 0)), 0.0)[:, None] * qk[:, None] \
+        * v[0, 0, src].astype(np.float64)[None, :]
+    np.testing.assert_allclose(o[0, 0], want, rtol=1e-12, atol=1e-300)
+    kv_want = math.exp(-s * (N - 1 - src)) * np.outer(k[0, 0, src].astype(np.float64), v[0, 0, src].astype(np.float64))
+    np.testing.assert_allclose(kv[0, 0], kv_want, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- P5: single token
+
+def test_p5_single_token_closed_form():
+    rng = np.random.default_rng(5)
+    d = 32
+    q, k, v = (rng.standard_normal((1, 1, 1, d)).astype(np.float32) for _ in range(3))
+    kv_in = rng.standard_normal((1, 1, d, d))
+    s = 0.3
+    o, kv, _ = oracle.recurrent(q, k, v, np.array([s]), kv_in=kv_in)
+    q64, k64, v64 = (x.astype(np.float64)[0, 0, 0] for x in (q, k, v))
+    kv_want = math.exp(-s) * kv_in[0, 0] + np.outer(k64, v64)
+    np.testing.assert_allclose(kv[0, 0], kv_want, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 0], q64 @ kv_want, rtol=1e-13)
+    o0, kv0, _ = oracle.recurrent(q, k, v, np.array([s]))
+    np.testing.assert_allclose(o0[0, 0, 0], (q64 @ k64) * v64, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- P6: continuation, checkpoints, decode
+
+def test_p6_continuation_and_checkpoints_and_decode():
+    q, k, v, s = _tiny()
+    N1 = 200
+    o, kv, ck = oracle.recurrent(q, k, v, s, ckpt_every=100)
+    o1, kv1, _ = oracle.recurrent(q[:, :, :N1], k[:, :, :N1], v[:, :, :N1], s)
+    o2, kv2, _ = oracle.recurrent(q[:, :, N1:], k[:, :, N1:], v[:, :, N1:], s, kv_in=kv1)
+    assert _rel(np.concatenate([o1, o2], axis=2), o) < 1e-12 and _rel(kv2, kv) < 1e-12
+    assert ck.shape[2] == 5
+    assert _rel(ck[:, :, 1], kv1) < 1e-12
+    assert _rel(ck[:, :, 4], oracle.recurrent(q[:, :, :500], k[:, :, :500], v[:, :, :500], s, want_o=False)[1]) < 1e-12
+    state = kv1.copy()
+    for t in range(N1, N1 + 40):
+        ot = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], s, state)
+        assert _rel(ot, o[:, :, t]) < 1e-12
+    ref = oracle.recurrent(q[:, :, :N1 + 40], k[:, :, :N1 + 40], v[:, :, :N1 + 40], s, want_o=False)[1]
+    assert _rel(state, ref) < 1e-12
+
+
+# ---------------------------------------------------------------- P7: LASP+ prefixes
+
+@pytest.mark.parametrize("chunks", [[512], [256, 256], [100, 200, 212], [64] * 8, [1, 510, 1]])
+def test_p7_lasp_plus_combine_equals_serial(chunks):
+    q, k, v, s = _tiny()
+    rng = np.random.default_rng(8)
+    kv_in = rng.standard_normal((1, 2, 64, 64))
+    o, kv, _ = oracle.recurrent(q, k, v, s, kv_in=kv_in)
+    S = oracle.chunk_local_states(k, v, s, chunks)
+    P = oracle.lasp_plus_prefixes(S, s, chunks, kv_in=kv_in)
+    assert _rel(P[:, :, -1], kv) < 1e-12
+    start = 0
+    for j, C in enumerate(chunks):
+        oj, kvj, _ = oracle.recurrent(q[:, :, start:start + C], k[:, :, start:start + C],
+                                      v[:, :, start:start + C], s, kv_in=P[:, :, j])
+        assert _rel(oj, o[:, :, start:start + C]) < 1e-11
+        assert _rel(kvj, P[:, :, j + 1]) < 1e-12
+        start += C
+
+
+# ---------------------------------------------------------------- P8: linearity (no hidden normalisation)
+
+def test_p8_linearity():
+    q, k, v, s = _tiny()
+    q, k, v = q[:, :, :128], k[:, :, :128], v[:, :, :128]
+    rng = np.random.default_rng(9)
+    v2 = rng.standard_normal(v.shape).astype(np.float32)
+    a, b = 0.75, -2.0
+    o1 = oracle.recurrent(q, k, v, s)[0]
+    o2 = oracle.recurrent(q, k, v2, s)[0]
+    o12 = oracle.recurrent(q, k, (a * v.astype(np.float64) + b * v2).astype(np.float32), s)[0]
+    # a*v + b*v2 rounded to float32 -> compare against the same rounded input via linearity on exact parts
+    vmix = (a * v.astype(np.float64) + b * v2).astype(np.float32)
+    o_lin = oracle.recurrent(q, k, vmix, s)[0]
+    assert _rel(o12, o_lin) == 0.0
+    assert _rel(o12, a * o1 + b * o2) < 1e-6  # the only gap is the float32 rounding of vmix
+    o_scaled = oracle.recurrent((4.0 * q).astype(np.float32), k, v, s)[0]  # power of two: exact
+    assert _rel(o_scaled, 4.0 * o1) < 1e-13
+
+
+# ---------------------------------------------------------------- P9: windowing (long-context spot checks)
+
+def test_p9_window_restart_bound():
+    rng = np.random.default_rng(10)
+    N, d, W = 12000, 8, 8192
+    s = 2.0 ** -8
+    q, k, v = (rng.standard_normal((1, 1, N, d)).astype(np.float32) for _ in range(3))
+    o, kv, _ = oracle.recurrent(q, k, v, np.array([s]))
+    t0 = N - 500
+    ow, kvw, _ = oracle.recurrent(q[:, :, t0 - W:], k[:, :, t0 - W:], v[:, :, t0 - W:], np.array([s]))
+    bound = math.exp(-s * W)  # relative size of everything before the window
+    assert bound < 2e-14
+    assert _rel(ow[:, :, W:], o[:, :, t0:]) < 50 * bound
+    assert _rel(kvw, kv) < 50 * bound
+
+
+# ---------------------------------------------------------------- the pins catch planted mistakes
+
+def _mutant_recurrent(q, k, v, s, kind):
+    """Deliberately wrong variants, to show each is caught by the hand-worked example."""
+    q, k, v = (np.asarray(x, dtype=np.float64)[0, 0] for x in (q, k, v))
+    lam = math.exp(-s)
+    KV = np.zeros((q.shape[1], q.shape[1]))
+    out = []
+    for t in range(q.shape[0]):
+        prev = KV.copy()
+        if kind == "no_decay":
+            KV = KV + np.outer(k[t], v[t])
+        elif kind == "transposed_state":
+            KV = lam * KV + np.outer(v[t], k[t])
+        else:
+            KV = lam * KV + np.outer(k[t], v[t])
+        if kind == "read_before_update":
+            out.append(q[t] @ prev)
+        elif kind == "double_decay_on_read":
+            out.append(lam * (q[t] @ KV))
+        else:
+            out.append(q[t] @ KV)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("kind", ["no_decay", "transposed_state", "read_before_update", "double_decay_on_read"])
+def test_planted_mistakes_are_caught(kind):
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_d2_n3.json")))
+    q = np.array(g["q"], dtype=np.float32)[None, None]
+    k = np.array(g["k"], dtype=np.float32)[None, None]
+    v = np.array(g["v"], dtype=np.float32)[None, None]
+    got = _mutant_recurrent(q, k, v, g["slope"], kind)
+    assert np.abs(got - np.array(g["o_zero_state"])).max() > 0.1
+    ok = _mutant_recurrent(q, k, v, g["slope"], "correct")
+    np.testing.assert_allclose(ok, g["o_zero_state"], atol=1e-12)
