@@ -1,0 +1,242 @@
+"""Benchmark: Lightning Attention prefill and decode on one MI355X.
+
+Workload of the headline number: full-layer prefill, batch 1, 64 heads, head dim 128,
+131072 tokens, bf16 Q/K/V/O, fp32 state (the 64-head d=128 lightning layer of the
+MiniMax-01 pages at 128K context), seeded synthetic activations.  One step = one
+la_prefill over that batch (tile scores, masking, intra/inter terms, state
+recurrence, output write, final state).  The decode leg times 1000 consecutive
+la_decode steps on 128 sequences x 64 heads whose states were preloaded from a
+4096-token seeded prefix; it is reported as "decode" in the same JSON line.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+MODEL_TILE = 256               # the pages' tile: flop model 4*B*d + 4*d^2 per token-head
+BYTES_PER_TOKEN_HEAD = 4 * 128 * 2   # q, k, v read + o write, bf16, d = 128
+DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 4 * 128 * 2   # state read + write, q/k/v/o
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def model_flops_per_token_head(d=128, B=MODEL_TILE):
+    return 4 * B * d + 4 * d * d
+
+
+def upload_bf16(bits, device):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def make_prefill_inputs(w, device, head_group=8):
+    import torch
+
+    import synth
+
+    shape = (w.batch, w.heads, w.n, w.d)
+    out = []
+    for t in (synth.Q, synth.K, synth.V):
+        dev = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for h0 in range(0, w.heads, head_group):
+            nh = min(head_group, w.heads - h0)
+            bits = synth.generate(t, w.seed, w.d, nb=w.batch, h0=h0, nh=nh, nt=w.n, dtype="bf16")
+            dev[:, h0:h0 + nh] = upload_bf16(bits, device)
+        out.append(dev)
+    return out
+
+
+def time_prefill(w, steps, warmup, device):
+    import torch
+
+    import long_context_la_amd as la
+
+    log(f"generating {w.name} inputs {w.batch}x{w.heads}x{w.n}x{w.d} bf16")
+    t0 = time.time()
+    q, k, v = make_prefill_inputs(w, device)
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+    slopes = torch.from_numpy(w.slopes()).to(device)
+    kv = torch.zeros(w.batch, w.heads, w.d, w.d, dtype=torch.float32, device=device)
+    o = torch.empty_like(q)
+    ws_bytes = la.la_prefill_workspace_size(la.LA_BF16, w.batch, w.heads, w.n, w.d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def step():
+        la.la_state_init(kv)
+        la.la_prefill(q, k, v, slopes, kv, o=o, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    # the prefill kernel alone (state init excluded), timed on the same stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        la.la_state_init(kv)
+        a.record(stream)
+        la.la_prefill(q, k, v, slopes, kv, o=o, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    n_chunks = -(-w.n // la.la_prefill_chunk_tokens(la.LA_BF16, w.batch, w.heads, w.n, w.d))
+    del q, k, v, o, ws
+    return ms, kernel_ms, n_chunks
+
+
+def time_decode(w, steps, device, prefix_slab=16):
+    import torch
+
+    import long_context_la_amd as la
+    import synth
+
+    B, H, d, P = w.batch, w.heads, w.d, w.n
+    slopes = torch.from_numpy(w.slopes()).to(device)
+    kv = torch.empty(B, H, d, d, dtype=torch.float32, device=device)
+    la.la_state_init(kv)
+    log(f"decode: preloading {B}x{H} states from a {P}-token prefix")
+    t0 = time.time()
+    for b0 in range(0, B, prefix_slab):
+        nb = min(prefix_slab, B - b0)
+        kk = upload_bf16(synth.generate(synth.K, w.seed, d, b0=b0, nb=nb, nh=H, nt=P, dtype="bf16"), device)
+        vv = upload_bf16(synth.generate(synth.V, w.seed, d, b0=b0, nb=nb, nh=H, nt=P, dtype="bf16"), device)
+        la.la_prefill(kk, kk, vv, slopes, kv[b0:b0 + nb], o=None)  # state only: q is not read
+        del kk, vv
+    torch.cuda.synchronize()
+    log(f"decode: prefix done in {time.time() - t0:.1f} s; generating {steps} step tokens")
+    toks = []
+    for t in (synth.Q, synth.K, synth.V):
+        bits = synth.generate(t, w.seed, d, nb=B, nh=H, t0=P, nt=steps, dtype="bf16")  # [B,H,steps,d]
+        toks.append(upload_bf16(np.ascontiguousarray(bits.transpose(2, 0, 1, 3)), device))  # [steps,B,H,d]
+    o = torch.empty(B, H, d, dtype=torch.bfloat16, device=device)
+    stream = torch.cuda.current_stream(device)
+    # warm-up on a scratch copy of the state so the timed run starts from the preloaded one
+    scratch = kv.clone()
+    for s in range(3):
+        la.la_decode(toks[0][s], toks[1][s], toks[2][s], slopes, scratch, o)
+    del scratch
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(steps):
+        la.la_decode(toks[0][s], toks[1][s], toks[2][s], slopes, kv, o)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / steps
+    return us
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The fp64 oracle (token recurrence, OpenMP over heads) on the host cores, on a bounded
+    sample of the workload: all heads, the first T tokens, T sized to ~target_s of CPU work."""
+    import oracle
+    import synth
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+
+    def run(T):
+        ex = [synth.bf16_bits_to_f32(synth.generate(t, w.seed, w.d, nb=w.batch, nh=w.heads, nt=T, dtype="bf16"))
+              for t in (synth.Q, synth.K, synth.V)]
+        t0 = time.perf_counter()
+        oracle.recurrent(*ex, w.slopes())
+        return time.perf_counter() - t0
+
+    T = 256
+    dt = run(T)
+    T = int(min(w.n, max(256, T * target_s / max(dt, 1e-3))) // 256 * 256)
+    dt = run(T)
+    return {"value": w.batch * T / dt, "unit": "tokens/s", "cores": min(cores, w.batch * w.heads),
+            "kind": "oracle",
+            "sample": f"all {w.heads} heads x first {T} tokens of the {w.n}-token workload "
+                      f"(fp64 recurrence, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="full", choices=["full", "share", "long"])
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences would "
+              "shard across GPUs with no or one small exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_la_amd as la
+    import synth
+
+    la.lib()
+    device = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    ms, kernel_ms, n_chunks = time_prefill(w, args.steps, args.warmup, device)
+    token_heads = w.batch * w.heads * w.n
+    tokens_s = w.batch * w.n / (ms * 1e-3)
+    flops = model_flops_per_token_head(w.d) * token_heads
+    alg_bytes = BYTES_PER_TOKEN_HEAD * token_heads
+    log(f"prefill {w.name}: {ms:.3f} ms/step, kernel(s) {kernel_ms:.3f} ms, {n_chunks} chunk(s)")
+    result = {
+        "metric": "prefill tokens/s (all heads, d=128) + % MFMA roofline; decode GB/s",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller activations, SiLU on Q/K)",
+        "config": {"workload": f"{w.name} prefill: batch {w.batch}, {w.heads} heads, d={w.d}, N={w.n}, "
+                               f"bf16 q/k/v/o, fp32 state, per-head decay",
+                   "global_batch": w.batch, "seq_len": w.n, "heads": w.heads, "head_dim": w.d},
+        "model_tflops": flops / (ms * 1e-3) / 1e12,
+        "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": alg_bytes / (kernel_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None},
+    }
+    if not args.no_decode:
+        wd = synth.WORKLOADS["decode"]
+        us = time_decode(wd, args.decode_steps, device)
+        gbs = wd.batch * wd.heads * DECODE_BYTES_PER_UNIT / (us * 1e-6) / 1e9
+        log(f"decode: {us:.1f} us/step, {gbs:.0f} GB/s")
+        result["decode"] = {"workload": f"{wd.batch} seqs x {wd.heads} heads, d={wd.d}, prefix {wd.n}, "
+                                        f"{args.decode_steps} steps", "us_per_step": us, "GB/s": gbs,
+                            "frac": gbs / PEAK_HBM_GBS}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,145 @@
+/*
+ * la.h -- C ABI of the MI355X (gfx950) Lightning Attention library
+ * (liblightning_la.so).
+ *
+ * The operation: causal linear attention with a per-head exponential decay,
+ * evaluated tile by tile with a d x d key-value state carried across tiles --
+ * the "lightning attention" of the page "MiniMax-01: Scaling Foundation Models
+ * with Lightning Attention | Summary", section 2.2 (Linear Attention): the
+ * product is reordered to Q(K^T V) so no n x n matrix is formed, each tile
+ * takes a masked intra-tile term plus a term from the accumulated state of
+ * earlier tiles, then the state is updated; normalisation, SiLU and gating
+ * are not part of it.  With lambda_h = exp(-slopes[h]) and, per (batch,
+ * head), KV_{-1} = the incoming state:
+ *
+ *     KV_t = lambda_h * KV_{t-1} + k_t^T v_t        KV[i][j]: i = key dim, j = value dim
+ *     o_t  = q_t . KV_t
+ *
+ * equivalently O = [(Q K^T) (.) M] V + diag(lambda^(t+1)) Q KV_{-1} with
+ * M[t][s] = lambda^(t-s) for s <= t and 0 otherwise.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory and keeps no state between calls other than
+ *     a thread-local error string.
+ *   - Every call only enqueues work on `stream` (a hipStream_t passed as void*,
+ *     NULL = the default stream) and returns; device-side faults appear at the
+ *     caller's next synchronisation.
+ *   - The return value reports argument validation and launch errors.  Invalid
+ *     arguments are rejected before any HIP call.  With no usable GPU the call
+ *     returns LA_ERR_DEVICE (it never aborts).  No C++ exception crosses the ABI.
+ *   - The KV state is always float32, [batch][heads][d][d], row i = key dim.
+ *   - Results are deterministic: the same inputs on the same device give the
+ *     same bits (no floating-point atomics).
+ */
+#ifndef LIGHTNING_LA_H
+#define LIGHTNING_LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad stride/alignment */
+    LA_ERR_UNSUPPORTED = 2,      /* valid request outside the supported matrix (d, dtype, ckpt_every) */
+    LA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than the queried size */
+    LA_ERR_DEVICE = 4,           /* no GPU, or a HIP runtime error */
+    LA_ERR_INTERNAL = 5
+} la_status;
+
+typedef enum {
+    LA_F32 = 0,  /* q, k, v, o are float32 */
+    LA_BF16 = 1  /* q, k, v, o are bfloat16; accumulation and state are float32 */
+} la_dtype;
+
+/*
+ * kv[batch][heads][d][d] (float32) := 0 when kv0 == NULL, else a copy of kv0
+ * (same layout; kv0 may not overlap kv).  The state a prefill or decode
+ * starts from, e.g. a cached prefix (section 3 of the page above reuses the
+ * computation of earlier input segments).  d in {64, 128}.
+ */
+la_status la_state_init(float* kv, const float* kv0, int64_t batch, int64_t heads, int64_t d,
+                        void* stream);
+
+/*
+ * Tokens per sequence chunk that la_prefill uses for this shape.  Chunks are
+ * the single-GPU form of LASP+ (section 3.2 of the page above: local prefix
+ * summaries, combined into global prefixes): each chunk's local state is
+ * computed from a zero state, the prefixes are combined, and every chunk then
+ * runs from its own prefix, so a long sequence fills all compute units.  The
+ * result equals the serial recurrence.  Returns n when one chunk is used, a
+ * positive multiple of 64 otherwise, or -1 for invalid shapes.
+ */
+int64_t la_prefill_chunk_tokens(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d);
+
+/* Bytes of device workspace la_prefill needs for this shape (0 when it needs none). */
+size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d);
+
+/*
+ * Prefill: for every (b, h), run tokens 0..n-1 starting from the state in
+ * kv[b][h], write o (unless o == NULL: state only) and leave in kv[b][h] the
+ * state after token n-1.
+ *   q, k, v, o : element (b, h, t, e) at base + b*stride_b + h*stride_h +
+ *                t*stride_n + e (strides in elements, shared by all four;
+ *                the last dimension is contiguous).  q, k, v are read-only and
+ *                may alias each other; o must not overlap q, k, v or kv.
+ *                Pointers 16-byte aligned; strides multiples of 8 elements
+ *                (bf16) or 4 (f32); stride_n >= d.
+ *   slopes     : [heads] float32 device array, s_h >= 0 and finite
+ *                (documented, not checked: reading it would need a sync);
+ *                lambda_h = exp(-s_h).
+ *   kv         : [batch][heads][d][d] float32, read then overwritten.
+ *   ckpt       : NULL, or [batch][heads][n / ckpt_every][d][d] float32 that
+ *                receives the state after token (m+1)*ckpt_every - 1 in slot m.
+ *                ckpt_every must be a positive multiple of 64.
+ *   workspace  : device scratch of at least la_prefill_workspace_size() bytes
+ *                (may be NULL when that size is 0); contents are clobbered.
+ * Supported: LA_F32 with d in {64, 128}; LA_BF16 with d = 128.  n == 0 is a
+ * no-op that leaves kv unchanged.
+ */
+la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                     int64_t batch, int64_t heads, int64_t n, int64_t d,
+                     int64_t stride_b, int64_t stride_h, int64_t stride_n,
+                     const float* slopes, float* kv, float* ckpt, int64_t ckpt_every,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As la_prefill with an explicit chunk length: chunk_tokens == 0 picks the
+ * default (la_prefill_chunk_tokens), otherwise it must be a positive multiple
+ * of 64 (values >= n mean one chunk).  The workspace must hold
+ * la_prefill_workspace_size_ex() bytes for the same chunk_tokens.
+ */
+size_t la_prefill_workspace_size_ex(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d,
+                                    int64_t chunk_tokens);
+la_status la_prefill_ex(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                        int64_t batch, int64_t heads, int64_t n, int64_t d,
+                        int64_t stride_b, int64_t stride_h, int64_t stride_n,
+                        const float* slopes, float* kv, float* ckpt, int64_t ckpt_every,
+                        int64_t chunk_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step per (b, h) (section 3.3 of the page above runs single-token
+ * generation as its own kernel): kv <- lambda_h * kv + k^T v, then o = q . kv.
+ *   q, k, v, o : contiguous [batch][heads][d] of dtype dt (o must not overlap
+ *                q, k, v or kv); slopes [heads] float32; kv [batch][heads][d][d]
+ *                float32 updated in place.  d in {64, 128}; both dtypes.
+ */
+la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                    int64_t batch, int64_t heads, int64_t d,
+                    const float* slopes, float* kv, void* stream);
+
+/* Static description of a status code. */
+const char* la_status_string(la_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_LA_H */

@@ -1,0 +1,170 @@
+"""Lightning Attention on MI355X: thin Python binding over liblightning_la.so.
+
+The C ABI (include/la.h) is the product boundary; this module only marshals
+arguments: it takes torch tensors on the GPU, passes their device pointers,
+strides and torch's current HIP stream, and raises on a non-OK status.  Every
+step of the computation runs in the library's gfx950 kernels -- there is no
+fallback: if the library is missing, every call raises.
+
+Names follow the C entry points: la_state_init, la_prefill,
+la_prefill_workspace_size, la_prefill_chunk_tokens, la_decode,
+la_status_string, la_last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblightning_la.so")
+
+LA_OK = 0
+LA_ERR_INVALID_ARGUMENT = 1
+LA_ERR_UNSUPPORTED = 2
+LA_ERR_WORKSPACE = 3
+LA_ERR_DEVICE = 4
+LA_ERR_INTERNAL = 5
+LA_F32 = 0
+LA_BF16 = 1
+
+EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_size",
+            "la_prefill_workspace_size_ex", "la_prefill", "la_prefill_ex", "la_decode",
+            "la_status_string", "la_last_error"]
+
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {detail} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded library with ctypes signatures set (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(there is no non-HIP fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    L.la_state_init.restype = i32
+    L.la_state_init.argtypes = [p, p, i64, i64, i64, p]
+    L.la_prefill_chunk_tokens.restype = i64
+    L.la_prefill_chunk_tokens.argtypes = [i32, i64, i64, i64, i64]
+    L.la_prefill_workspace_size.restype = sz
+    L.la_prefill_workspace_size.argtypes = [i32, i64, i64, i64, i64]
+    L.la_prefill_workspace_size_ex.restype = sz
+    L.la_prefill_workspace_size_ex.argtypes = [i32, i64, i64, i64, i64, i64]
+    L.la_prefill.restype = i32
+    L.la_prefill.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, p, sz, p]
+    L.la_prefill_ex.restype = i32
+    L.la_prefill_ex.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, i64, p, sz, p]
+    L.la_decode.restype = i32
+    L.la_decode.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, p]
+    L.la_status_string.restype = ctypes.c_char_p
+    L.la_status_string.argtypes = [i32]
+    L.la_last_error.restype = ctypes.c_char_p
+    L.la_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def la_status_string(status: int) -> str:
+    return lib().la_status_string(status).decode()
+
+
+def la_last_error() -> str:
+    return lib().la_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != LA_OK:
+        raise LAError(status, where, la_last_error() or la_status_string(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_ptr(stream, device):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def la_state_init(kv, kv0=None, stream=None) -> None:
+    """kv[B,H,d,d] (float32) := 0, or a copy of kv0."""
+    _require_cuda(kv, kv0)
+    B, H, d, _ = kv.shape
+    _check(lib().la_state_init(_ptr(kv), _ptr(kv0), B, H, d, _stream_ptr(stream, kv.device)), "la_state_init")
+
+
+def la_prefill_chunk_tokens(dtype: int, batch: int, heads: int, n: int, d: int) -> int:
+    return int(lib().la_prefill_chunk_tokens(dtype, batch, heads, n, d))
+
+
+def la_prefill_workspace_size(dtype: int, batch: int, heads: int, n: int, d: int, chunk_tokens: int = 0) -> int:
+    return int(lib().la_prefill_workspace_size_ex(dtype, batch, heads, n, d, chunk_tokens))
+
+
+def la_prefill(q, k, v, slopes, kv, o=None, ckpt=None, ckpt_every: int = 0, workspace=None,
+               chunk_tokens: int = 0, stream=None) -> None:
+    """Prefill over q, k, v [B,H,N,d] (views allowed if the last dim is contiguous and the
+    three share strides).  Updates kv [B,H,d,d] in place; writes o (same shape/strides as q)
+    unless it is None; fills ckpt [B,H,N//ckpt_every,d,d] when given.  A workspace of
+    la_prefill_workspace_size() bytes is allocated here when not supplied."""
+    import torch
+
+    _require_cuda(q, k, v, slopes, kv, o, ckpt, workspace)
+    dt = _dtype_code(q)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(-1) != 1:
+        raise ValueError("q, k, v must share strides with a contiguous last dimension")
+    if o is not None and (o.shape != q.shape or o.stride() != q.stride() or o.dtype != q.dtype):
+        raise ValueError("o must match q in shape, strides and dtype")
+    if slopes.dtype != torch.float32 or kv.dtype != torch.float32:
+        raise ValueError("slopes and kv must be float32")
+    need = la_prefill_workspace_size(dt, B, H, N, d, chunk_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sb, sh, sn, _ = q.stride()
+    st = lib().la_prefill_ex(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, sb, sh, sn,
+                             _ptr(slopes), _ptr(kv), _ptr(ckpt), ckpt_every, chunk_tokens,
+                             _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
+    _check(st, "la_prefill")
+
+
+def la_decode(q, k, v, slopes, kv, o, stream=None) -> None:
+    """One decode step: kv <- lambda*kv + k^T v ; o = q . kv.  q,k,v,o contiguous [B,H,d]."""
+    _require_cuda(q, k, v, slopes, kv, o)
+    dt = _dtype_code(q)
+    B, H, d = q.shape
+    for t in (q, k, v, o):
+        if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o must be contiguous [B,H,d] tensors of one dtype")
+    st = lib().la_decode(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d, _ptr(slopes), _ptr(kv),
+                         _stream_ptr(stream, q.device))
+    _check(st, "la_decode")

@@ -1,0 +1,92 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer of
+// liblightning_la.so.  Not installed; the public interface is include/la.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la.h"
+
+namespace la {
+
+constexpr int kBlock = 64;       // tokens per kernel tile (the model's tile of 256 is a flop-count
+                                 // convention only; results do not depend on the tile)
+constexpr int kSliceW = 32;      // value columns per workgroup (value-dim slicing)
+constexpr int kTargetGroups = 256;  // workgroups that fill one MI355X (256 CUs, one resident each)
+constexpr int kMinChunk = 1024;  // shortest chunk worth a 64 KiB state exchange
+
+// How a prefill is split: value-column slices x sequence chunks per (batch, head).
+struct Plan {
+    int64_t chunk;     // tokens per chunk (multiple of kBlock unless a single chunk)
+    int64_t n_chunks;  // >= 1
+    int slices;        // d / kSliceW
+};
+
+Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk_override);
+
+// What a forward kernel launch does with each (batch, head, chunk, slice) it owns.
+enum FwdMode : int {
+    kModeOut = 0,    // outputs + state, starting from the chunk's prefix state
+    kModeState = 1,  // state (and checkpoints) only, starting from the chunk's prefix state
+    kModeLocal = 2,  // local chunk summary from a zero state, written to the workspace
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int64_t sb, sh, sn;      // element strides of q/k/v/o
+    int64_t heads;
+    int64_t n;               // tokens per sequence
+    int64_t chunk;           // tokens per chunk
+    int64_t n_chunks;        // chunks per sequence
+    int64_t chunks_launched; // chunks per sequence covered by this launch (n_chunks or n_chunks-1)
+    int64_t groups;          // batch*heads*chunks_launched
+    int slices;
+    const float* slopes;
+    float* kv;               // [B*H][d][d]
+    float* ws;               // [B*H][n_chunks][d][d] (slot j = state entering chunk j) or null
+    float* ckpt;             // [B*H][n_ckpt][d][d] or null
+    int64_t ckpt_every;
+    int64_t n_ckpt;
+};
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream);
+hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
+                       int64_t n_chunks, int64_t chunk, int d, hipStream_t stream);
+hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);
+hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                         int64_t bh, int64_t heads, int d, const float* slopes, float* kv,
+                         hipStream_t stream);
+
+// Workgroup index -> (group, slice) with the slices of one group on one XCD.  Consecutive
+// workgroup ids are dispatched round-robin over the 8 XCDs, so slices that share Q/K rows
+// land on the same XCD and share its L2.
+__host__ __device__ inline int64_t xcd_grid_size(int64_t groups, int slices)
+{
+    return ((groups + 7) / 8) * 8 * slices;
+}
+
+__device__ inline void xcd_decode(int64_t x, int slices, int64_t& group, int& slice)
+{
+    const int64_t xcd = x & 7;
+    const int64_t loc = x >> 3;
+    slice = (int)(loc % slices);
+    group = (loc / slices) * 8 + xcd;
+}
+
+// lambda^k = exp(-s*k) for k >= 0, as exp2(nsl*k) with nsl = -s*log2(e).
+__device__ inline float decay_pow(float nsl, float k)
+{
+    return exp2f(nsl * k);
+}
+
+__device__ inline float neg_slope_log2e(const float* slopes, int64_t h)
+{
+    return (float)(-(double)slopes[h] * 1.4426950408889634);
+}
+
+}  // namespace la

@@ -1,0 +1,103 @@
+// Single-token decode step on gfx950: kv <- lambda*kv + k^T v, then o = q . kv.
+//
+// Page "MiniMax-01: Scaling Foundation Models with Lightning Attention |
+// Summary", section 3.3: single-token generation runs as its own kernel and
+// is limited by memory traffic.  Per (batch, head) the step streams the
+// 64 KiB float32 state once in and once out; everything else is 4*d values.
+//
+// One 256-thread workgroup per (batch, head).  Thread t owns four adjacent
+// value columns (a float4) and every (256/(d/4))-th key row, so each wave's
+// load/store covers whole contiguous state rows (1 KiB per instruction at
+// d = 128).  The readout o[j] = sum_i q_i KV[i][j] is reduced across the row
+// groups through LDS.
+#include "la_common.h"
+
+namespace la {
+namespace {
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(__bf16 x) { return (float)x; }
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
+                                                const T* __restrict__ v, T* __restrict__ o,
+                                                const float* __restrict__ slopes,
+                                                float* __restrict__ kv, int64_t heads)
+{
+    constexpr int CG = D / 4;       // float4 column groups per row
+    constexpr int RG = 256 / CG;    // row groups
+    constexpr int RPT = D / RG;     // rows per thread
+    const int64_t u = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+
+    __shared__ float sq[D];
+    __shared__ float sk[D];
+    __shared__ f32x4 red[RG][CG];
+
+    float* S = kv + u * (int64_t)(D * D);
+    f32x4 st[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        st[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (rg + RG * m) * D) + cg);
+
+    if (tid < D) {
+        sq[tid] = to_f32(q[u * D + tid]);
+        sk[tid] = to_f32(k[u * D + tid]);
+    }
+    const T* vu = v + u * D + 4 * cg;
+    const f32x4 vv = {to_f32(vu[0]), to_f32(vu[1]), to_f32(vu[2]), to_f32(vu[3])};
+    const float lam = (float)exp(-(double)slopes[u % heads]);
+    __syncthreads();
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const f32x4 s = lam * st[m] + sk[i] * vv;
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(S + i * D) + cg);
+        acc += sq[i] * s;
+    }
+    red[rg][cg] = acc;
+    __syncthreads();
+    if (tid < CG) {
+        f32x4 r = red[0][tid];
+        for (int g = 1; g < RG; ++g) r += red[g][tid];
+        T* ou = o + u * D + 4 * tid;
+        ou[0] = from_f32<T>(r[0]);
+        ou[1] = from_f32<T>(r[1]);
+        ou[2] = from_f32<T>(r[2]);
+        ou[3] = from_f32<T>(r[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                         int64_t bh, int64_t heads, int d, const float* slopes, float* kv,
+                         hipStream_t stream)
+{
+    const dim3 grid((unsigned)bh), block(256);
+    if (dt == LA_BF16) {
+        auto qq = static_cast<const __bf16*>(q), kk = static_cast<const __bf16*>(k),
+             vv = static_cast<const __bf16*>(v);
+        auto oo = static_cast<__bf16*>(o);
+        if (d == 128) hipLaunchKernelGGL((k_decode<__bf16, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads);
+        else hipLaunchKernelGGL((k_decode<__bf16, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads);
+    } else {
+        auto qq = static_cast<const float*>(q), kk = static_cast<const float*>(k),
+             vv = static_cast<const float*>(v);
+        auto oo = static_cast<float*>(o);
+        if (d == 128) hipLaunchKernelGGL((k_decode<float, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads);
+        else hipLaunchKernelGGL((k_decode<float, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,72 @@
+// Chunk-prefix combine and state initialisation.
+//
+// Page "MiniMax-01: Scaling Foundation Models with Lightning Attention |
+// Summary", section 3.2 (LASP+): each sequence partition first computes a
+// local summary, the summaries are gathered, and the global prefixes are
+// built from them.  On one GPU the partitions are chunks of the sequence:
+// slot j+1 of the workspace holds the local state S_j of chunk j (from a zero
+// state); this kernel turns the slots into prefixes in place,
+//     P_0 = KV_in,   P_{j+1} = lambda^C * P_j + S_j,
+// so that slot j is the state entering chunk j.  Every state element is an
+// independent scalar recurrence over the chunks, so threads own float4s of the
+// state and walk the chunks; all loads of a thread are independent of the
+// running value and are issued ahead of the multiply-adds.
+#include "la_common.h"
+
+namespace la {
+namespace {
+
+__global__ __launch_bounds__(256) void k_scan(float* __restrict__ ws, const float* __restrict__ kv,
+                                              const float* __restrict__ slopes, int64_t bh,
+                                              int64_t heads, int64_t n_chunks, int64_t chunk, int d2)
+{
+    const int64_t per = d2 / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= bh * per) return;
+    const int64_t u = idx / per;
+    const int64_t e = idx % per;
+    const float nsl = neg_slope_log2e(slopes, u % heads);
+    const float lc = decay_pow(nsl, (float)chunk);
+    float4* base = reinterpret_cast<float4*>(ws + u * n_chunks * (int64_t)d2) + e;
+    float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
+    base[0] = p;
+    for (int64_t j = 1; j < n_chunks; ++j) {
+        const float4 s = base[j * per];
+        p.x = lc * p.x + s.x;
+        p.y = lc * p.y + s.y;
+        p.z = lc * p.z + s.z;
+        p.w = lc * p.w + s.w;
+        base[j * per] = p;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_state_init(float* __restrict__ kv, const float* __restrict__ kv0,
+                                                    int64_t count4)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count4) return;
+    reinterpret_cast<float4*>(kv)[i] =
+        kv0 ? reinterpret_cast<const float4*>(kv0)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+}  // namespace
+
+hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
+                       int64_t n_chunks, int64_t chunk, int d, hipStream_t stream)
+{
+    const int d2 = d * d;
+    const int64_t threads = bh * (d2 / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_scan, grid, block, 0, stream, ws, kv, slopes, bh, heads, n_chunks, chunk, d2);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream)
+{
+    const int64_t count4 = count / 4;  // count = B*H*d*d, a multiple of 4096
+    const dim3 grid((unsigned)((count4 + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_state_init, grid, block, 0, stream, kv, kv0, count4);
+    return hipGetLastError();
+}
+
+}  // namespace la

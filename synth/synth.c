@@ -44,17 +44,20 @@ static inline uint64_t draw(uint64_t key, uint64_t n)
     return mix64(key + (n + 1) * GOLDEN);
 }
 
-/* Value of element e of the stream, before the float32 rounding. */
-static inline double element(uint64_t key, int tensor, uint64_t e)
+/* Values of elements 2p and 2p+1 of the stream (Box-Muller pair), after SiLU for Q/K. */
+static inline void element_pair(uint64_t key, int tensor, uint64_t p, double* z0, double* z1)
 {
-    const uint64_t p = e >> 1;
     const double u1 = (double)((draw(key, 2 * p) >> 11) + 1) * 0x1.0p-53;
     const double u2 = (double)(draw(key, 2 * p + 1) >> 11) * 0x1.0p-53;
     const double r = sqrt(-2.0 * log(u1));
     const double a = 6.283185307179586476925286766559 * u2;
-    const double z = (e & 1) ? r * sin(a) : r * cos(a);
-    if (tensor == 2) return z;
-    return z / (1.0 + exp(-z));
+    double c = r * cos(a), s = r * sin(a);
+    if (tensor != 2) {
+        c = c / (1.0 + exp(-c));
+        s = s / (1.0 + exp(-s));
+    }
+    *z0 = c;
+    *z1 = s;
 }
 
 static inline uint16_t f32_to_bf16_rne(float f)
@@ -88,12 +91,18 @@ int synth_fill(void* out, int as_bf16, uint64_t seed, int tensor,
         const int64_t b = row / (nt * nh);
         const uint64_t key = stream_key(seed, (uint64_t)tensor, (uint64_t)(b0 + b), (uint64_t)(h0 + h));
         const uint64_t e0 = (uint64_t)(t0 + t) * (uint64_t)d;
-        if (as_bf16) {
-            uint16_t* o = (uint16_t*)out + row * d;
-            for (int64_t i = 0; i < d; ++i) o[i] = f32_to_bf16_rne((float)element(key, tensor, e0 + (uint64_t)i));
-        } else {
-            float* o = (float*)out + row * d;
-            for (int64_t i = 0; i < d; ++i) o[i] = (float)element(key, tensor, e0 + (uint64_t)i);
+        for (int64_t i = 0; i < d; i += 2) {
+            double z0, z1;
+            element_pair(key, tensor, (e0 + (uint64_t)i) >> 1, &z0, &z1);
+            if (as_bf16) {
+                uint16_t* o = (uint16_t*)out + row * d + i;
+                o[0] = f32_to_bf16_rne((float)z0);
+                o[1] = f32_to_bf16_rne((float)z1);
+            } else {
+                float* o = (float*)out + row * d + i;
+                o[0] = (float)z0;
+                o[1] = (float)z1;
+            }
         }
     }
     return 0;

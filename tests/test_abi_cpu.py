@@ -1,0 +1,103 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point,
+validates arguments before touching HIP, and reports a missing device as LA_ERR_DEVICE."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_la_amd as la
+from conftest import gpu_available
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "la.h")
+FAKE = ctypes.c_void_p(1 << 20)  # aligned non-null address, never dereferenced by validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = la.lib()
+    names = declared_functions()
+    assert set(names) == set(la.EXPORTED)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for s in range(6):
+        assert la.la_status_string(s).startswith("LA_")
+    assert "unknown" in la.la_status_string(99)
+
+
+def _prefill(**kw):
+    args = dict(dt=la.LA_BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=8, N=4096, d=128,
+                sb=8 * 4096 * 128, sh=4096 * 128, sn=128, slopes=FAKE, kv=FAKE, ckpt=None,
+                ckpt_every=0, chunk=0, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return la.lib().la_prefill_ex(a["dt"], a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["d"],
+                                  a["sb"], a["sh"], a["sn"], a["slopes"], a["kv"], a["ckpt"], a["ckpt_every"],
+                                  a["chunk"], a["ws"], a["ws_bytes"], None)
+
+
+def test_prefill_validation_codes():
+    assert _prefill(q=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(kv=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(slopes=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(dt=7) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(B=0) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(N=-1) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(d=96, sn=96) == la.LA_ERR_UNSUPPORTED
+    assert _prefill(d=64, sn=64) == la.LA_ERR_UNSUPPORTED          # bf16 needs d = 128
+    assert _prefill(sn=100) == la.LA_ERR_INVALID_ARGUMENT           # not a 16-byte multiple
+    assert _prefill(sn=64) == la.LA_ERR_INVALID_ARGUMENT            # stride_n < d
+    assert _prefill(q=ctypes.c_void_p((1 << 20) + 2)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned
+    assert _prefill(ckpt=FAKE, ckpt_every=100) == la.LA_ERR_UNSUPPORTED
+    assert _prefill(ckpt=FAKE, ckpt_every=0) == la.LA_ERR_UNSUPPORTED
+    assert _prefill(chunk=100) == la.LA_ERR_INVALID_ARGUMENT
+    assert "64" in la.la_last_error()
+    # chunked plan without (enough) workspace
+    assert _prefill(ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
+    assert _prefill(ws_bytes=10) == la.LA_ERR_WORKSPACE
+    # n == 0 is a no-op and never touches the device
+    assert _prefill(N=0, q=None, k=None, v=None, ws=None, ws_bytes=0) == la.LA_OK
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
+def test_no_device_is_reported_not_fatal():
+    assert _prefill() == la.LA_ERR_DEVICE
+    assert "GPU" in la.la_last_error()
+    L = la.lib()
+    assert L.la_decode(la.LA_BF16, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, FAKE, FAKE, None) == la.LA_ERR_DEVICE
+    assert L.la_state_init(FAKE, None, 2, 2, 128, None) == la.LA_ERR_DEVICE
+
+
+def test_decode_and_state_init_validation():
+    L = la.lib()
+    assert L.la_decode(la.LA_BF16, None, FAKE, FAKE, FAKE, 2, 2, 128, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARGUMENT
+    assert L.la_decode(la.LA_BF16, FAKE, FAKE, FAKE, FAKE, 2, 2, 96, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
+    assert L.la_decode(la.LA_F32, FAKE, FAKE, FAKE, FAKE, 0, 2, 64, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARGUMENT
+    assert L.la_state_init(None, None, 1, 1, 128, None) == la.LA_ERR_INVALID_ARGUMENT
+    assert L.la_state_init(FAKE, None, 1, 1, 32, None) == la.LA_ERR_UNSUPPORTED
+
+
+def test_plan_and_workspace_sizes():
+    # 64 heads x 4 value slices fill the GPU: one chunk, no workspace
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 64, 131072, 128) == 131072
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 0
+    # 8 heads: 8 chunks per sequence
+    c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 32768, 128)
+    assert c == 4096
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * 8 * 128 * 128 * 4
+    c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 1048576, 128)
+    assert c == 131072
+    # short sequences are not chunked
+    assert la.la_prefill_chunk_tokens(la.LA_F32, 1, 2, 512, 64) == 512
+    # explicit chunking
+    assert la.la_prefill_workspace_size(la.LA_F32, 1, 2, 512, 64, chunk_tokens=128) == 2 * 4 * 64 * 64 * 4
+    assert la.la_prefill_workspace_size(la.LA_F32, 1, 2, 512, 64, chunk_tokens=1024) == 0
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 100, 96) == -1
