@@ -17,72 +17,95 @@
 // after a large incoming state (KV).  Every product accumulates in float32 and
 // the state itself stays float32 in accumulators.
 //
-// Decomposition.  A workgroup (4 waves) owns one (batch, head, chunk, slice of
-// 32 value columns): both the state's columns and the outputs' columns split
-// by value column with no communication, which gives 4 workgroups per head
-// without a second pass over K and V.  Q and K rows are read by the four
-// slices of a head; their workgroups sit on one XCD so the re-reads hit L2.
-// Sequences with too few heads to fill the GPU are also cut into chunks
-// (la_scan.hip combines the chunk summaries).
+// Decomposition.  A workgroup owns one (batch, head, chunk, slice of 32 value
+// columns): both the state's columns and the outputs' columns split by value
+// column with no communication, which gives 4 workgroups per head without a
+// second pass over K and V.  Q and K rows are read by the four slices of a
+// head; their workgroups sit on one XCD so the re-reads hit L2.  Sequences
+// with too few heads to fill the GPU are also cut into chunks (la_scan.hip
+// combines the chunk summaries).
 //
-// Per 64-token tile, wave w owns query rows 16w..16w+15 (scores, masking,
-// outputs) and state rows 32w..32w+31.  MFMA used: v_mfma_f32_16x16x32_bf16
-// (A 16x32, B 32x16, C 16x16 fp32; lane l holds A row l%16 / B column l%16 and
-// 8 consecutive k of group l/16; C column l%16, rows 4(l/16)..+3).  Any
-// permutation of k works as long as A and B use the same one; this is used
-// twice:
-//   * S is computed transposed (S^T = K Q^T), so a lane's accumulator holds
-//     one query row r and the key columns {4g..4g+3} and {16+4g..16+4g+3} of
-//     two adjacent 16-key tiles -- exactly an A operand of P.V over a 32-key
-//     step with that k order, with no data movement;
-//   * V^T and K^T are stored in LDS with tokens in that same order (tok_pos),
-//     so the B operand of P.V and both operands of the state update are plain
-//     16-byte LDS reads.
-// Q goes straight from global memory into registers in operand layout (it is
-// the B operand of S^T and the A operand of Q.KV for the same rows).  K is
-// staged twice: row-major for S^T and transposed for the state update; V is
-// staged transposed, plain for P.V and decay-weighted (hi + lo) for the state
-// update.  Staging of tile b+1 overlaps tile b (global
-// loads issued before the tile's MFMAs, LDS double-buffered), one barrier per
-// tile.
+// Wave roles (8 waves, two per SIMD, so one wave's latencies hide behind the
+// other's work).  Output waves 0..3: wave w owns query rows 16w..16w+15 of
+// each 64-token tile -- scores, masking, P V, the inter-tile term and the
+// output store; Q goes straight from global memory into registers in operand
+// layout (B operand of S^T, A operand of Q KV).  State waves 4..7: the global
+// loads and LDS staging of K and V, the decay-weighted W V, and the state
+// update, with the state's 16 tiles of 16x16 split 6/5/3/2 so that each SIMD
+// (output wave w + state wave w) issues the same 48 MFMAs per tile.  The state
+// waves publish the state after tile b (bf16 hi/lo copy in LDS) for the output
+// waves' inter term of tile b+1.  Without outputs (state-only modes) the
+// kernel runs the four state waves alone.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, C 16x16 fp32; lane l holds
+// A row l%16 / B column l%16 and 8 k-values of group g = l/16; C column l%16,
+// rows 4g..4g+3).  The sum over k does not care which k a slot holds as long
+// as A and B agree, which is used twice:
+//   * S is computed transposed (S^T = K Q^T), so a lane's accumulators hold
+//     one query row r and keys {4g..4g+3} and {16+4g..16+4g+3} of two
+//     adjacent 16-key tiles -- an A operand of P.V over a 32-key step in that
+//     k order, with no data movement;
+//   * the k = token operands (V for P.V; K^T and W V for the state update) are
+//     read from row-major LDS tiles with the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16): within each 16-lane group, the lane that supplies
+//     the address of row k0 + a/4, columns c0 + 4(a%4)..+3 makes lane i
+//     receive rows k0..k0+3 of column c0 + i, i.e. four consecutive k of one
+//     MFMA row/column.  Two such reads fill an 8-value operand, so tiles are
+//     staged as plain row copies and any k order is available.
+// Global traffic uses buffer loads/stores on a per-tile resource whose size
+// ends at the tile's last valid row, so the rows of a ragged last tile read as
+// zero without branches.  Loads run two tiles ahead (two register sets), tiles
+// are double-buffered in LDS, one barrier per tile.  Per-element decay factors
+// come from per-lane tables computed once per workgroup.
 #include "la_common.h"
 
 namespace la {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 128, BK = kBlock, SW = kSliceW;
-constexpr int KS = D + 8;   // row stride (elements) of row-major K tiles
-constexpr int TS = BK + 8;  // row stride of transposed K / V tiles
-constexpr int SS = D + 8;   // row stride of the bf16 state copies (stored KV^T: [value col][key row])
+constexpr int KS = D + 8;   // row stride (elements) of the row-major K tile
+constexpr int VS = SW + 8;  // row stride of the V, W V tiles
+constexpr int SS = D + 8;   // row stride of the state copies (stored KV^T: [value col][key row])
 constexpr int OS = SW + 8;  // row stride of the output staging tile
-
-// Position of token c (0..63) inside a transposed tile row; see the header comment.
-__device__ __forceinline__ int tok_pos(int c)
-{
-    const int u = c & 31;
-    return (c & 32) + 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3);
-}
-
-__device__ __forceinline__ uint32_t elem_bits(const uint4& x, int e)
-{
-    const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descriptor word 3
 
 __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t f32_to_bits(float f) { return (uint32_t)__builtin_bit_cast(u16, (__bf16)f); }
+__device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-__device__ __forceinline__ uint32_t f32_to_bits(float f)
+// Two floats -> packed bf16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t cvt2(float a, float b)
 {
-    return (uint32_t)__builtin_bit_cast(u16, (__bf16)f);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// (a, b) -> bf16 pairs hi and lo with x = hi + lo to about 16 bits.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo)
+{
+    hi = cvt2(a, b);
+    lo = cvt2(a - bits_to_f32(hi & 0xffffu), b - hi_to_f32(hi));
 }
 
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+// Transposing LDS read (see the header comment): returns rows k0..k0+3 of column c0 + (lane % 16)
+// when this lane passes the address of row k0 + (lane%16)/4, column c0 + 4*(lane%4).
+__device__ __forceinline__ s16x4 lds_tr(const u16* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)p));
+}
 
-__device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 join(s16x4 a, s16x4 b)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 {
@@ -96,15 +119,28 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Raw buffer covering `bytes` bytes from p (reads past the end return 0, writes there are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32ks + 8g .. +7
+struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
+
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void k_fwd_bf16(FwdArgs a)
+__global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
     constexpr bool OUT = MODE == kModeOut;
+    constexpr int SW0 = OUT ? 4 : 0;  // first state wave
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
-    __shared__ __attribute__((aligned(16))) u16 sKT[2][D * TS];
-    __shared__ __attribute__((aligned(16))) u16 sVT[2][SW * TS];
-    __shared__ __attribute__((aligned(16))) u16 sVWh[2][SW * TS];
-    __shared__ __attribute__((aligned(16))) u16 sVWl[2][SW * TS];
+    __shared__ __attribute__((aligned(16))) u16 sV[2][BK * VS];
+    __shared__ __attribute__((aligned(16))) u16 sVWh[2][BK * VS];
+    __shared__ __attribute__((aligned(16))) u16 sVWl[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sSh[2][SW * SS];
     __shared__ __attribute__((aligned(16))) u16 sSl[2][SW * SS];
     __shared__ __attribute__((aligned(16))) u16 sO[BK * OS];
@@ -119,9 +155,11 @@ __global__ __launch_bounds__(256, 1) void k_fwd_bf16(FwdArgs a)
     const int64_t t_begin = j * a.chunk;
     const int64_t t_end = (t_begin + a.chunk < a.n) ? t_begin + a.chunk : a.n;
     const int64_t d2 = (int64_t)D * D;
+    const int n_tiles = (int)((t_end - t_begin + BK - 1) / BK);
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_state = w >= SW0;
     const int l = tid & 63, lr = l & 15, g = l >> 4;
     const float nsl = neg_slope_log2e(a.slopes, h);
     const int64_t base = bb * a.sb + h * a.sh;
@@ -130,264 +168,277 @@ __global__ __launch_bounds__(256, 1) void k_fwd_bf16(FwdArgs a)
     const u16* Vg = static_cast<const u16*>(a.v) + base + slice * SW;
     u16* Og = OUT ? static_cast<u16*>(a.o) + base + slice * SW : nullptr;
     const int64_t sn = a.sn;
+    const uint32_t row_bytes = (uint32_t)(sn * 2);
+    // transposing-read address pieces: row k0 + lr/4, column c0 + 4*(lr%4)
+    const int tr_row = lr >> 2, tr_col = 4 * (lr & 3);
 
-    // staging roles: threads 0..127 carry an 8x8 K tile, 128..159 an 8x8 V tile
-    const bool k_role = tid < 128;
-    const bool v_role = tid >= 128 && tid < 160;
-    const int ktg = tid >> 4, kdg = tid & 15;                 // K: token group, feature group
-    const int vtg = (tid - 128) >> 2, vcg = (tid - 128) & 3;  // V: token group, column group
+    auto tile_start = [&](int tile) __attribute__((always_inline)) { return t_begin + (int64_t)tile * BK; };
+    auto tile_len = [&](int tile) __attribute__((always_inline)) {
+        const int64_t t0 = t_begin + (int64_t)tile * BK;
+        return (int)((t_end - t0 < BK) ? t_end - t0 : BK);
+    };
 
-    uint4 qn[4];   // next tile's Q operand fragments (rows 16w+lr, features 32ks+8g..)
-    uint4 tn[8];   // next tile's 8x8 K or V block (8 token rows x 16 bytes)
+    // ------------------------------------------------------------------ state waves
+    const int sw = w - SW0;          // state wave index 0..3
+    const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
+    // state tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), split for balance
+    const int st_first = OUT ? (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14) : 4 * sw;
+    const int st_count = OUT ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : 4;
+    constexpr int MAXT = OUT ? 6 : 4;
+    f32x4 st[MAXT];
 
-    auto load_tile = [&](int64_t t0, int L) {
-        if (OUT) {
-            const int r = 16 * w + lr;
+    auto load_kv = [&](KVRegs& R, int tile) __attribute__((always_inline)) {
+        const int64_t t0 = tile_start(tile);
+        const int L = tile_len(tile);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, (int64_t)L * row_bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, (int64_t)L * row_bytes);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qn[ks] = (r < L) ? *reinterpret_cast<const uint4*>(Qg + (t0 + r) * sn + 32 * ks + 8 * g)
-                                 : make_uint4(0, 0, 0, 0);
+        for (int m = 0; m < 4; ++m) {
+            const int c = st_id + 256 * m;
+            R.k[m] = buf_load16(rk, (uint32_t)(c >> 4) * row_bytes + 16u * (c & 15));
         }
-        if (k_role) {
+        R.v = buf_load16(rv, (uint32_t)(st_id >> 2) * row_bytes + 16u * (st_id & 3));
+    };
+    // K and V rows into LDS buffer `buf`, with the decay-weighted V as bf16 hi + lo.
+    auto stage_tile = [&](const KVRegs& R, int buf, int tile) __attribute__((always_inline)) {
+        const int L = tile_len(tile);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int r = 8 * ktg + m;
-                tn[m] = (r < L) ? *reinterpret_cast<const uint4*>(Kg + (t0 + r) * sn + 8 * kdg)
-                                : make_uint4(0, 0, 0, 0);
-            }
-        } else if (v_role) {
+        for (int m = 0; m < 4; ++m) {
+            const int c = st_id + 256 * m;
+            *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + 8 * (c & 15)]) = R.k[m];
+        }
+        const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
+        *reinterpret_cast<uint4*>(&sV[buf][off]) = R.v;
+        const float wt = (r < L) ? decay_pow(nsl, (float)(L - 1 - r)) : 0.f;
+        const uint32_t in[4] = {R.v.x, R.v.y, R.v.z, R.v.w};
+        uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int r = 8 * vtg + m;
-                tn[m] = (r < L) ? *reinterpret_cast<const uint4*>(Vg + (t0 + r) * sn + 8 * vcg)
-                                : make_uint4(0, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
+        *reinterpret_cast<uint4*>(&sVWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(&sVWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    };
+    // state copy for the inter term: KV^T[value col][key row], 4 consecutive key rows per lane
+    auto write_state_copy = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) {
+            if (k < st_count) {
+                const int q = st_first + k;
+                uint32_t h01, l01, h23, l23;
+                split2(st[k][0], st[k][1], h01, l01);
+                split2(st[k][2], st[k][3], h23, l23);
+                const int off = (16 * (q & 1) + lr) * SS + 16 * (q >> 1) + 4 * g;
+                *reinterpret_cast<uint2*>(&sSh[buf][off]) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(l01, l23);
             }
         }
     };
-
-    auto stage_tile = [&](int buf, int L) {
-        if (k_role) {
-            if (OUT) {
+    auto store_state = [&](float* dst) __attribute__((always_inline)) {
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    *reinterpret_cast<uint4*>(&sK[buf][(8 * ktg + m) * KS + 8 * kdg]) = tn[m];
+        for (int k = 0; k < MAXT; ++k) {
+            if (k < st_count) {
+                const int q = st_first + k;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    dst[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] = st[k][t];
             }
-            const int p0 = tok_pos(8 * ktg), p1 = tok_pos(8 * ktg + 4);
+        }
+    };
+    // KV <- lambda^L KV + K^T (W V) on this wave's state tiles
+    auto update_state = [&](int buf, int tile) __attribute__((always_inline)) {
+        const int L = tile_len(tile);
+        const float dl = decay_pow(nsl, (float)L);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t x[8];
+        for (int k = 0; k < MAXT; ++k)
+            if (k < st_count) st[k] *= dl;
 #pragma unroll
-                for (int m = 0; m < 8; ++m) x[m] = elem_bits(tn[m], e);
-                u16* row = &sKT[buf][(8 * kdg + e) * TS];
-                *reinterpret_cast<uint2*>(row + p0) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
-                *reinterpret_cast<uint2*>(row + p1) = make_uint2(pack2(x[4], x[5]), pack2(x[6], x[7]));
+        for (int ks = 0; ks < 2; ++ks) {
+            const int k0 = 32 * ks + 8 * g;
+            bf16x8 vh[2], vl[2];
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const int o = (k0 + tr_row) * VS + 16 * jt + tr_col;
+                vh[jt] = join(lds_tr(&sVWh[buf][o]), lds_tr(&sVWh[buf][o + 4 * VS]));
+                vl[jt] = join(lds_tr(&sVWl[buf][o]), lds_tr(&sVWl[buf][o + 4 * VS]));
             }
-        } else if (v_role) {
-            float wt[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int c = 8 * vtg + m;
-                wt[m] = (c < L) ? decay_pow(nsl, (float)(L - 1 - c)) : 0.f;
-            }
-            const int p0 = tok_pos(8 * vtg), p1 = tok_pos(8 * vtg + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t x[8], hi[8], lo[8];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    x[m] = elem_bits(tn[m], e);
-                    const float y = bits_to_f32(x[m]) * wt[m];
-                    hi[m] = f32_to_bits(y);
-                    lo[m] = f32_to_bits(y - bits_to_f32(hi[m]));
+            for (int k = 0; k < MAXT; ++k) {
+                if (k < st_count) {
+                    const int q = st_first + k;
+                    const int o = (k0 + tr_row) * KS + 16 * (q >> 1) + tr_col;
+                    const bf16x8 ka = join(lds_tr(&sK[buf][o]), lds_tr(&sK[buf][o + 4 * KS]));
+                    const bf16x8 bh = (q & 1) ? vh[1] : vh[0];
+                    const bf16x8 bl = (q & 1) ? vl[1] : vl[0];
+                    st[k] = mfma(ka, bh, st[k]);
+                    st[k] = mfma(ka, bl, st[k]);
                 }
-                const int ro = (8 * vcg + e) * TS;
-                *reinterpret_cast<uint2*>(&sVT[buf][ro + p0]) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
-                *reinterpret_cast<uint2*>(&sVT[buf][ro + p1]) = make_uint2(pack2(x[4], x[5]), pack2(x[6], x[7]));
-                *reinterpret_cast<uint2*>(&sVWh[buf][ro + p0]) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-                *reinterpret_cast<uint2*>(&sVWh[buf][ro + p1]) = make_uint2(pack2(hi[4], hi[5]), pack2(hi[6], hi[7]));
-                *reinterpret_cast<uint2*>(&sVWl[buf][ro + p0]) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
-                *reinterpret_cast<uint2*>(&sVWl[buf][ro + p1]) = make_uint2(pack2(lo[4], lo[5]), pack2(lo[6], lo[7]));
             }
         }
     };
 
-    // incoming state: rows i = 32w + 16it + 4g + t, value columns 16jt + lr of this slice
-    f32x4 st[2][2];
-    {
+    // ------------------------------------------------------------------ output waves
+    // dmask[ct][t] = lambda^(r - c) for query r = 16w + lr and key c = 16ct + 4g + t (0 if c > r);
+    // drow[t] = lambda^(r+1) for output rows r = 16w + 4g + t.
+    float dmask[4][4], drow[4];
+    if (OUT && !is_state) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = 16 * (w - ct) + lr - 4 * g - t;
+                dmask[ct][t] = (e >= 0) ? decay_pow(nsl, (float)e) : 0.f;
+            }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) drow[t] = decay_pow(nsl, (float)(16 * w + 4 * g + t + 1));
+    }
+    auto load_q = [&](QRegs& R, int tile) __attribute__((always_inline)) {
+        const int64_t t0 = tile_start(tile);
+        const int L = tile_len(tile);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, (int64_t)L * row_bytes);
+        const uint32_t off = (uint32_t)(16 * w + lr) * row_bytes + 16u * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ks);
+    };
+    // Outputs of tile `tile` from LDS buffer `buf`; R.q is refilled with tile next_q once consumed.
+    auto compute_out = [&](QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
+        const int64_t t0 = tile_start(tile);
+        const int L = tile_len(tile);
+        bf16x8 qf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, R.q[ks]);
+        // inter-tile term: Q KV, rows scaled by lambda^(r+1)
+        f32x4 acc[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = (16 * jt + lr) * SS + 32 * ks + 8 * g;
+                acc[jt] = mfma(qf[ks], lds8(&sSh[buf][off]), acc[jt]);
+                acc[jt] = mfma(qf[ks], lds8(&sSl[buf][off]), acc[jt]);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[jt][t] *= drow[t];
+        }
+        // intra-tile scores S^T for key tiles 0..w (later key tiles are fully masked)
+        float p[4][4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            if (ct <= w) {
+                f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    s = mfma(lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ks + 8 * g]), qf[ks], s);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) p[ct][t] = s[t] * dmask[ct][t];
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) p[ct][t] = 0.f;
+            }
+        }
+        if (next_q < n_tiles) load_q(R, next_q);
+        // intra-tile output P V (keys 32k2 + {4g..4g+3, 16+4g..16+4g+3} in each 32-key step)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            if (2 * k2 <= w) {
+                uint32_t hh[4], ll[4];
+                split2(p[2 * k2][0], p[2 * k2][1], hh[0], ll[0]);
+                split2(p[2 * k2][2], p[2 * k2][3], hh[1], ll[1]);
+                split2(p[2 * k2 + 1][0], p[2 * k2 + 1][1], hh[2], ll[2]);
+                split2(p[2 * k2 + 1][2], p[2 * k2 + 1][3], hh[3], ll[3]);
+                const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
+                const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    const u16* vb = &sV[buf][tr_row * VS + 16 * jt + tr_col];
+                    const bf16x8 vo = join(lds_tr(vb + (32 * k2 + 4 * g) * VS),
+                                           lds_tr(vb + (32 * k2 + 16 + 4 * g) * VS));
+                    acc[jt] = mfma(ph, vo, acc[jt]);
+                    acc[jt] = mfma(pl, vo, acc[jt]);
+                }
+            }
+        }
+        // output tile: stage this wave's 16 rows, then 16-byte stores
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                sO[(16 * w + 4 * g + t) * OS + 16 * jt + lr] = (u16)f32_to_bits(acc[jt][t]);
+        wave_lds_sync();
+        {
+            const int rr = 16 * w + (l >> 2), cc = 8 * (l & 3);
+            const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + t0 * sn, (int64_t)L * row_bytes);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
+                                                   (int)((uint32_t)rr * row_bytes + 2u * cc), 0, 0);
+        }
+    };
+
+    // ------------------------------------------------------------------ tile loops
+    // Each role runs its own loop (so their registers do not overlap); both pass the same
+    // barriers: one after the prologue and one between consecutive tiles.  Tiles alternate
+    // between LDS buffers 0 and 1 and between register sets A and B.
+    if (is_state) {
         const float* src = nullptr;
         if (MODE != kModeLocal) src = (a.n_chunks > 1) ? a.ws + (u * a.n_chunks + j) * d2 : a.kv + u * d2;
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
+        for (int k = 0; k < MAXT; ++k) {
+            if (k < st_count) {
+                const int q = st_first + k;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    st[it][jt][t] = src ? src[(32 * w + 16 * it + 4 * g + t) * D + slice * SW + 16 * jt + lr] : 0.f;
-    }
-    auto write_state_copy = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    hi[t] = f32_to_bits(st[it][jt][t]);
-                    lo[t] = f32_to_bits(st[it][jt][t] - bits_to_f32(hi[t]));
-                }
-                const int off = (16 * jt + lr) * SS + 32 * w + 16 * it + 4 * g;
-                *reinterpret_cast<uint2*>(&sSh[buf][off]) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-                *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+                    st[k][t] = src ? src[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] : 0.f;
             }
-    };
-    auto store_state = [&](float* dst) {
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    dst[(32 * w + 16 * it + 4 * g + t) * D + slice * SW + 16 * jt + lr] = st[it][jt][t];
-    };
-
-    {
-        const int L0 = (int)((t_end - t_begin < BK) ? t_end - t_begin : BK);
-        load_tile(t_begin, L0);
-        stage_tile(0, L0);
+        }
+        KVRegs RA, RB;
+        load_kv(RA, 0);
+        if (n_tiles > 1) load_kv(RB, 1);
+        stage_tile(RA, 0, 0);
         if (OUT) write_state_copy(0);
         __syncthreads();
-    }
-
-    int cur = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += BK, cur ^= 1) {
-        const int L = (int)((t_end - t0 < BK) ? t_end - t0 : BK);
-        const bool has_next = t0 + BK < t_end;
-        const int Ln = has_next ? (int)((t_end - t0 - BK < BK) ? t_end - t0 - BK : BK) : 0;
-        bf16x8 qf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qn[ks]);
-        if (has_next) load_tile(t0 + BK, Ln);
-
-        if (OUT) {
-            // inter-tile term: Q KV, rows scaled by lambda^(r+1)
-            f32x4 acc[2];
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int off = (16 * jt + lr) * SS + 32 * ks + 8 * g;
-                    acc[jt] = mfma(qf[ks], lds8(&sSh[cur][off]), acc[jt]);
-                    acc[jt] = mfma(qf[ks], lds8(&sSl[cur][off]), acc[jt]);
-                }
+        auto step = [&](KVRegs& R, KVRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
+            if (tile + 2 < n_tiles) load_kv(R, tile + 2);
+            update_state(buf, tile);
+            if (OUT && tile + 1 < n_tiles) write_state_copy(buf ^ 1);
+            if (MODE != kModeLocal && a.ckpt) {
+                const int64_t end = tile_start(tile) + tile_len(tile);
+                if (end % a.ckpt_every == 0) store_state(a.ckpt + (u * a.n_ckpt + (end / a.ckpt_every - 1)) * d2);
             }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float rs = decay_pow(nsl, (float)(16 * w + 4 * g + t + 1));
-                acc[0][t] *= rs;
-                acc[1][t] *= rs;
-            }
-            // intra-tile scores S^T for key tiles 0..w (later key tiles are fully masked)
-            const int r = 16 * w + lr;
-            float p[4][4];
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                if (ct <= w) {
-                    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        s = mfma(lds8(&sK[cur][(16 * ct + lr) * KS + 32 * ks + 8 * g]), qf[ks], s);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int c = 16 * ct + 4 * g + t;
-                        p[ct][t] = (c <= r) ? s[t] * decay_pow(nsl, (float)(r - c)) : 0.f;
-                    }
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) p[ct][t] = 0.f;
-                }
-            }
-            // intra-tile output P V
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                if (2 * k2 <= w) {
-                    bf16x8 ph, pl;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        ph[t] = (__bf16)p[2 * k2][t];
-                        ph[4 + t] = (__bf16)p[2 * k2 + 1][t];
-                        pl[t] = (__bf16)(p[2 * k2][t] - (float)ph[t]);
-                        pl[4 + t] = (__bf16)(p[2 * k2 + 1][t] - (float)ph[4 + t]);
-                    }
-#pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
-                        const bf16x8 vb = lds8(&sVT[cur][(16 * jt + lr) * TS + 32 * k2 + 8 * g]);
-                        acc[jt] = mfma(ph, vb, acc[jt]);
-                        acc[jt] = mfma(pl, vb, acc[jt]);
-                    }
-                }
-            }
-            // output tile: stage this wave's 16 rows, then 16-byte stores
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    sO[(16 * w + 4 * g + t) * OS + 16 * jt + lr] = (u16)f32_to_bits(acc[jt][t]);
-            wave_lds_sync();
-            {
-                const int rr = 16 * w + (l >> 2), cc = 8 * (l & 3);
-                const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
-                if (rr < L) *reinterpret_cast<uint4*>(Og + (t0 + rr) * sn + cc) = x;
-            }
+            if (tile + 1 < n_tiles) stage_tile(Rn, buf ^ 1, tile + 1);
+        };
+        for (int tile = 0;; tile += 2) {
+            step(RA, RB, 0, tile);
+            if (tile + 1 >= n_tiles) break;
+            __syncthreads();
+            step(RB, RA, 1, tile + 1);
+            if (tile + 2 >= n_tiles) break;
+            __syncthreads();
         }
-
-        // state update: KV <- lambda^L KV + K^T (W V) for this wave's 32 key rows
-        {
-            const float dl = decay_pow(nsl, (float)L);
-#pragma unroll
-            for (int it = 0; it < 2; ++it)
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) st[it][jt] *= dl;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 vh[2], vl[2];
-#pragma unroll
-                for (int jt = 0; jt < 2; ++jt) {
-                    vh[jt] = lds8(&sVWh[cur][(16 * jt + lr) * TS + 32 * ks + 8 * g]);
-                    vl[jt] = lds8(&sVWl[cur][(16 * jt + lr) * TS + 32 * ks + 8 * g]);
-                }
-#pragma unroll
-                for (int it = 0; it < 2; ++it) {
-                    const bf16x8 ka = lds8(&sKT[cur][(32 * w + 16 * it + lr) * TS + 32 * ks + 8 * g]);
-#pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) {
-                        st[it][jt] = mfma(ka, vh[jt], st[it][jt]);
-                        st[it][jt] = mfma(ka, vl[jt], st[it][jt]);
-                    }
-                }
-            }
-        }
-        if (OUT && has_next) write_state_copy(cur ^ 1);
-        if (MODE != kModeLocal && a.ckpt) {
-            const int64_t end = t0 + L;
-            if (end % a.ckpt_every == 0) store_state(a.ckpt + (u * a.n_ckpt + (end / a.ckpt_every - 1)) * d2);
-        }
-        if (has_next) stage_tile(cur ^ 1, Ln);
+        if (MODE == kModeLocal) store_state(a.ws + (u * a.n_chunks + j + 1) * d2);
+        else if (j == a.n_chunks - 1) store_state(a.kv + u * d2);
+    } else if (OUT) {
+        QRegs QA, QB;
+        load_q(QA, 0);
+        if (n_tiles > 1) load_q(QB, 1);
         __syncthreads();
+        for (int tile = 0;; tile += 2) {
+            compute_out(QA, 0, tile, tile + 2);
+            if (tile + 1 >= n_tiles) break;
+            __syncthreads();
+            compute_out(QB, 1, tile + 1, tile + 3);
+            if (tile + 2 >= n_tiles) break;
+            __syncthreads();
+        }
     }
-
-    if (MODE == kModeLocal) store_state(a.ws + (u * a.n_chunks + j + 1) * d2);
-    else if (j == a.n_chunks - 1) store_state(a.kv + u * d2);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream)
 {
-    const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices)), block(256);
-    if (mode == kModeOut) hipLaunchKernelGGL(k_fwd_bf16<kModeOut>, grid, block, 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL(k_fwd_bf16<kModeState>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(k_fwd_bf16<kModeLocal>, grid, block, 0, stream, a);
+    const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
+    if (mode == kModeOut) hipLaunchKernelGGL(k_fwd_bf16<kModeOut>, grid, dim3(512), 0, stream, a);
+    else if (mode == kModeState) hipLaunchKernelGGL(k_fwd_bf16<kModeState>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(k_fwd_bf16<kModeLocal>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
