@@ -70,9 +70,11 @@ typedef unsigned short u16;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 128, BK = kBlock, SW = kSliceW;
-constexpr int KS = D + 8;   // row stride (elements) of the row-major K tile
-constexpr int VS = SW + 8;  // row stride of the V, W V tiles
-constexpr int SS = D + 8;   // row stride of the state copies (stored KV^T: [value col][key row])
+constexpr int KS = D + 16;  // row stride (elements) of the row-major K tile: 288 B, so the 4 rows of a
+                            // transposing read fall in disjoint banks
+constexpr int VS = SW + 16;  // row stride of the V, W V tiles: 96 B (same reason)
+constexpr int SS = D;       // row stride of the state copies (stored KV^T: [value col][key row]); the
+                            // 16-byte chunk index is XORed with row % 16 (see ss_off)
 constexpr int OS = SW + 8;  // row stride of the output staging tile
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descriptor word 3
 
@@ -80,6 +82,14 @@ __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_fl
 __device__ __forceinline__ float hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ uint32_t f32_to_bits(float f) { return (uint32_t)__builtin_bit_cast(u16, (__bf16)f); }
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Element offset of (row, col) in a state copy: unpadded 256-byte rows whose 16-byte chunks are
+// permuted by row % 16, so that 16 lanes reading one chunk position of 16 rows (operand reads) or
+// writing 8-byte halves of 16 rows (state publication) touch 16 different chunks of the bank space.
+__device__ __forceinline__ int ss_off(int row, int col)
+{
+    return row * SS + ((((col >> 3) ^ row) & 15) << 3) + (col & 7);
+}
 
 // Two floats -> packed bf16 pair (round to nearest even).
 __device__ __forceinline__ uint32_t cvt2(float a, float b)
@@ -128,6 +138,8 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+
+template <int N> struct IntC { static constexpr int value = N; };
 
 struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32ks + 8g .. +7
 struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
@@ -179,13 +191,11 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     };
 
     // ------------------------------------------------------------------ state waves
-    const int sw = w - SW0;          // state wave index 0..3
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
-    // state tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), split for balance
-    const int st_first = OUT ? (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14) : 4 * sw;
-    const int st_count = OUT ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : 4;
-    constexpr int MAXT = OUT ? 6 : 4;
-    f32x4 st[MAXT];
+    // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..) of state wave sw:
+    // [first, first + count), split 6/5/3/2 with outputs (to balance the SIMDs), 4 each without.
+    auto st_first = [](int sw) constexpr { return OUT ? (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14) : 4 * sw; };
+    auto st_count = [](int sw) constexpr { return OUT ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : 4; };
 
     auto load_kv = [&](KVRegs& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_start(tile);
@@ -218,61 +228,74 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         *reinterpret_cast<uint4*>(&sVWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     };
     // state copy for the inter term: KV^T[value col][key row], 4 consecutive key rows per lane
-    auto write_state_copy = [&](int buf) __attribute__((always_inline)) {
+    auto write_state_copy = [&](auto swc, const f32x4* st, int buf) __attribute__((always_inline)) {
+        constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
 #pragma unroll
-        for (int k = 0; k < MAXT; ++k) {
-            if (k < st_count) {
-                const int q = st_first + k;
-                uint32_t h01, l01, h23, l23;
-                split2(st[k][0], st[k][1], h01, l01);
-                split2(st[k][2], st[k][3], h23, l23);
-                const int off = (16 * (q & 1) + lr) * SS + 16 * (q >> 1) + 4 * g;
-                *reinterpret_cast<uint2*>(&sSh[buf][off]) = make_uint2(h01, h23);
-                *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(l01, l23);
-            }
+        for (int k = 0; k < C; ++k) {
+            const int q = F + k;
+            uint32_t h01, l01, h23, l23;
+            split2(st[k][0], st[k][1], h01, l01);
+            split2(st[k][2], st[k][3], h23, l23);
+            const int off = ss_off(16 * (q & 1) + lr, 16 * (q >> 1) + 4 * g);
+            *reinterpret_cast<uint2*>(&sSh[buf][off]) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(l01, l23);
         }
     };
-    auto store_state = [&](float* dst) __attribute__((always_inline)) {
+    auto store_state = [&](auto swc, const f32x4* st, float* dst) __attribute__((always_inline)) {
+        constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
 #pragma unroll
-        for (int k = 0; k < MAXT; ++k) {
-            if (k < st_count) {
-                const int q = st_first + k;
+        for (int k = 0; k < C; ++k) {
+            const int q = F + k;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    dst[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] = st[k][t];
-            }
+            for (int t = 0; t < 4; ++t)
+                dst[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] = st[k][t];
+        }
+    };
+    auto load_state = [&](auto swc, f32x4* st, const float* src) __attribute__((always_inline)) {
+        constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const int q = F + k;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                st[k][t] = src ? src[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] : 0.f;
         }
     };
     // KV <- lambda^L KV + K^T (W V) on this wave's state tiles
-    auto update_state = [&](int buf, int tile) __attribute__((always_inline)) {
+    auto update_state = [&](auto swc, f32x4* st, int buf, int tile) __attribute__((always_inline)) {
+        constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
         const int L = tile_len(tile);
         const float dl = decay_pow(nsl, (float)L);
 #pragma unroll
-        for (int k = 0; k < MAXT; ++k)
-            if (k < st_count) st[k] *= dl;
+        for (int k = 0; k < C; ++k) st[k] *= dl;
+        // key-row tiles it0..it1 cover this wave's state tiles; the two value-column tiles of one
+        // key-row tile share its K^T operand
+        constexpr int IT0 = F >> 1, NIT = ((F + C - 1) >> 1) - IT0 + 1;
+        bf16x8 vh[2][2], vl[2][2], ka[2][NIT];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int k0 = 32 * ks + 8 * g;
-            bf16x8 vh[2], vl[2];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
                 const int o = (k0 + tr_row) * VS + 16 * jt + tr_col;
-                vh[jt] = join(lds_tr(&sVWh[buf][o]), lds_tr(&sVWh[buf][o + 4 * VS]));
-                vl[jt] = join(lds_tr(&sVWl[buf][o]), lds_tr(&sVWl[buf][o + 4 * VS]));
+                vh[ks][jt] = join(lds_tr(&sVWh[buf][o]), lds_tr(&sVWh[buf][o + 4 * VS]));
+                vl[ks][jt] = join(lds_tr(&sVWl[buf][o]), lds_tr(&sVWl[buf][o + 4 * VS]));
             }
 #pragma unroll
-            for (int k = 0; k < MAXT; ++k) {
-                if (k < st_count) {
-                    const int q = st_first + k;
-                    const int o = (k0 + tr_row) * KS + 16 * (q >> 1) + tr_col;
-                    const bf16x8 ka = join(lds_tr(&sK[buf][o]), lds_tr(&sK[buf][o + 4 * KS]));
-                    const bf16x8 bh = (q & 1) ? vh[1] : vh[0];
-                    const bf16x8 bl = (q & 1) ? vl[1] : vl[0];
-                    st[k] = mfma(ka, bh, st[k]);
-                    st[k] = mfma(ka, bl, st[k]);
-                }
+            for (int n = 0; n < NIT; ++n) {
+                const int o = (k0 + tr_row) * KS + 16 * (IT0 + n) + tr_col;
+                ka[ks][n] = join(lds_tr(&sK[buf][o]), lds_tr(&sK[buf][o + 4 * KS]));
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const int q = F + k;
+                st[k] = mfma(ka[ks][(q >> 1) - IT0], vh[ks][q & 1], st[k]);
+                st[k] = mfma(ka[ks][(q >> 1) - IT0], vl[ks][q & 1], st[k]);
+            }
     };
 
     // ------------------------------------------------------------------ output waves
@@ -299,12 +322,30 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ks);
     };
     // Outputs of tile `tile` from LDS buffer `buf`; R.q is refilled with tile next_q once consumed.
-    auto compute_out = [&](QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
+    auto compute_out = [&](auto wc, QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
+        constexpr int W = decltype(wc)::value;
         const int64_t t0 = tile_start(tile);
         const int L = tile_len(tile);
         bf16x8 qf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, R.q[ks]);
+        // Issue every LDS operand read of the inter and score products up front (the fence keeps
+        // the scheduler from sinking them next to their MFMAs, which would expose each read's
+        // latency in turn).
+        bf16x8 sh[2][4], sl[2][4], kop[W + 1][4];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = ss_off(16 * jt + lr, 32 * ks + 8 * g);
+                sh[jt][ks] = lds8(&sSh[buf][off]);
+                sl[jt][ks] = lds8(&sSl[buf][off]);
+            }
+#pragma unroll
+        for (int ct = 0; ct <= W; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kop[ct][ks] = lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ks + 8 * g]);
+        __builtin_amdgcn_sched_barrier(0);
         // inter-tile term: Q KV, rows scaled by lambda^(r+1)
         f32x4 acc[2];
 #pragma unroll
@@ -312,22 +353,18 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int off = (16 * jt + lr) * SS + 32 * ks + 8 * g;
-                acc[jt] = mfma(qf[ks], lds8(&sSh[buf][off]), acc[jt]);
-                acc[jt] = mfma(qf[ks], lds8(&sSl[buf][off]), acc[jt]);
+                acc[jt] = mfma(qf[ks], sh[jt][ks], acc[jt]);
+                acc[jt] = mfma(qf[ks], sl[jt][ks], acc[jt]);
             }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[jt][t] *= drow[t];
         }
-        // intra-tile scores S^T for key tiles 0..w (later key tiles are fully masked)
+        // intra-tile scores S^T for key tiles 0..W (later key tiles are fully masked)
         float p[4][4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            if (ct <= w) {
+            if (ct <= W) {
                 f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    s = mfma(lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ks + 8 * g]), qf[ks], s);
+                for (int ks = 0; ks < 4; ++ks) s = mfma(kop[ct][ks], qf[ks], s);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) p[ct][t] = s[t] * dmask[ct][t];
             } else {
@@ -335,26 +372,34 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
                 for (int t = 0; t < 4; ++t) p[ct][t] = 0.f;
             }
         }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[jt][t] *= drow[t];
         if (next_q < n_tiles) load_q(R, next_q);
         // intra-tile output P V (keys 32k2 + {4g..4g+3, 16+4g..16+4g+3} in each 32-key step)
+        constexpr int NK2 = W / 2 + 1;
+        bf16x8 vop[NK2][2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            if (2 * k2 <= w) {
-                uint32_t hh[4], ll[4];
-                split2(p[2 * k2][0], p[2 * k2][1], hh[0], ll[0]);
-                split2(p[2 * k2][2], p[2 * k2][3], hh[1], ll[1]);
-                split2(p[2 * k2 + 1][0], p[2 * k2 + 1][1], hh[2], ll[2]);
-                split2(p[2 * k2 + 1][2], p[2 * k2 + 1][3], hh[3], ll[3]);
-                const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
-                const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+        for (int k2 = 0; k2 < NK2; ++k2)
 #pragma unroll
-                for (int jt = 0; jt < 2; ++jt) {
-                    const u16* vb = &sV[buf][tr_row * VS + 16 * jt + tr_col];
-                    const bf16x8 vo = join(lds_tr(vb + (32 * k2 + 4 * g) * VS),
-                                           lds_tr(vb + (32 * k2 + 16 + 4 * g) * VS));
-                    acc[jt] = mfma(ph, vo, acc[jt]);
-                    acc[jt] = mfma(pl, vo, acc[jt]);
-                }
+            for (int jt = 0; jt < 2; ++jt) {
+                const u16* vb = &sV[buf][tr_row * VS + 16 * jt + tr_col];
+                vop[k2][jt] = join(lds_tr(vb + (32 * k2 + 4 * g) * VS), lds_tr(vb + (32 * k2 + 16 + 4 * g) * VS));
+            }
+#pragma unroll
+        for (int k2 = 0; k2 < NK2; ++k2) {
+            uint32_t hh[4], ll[4];
+            split2(p[2 * k2][0], p[2 * k2][1], hh[0], ll[0]);
+            split2(p[2 * k2][2], p[2 * k2][3], hh[1], ll[1]);
+            split2(p[2 * k2 + 1][0], p[2 * k2 + 1][1], hh[2], ll[2]);
+            split2(p[2 * k2 + 1][2], p[2 * k2 + 1][3], hh[3], ll[3]);
+            const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
+            const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                acc[jt] = mfma(ph, vop[k2][jt], acc[jt]);
+                acc[jt] = mfma(pl, vop[k2][jt], acc[jt]);
             }
         }
         // output tile: stage this wave's 16 rows, then 16-byte stores
@@ -362,10 +407,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                sO[(16 * w + 4 * g + t) * OS + 16 * jt + lr] = (u16)f32_to_bits(acc[jt][t]);
+                sO[(16 * W + 4 * g + t) * OS + 16 * jt + lr] = (u16)f32_to_bits(acc[jt][t]);
         wave_lds_sync();
         {
-            const int rr = 16 * w + (l >> 2), cc = 8 * (l & 3);
+            const int rr = 16 * W + (l >> 2), cc = 8 * (l & 3);
             const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + t0 * sn, (int64_t)L * row_bytes);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
@@ -377,31 +422,25 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     // Each role runs its own loop (so their registers do not overlap); both pass the same
     // barriers: one after the prologue and one between consecutive tiles.  Tiles alternate
     // between LDS buffers 0 and 1 and between register sets A and B.
-    if (is_state) {
+    auto state_loop = [&](auto swc) __attribute__((always_inline)) {
+        f32x4 st[st_count(decltype(swc)::value)];
         const float* src = nullptr;
         if (MODE != kModeLocal) src = (a.n_chunks > 1) ? a.ws + (u * a.n_chunks + j) * d2 : a.kv + u * d2;
-#pragma unroll
-        for (int k = 0; k < MAXT; ++k) {
-            if (k < st_count) {
-                const int q = st_first + k;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    st[k][t] = src ? src[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] : 0.f;
-            }
-        }
+        load_state(swc, st, src);
         KVRegs RA, RB;
         load_kv(RA, 0);
         if (n_tiles > 1) load_kv(RB, 1);
         stage_tile(RA, 0, 0);
-        if (OUT) write_state_copy(0);
+        if (OUT) write_state_copy(swc, st, 0);
         __syncthreads();
         auto step = [&](KVRegs& R, KVRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
             if (tile + 2 < n_tiles) load_kv(R, tile + 2);
-            update_state(buf, tile);
-            if (OUT && tile + 1 < n_tiles) write_state_copy(buf ^ 1);
+            update_state(swc, st, buf, tile);
+            if (OUT && tile + 1 < n_tiles) write_state_copy(swc, st, buf ^ 1);
             if (MODE != kModeLocal && a.ckpt) {
                 const int64_t end = tile_start(tile) + tile_len(tile);
-                if (end % a.ckpt_every == 0) store_state(a.ckpt + (u * a.n_ckpt + (end / a.ckpt_every - 1)) * d2);
+                if (end % a.ckpt_every == 0)
+                    store_state(swc, st, a.ckpt + (u * a.n_ckpt + (end / a.ckpt_every - 1)) * d2);
             }
             if (tile + 1 < n_tiles) stage_tile(Rn, buf ^ 1, tile + 1);
         };
@@ -413,21 +452,34 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             if (tile + 2 >= n_tiles) break;
             __syncthreads();
         }
-        if (MODE == kModeLocal) store_state(a.ws + (u * a.n_chunks + j + 1) * d2);
-        else if (j == a.n_chunks - 1) store_state(a.kv + u * d2);
-    } else if (OUT) {
+        if (MODE == kModeLocal) store_state(swc, st, a.ws + (u * a.n_chunks + j + 1) * d2);
+        else if (j == a.n_chunks - 1) store_state(swc, st, a.kv + u * d2);
+    };
+    auto out_loop = [&](auto wc) __attribute__((always_inline)) {
         QRegs QA, QB;
         load_q(QA, 0);
         if (n_tiles > 1) load_q(QB, 1);
         __syncthreads();
         for (int tile = 0;; tile += 2) {
-            compute_out(QA, 0, tile, tile + 2);
+            compute_out(wc, QA, 0, tile, tile + 2);
             if (tile + 1 >= n_tiles) break;
             __syncthreads();
-            compute_out(QB, 1, tile + 1, tile + 3);
+            compute_out(wc, QB, 1, tile + 1, tile + 3);
             if (tile + 2 >= n_tiles) break;
             __syncthreads();
         }
+    };
+    // Each wave runs a loop specialised to its role and index (static work lists, no per-tile
+    // branches); all loops pass the same barriers: one after the prologue and one between tiles.
+    switch (w) {
+    case 0: if constexpr (OUT) out_loop(IntC<0>{}); else state_loop(IntC<0>{}); break;
+    case 1: if constexpr (OUT) out_loop(IntC<1>{}); else state_loop(IntC<1>{}); break;
+    case 2: if constexpr (OUT) out_loop(IntC<2>{}); else state_loop(IntC<2>{}); break;
+    case 3: if constexpr (OUT) out_loop(IntC<3>{}); else state_loop(IntC<3>{}); break;
+    case 4: state_loop(IntC<0>{}); break;
+    case 5: state_loop(IntC<1>{}); break;
+    case 6: state_loop(IntC<2>{}); break;
+    default: state_loop(IntC<3>{}); break;
     }
 }
 
