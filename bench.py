@@ -31,6 +31,52 @@ BYTES_PER_TOKEN_HEAD = 4 * 128 * 2   # q, k, v read + o write, bf16, d = 128
 DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 4 * 128 * 2   # state read + write, q/k/v/o
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_SOURCE = os.path.join(ROOT, "long_context_la_amd", "csrc", "la_prefill_bf16.hip")
+
+
+def source_digest(path=PREFILL_SOURCE):
+    import hashlib
+
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per prefill launch from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain copy of known
+    size), or None when there is none for this workload or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"prefill_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, _, val = line.partition("=")
+            vals[key.strip()] = val.strip()
+    try:
+        if vals.get("kernel_source_sha256_16") != source_digest():
+            return None
+        fetch = float(vals["fetch_kib_per_dispatch"]) * 1024 * float(vals["copy_fetch_factor"])
+        write = float(vals["write_kib_per_dispatch"]) * 1024 * float(vals["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def copy_probe(device, gib=4, reps=3):
+    """A plain device copy of known size, for calibrating the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps}), flush=True)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -182,6 +228,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences would "
@@ -193,8 +241,11 @@ def main():
     import long_context_la_amd as la
     import synth
 
-    la.lib()
     device = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(device)
+        return
+    la.lib()
     w = synth.WORKLOADS[args.workload]
     ms, kernel_ms, n_chunks = time_prefill(w, args.steps, args.warmup, device)
     token_heads = w.batch * w.heads * w.n
@@ -222,7 +273,7 @@ def main():
         "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": alg_bytes / (kernel_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
     }
     if not args.no_decode:
         wd = synth.WORKLOADS["decode"]
