@@ -189,6 +189,14 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int64_t t0 = t_begin + (int64_t)tile * BK;
         return (int)((t_end - t0 < BK) ? t_end - t0 : BK);
     };
+    // Bytes of a tile's rows that lie inside the chunk: 0 for tiles past its end, whose loads
+    // then return zeros without touching memory.  Prefetches are therefore issued every step,
+    // unconditionally, which lets the compiler wait for exactly the loads a step consumes rather
+    // than for every outstanding load and store.
+    auto tile_bytes = [&](int tile) __attribute__((always_inline)) {
+        const int L = tile_len(tile);
+        return (int64_t)(L > 0 ? L : 0) * row_bytes;
+    };
 
     // ------------------------------------------------------------------ state waves
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
@@ -199,9 +207,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 
     auto load_kv = [&](KVRegs& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_start(tile);
-        const int L = tile_len(tile);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, (int64_t)L * row_bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, (int64_t)L * row_bytes);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, tile_bytes(tile));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, tile_bytes(tile));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int c = st_id + 256 * m;
@@ -315,8 +322,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     }
     auto load_q = [&](QRegs& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_start(tile);
-        const int L = tile_len(tile);
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, (int64_t)L * row_bytes);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, tile_bytes(tile));
         const uint32_t off = (uint32_t)(16 * w + lr) * row_bytes + 16u * g;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ks);
@@ -325,7 +331,6 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     auto compute_out = [&](auto wc, QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
         const int64_t t0 = tile_start(tile);
-        const int L = tile_len(tile);
         bf16x8 qf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, R.q[ks]);
@@ -376,7 +381,11 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[jt][t] *= drow[t];
-        if (next_q < n_tiles) load_q(R, next_q);
+        // (the fences keep the refill in program order: were it hoisted above the products that
+        // read the old values, the two would need separate registers and a copy that waits)
+        __builtin_amdgcn_sched_barrier(0);
+        load_q(R, next_q);
+        __builtin_amdgcn_sched_barrier(0);
         // intra-tile output P V (keys 32k2 + {4g..4g+3, 16+4g..16+4g+3} in each 32-key step)
         constexpr int NK2 = W / 2 + 1;
         bf16x8 vop[NK2][2];
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         {
             const int rr = 16 * W + (l >> 2), cc = 8 * (l & 3);
             const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
-            const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + t0 * sn, (int64_t)L * row_bytes);
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + t0 * sn, tile_bytes(tile));
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
                                                    (int)((uint32_t)rr * row_bytes + 2u * cc), 0, 0);
         }
@@ -429,12 +438,16 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         load_state(swc, st, src);
         KVRegs RA, RB;
         load_kv(RA, 0);
-        if (n_tiles > 1) load_kv(RB, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_kv(RB, 1);
+        __builtin_amdgcn_sched_barrier(0);
         stage_tile(RA, 0, 0);
         if (OUT) write_state_copy(swc, st, 0);
         __syncthreads();
         auto step = [&](KVRegs& R, KVRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
-            if (tile + 2 < n_tiles) load_kv(R, tile + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            load_kv(R, tile + 2);
+            __builtin_amdgcn_sched_barrier(0);
             update_state(swc, st, buf, tile);
             if (OUT && tile + 1 < n_tiles) write_state_copy(swc, st, buf ^ 1);
             if (MODE != kModeLocal && a.ckpt) {
@@ -444,30 +457,32 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
             if (tile + 1 < n_tiles) stage_tile(Rn, buf ^ 1, tile + 1);
         };
-        for (int tile = 0;; tile += 2) {
+        int tile = 0;
+        for (; tile + 2 <= n_tiles; tile += 2) {
             step(RA, RB, 0, tile);
-            if (tile + 1 >= n_tiles) break;
             __syncthreads();
             step(RB, RA, 1, tile + 1);
-            if (tile + 2 >= n_tiles) break;
             __syncthreads();
         }
+        if (tile < n_tiles) step(RA, RB, 0, tile);
         if (MODE == kModeLocal) store_state(swc, st, a.ws + (u * a.n_chunks + j + 1) * d2);
         else if (j == a.n_chunks - 1) store_state(swc, st, a.kv + u * d2);
     };
     auto out_loop = [&](auto wc) __attribute__((always_inline)) {
         QRegs QA, QB;
         load_q(QA, 0);
-        if (n_tiles > 1) load_q(QB, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_q(QB, 1);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        for (int tile = 0;; tile += 2) {
+        int tile = 0;
+        for (; tile + 2 <= n_tiles; tile += 2) {
             compute_out(wc, QA, 0, tile, tile + 2);
-            if (tile + 1 >= n_tiles) break;
             __syncthreads();
             compute_out(wc, QB, 1, tile + 1, tile + 3);
-            if (tile + 2 >= n_tiles) break;
             __syncthreads();
         }
+        if (tile < n_tiles) compute_out(wc, QA, 0, tile, tile + 2);
     };
     // Each wave runs a loop specialised to its role and index (static work lists, no per-tile
     // branches); all loops pass the same barriers: one after the prologue and one between tiles.
