@@ -141,7 +141,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 template <int N> struct IntC { static constexpr int value = N; };
 
-struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32ks + 8g .. +7
+// The four value slices of a head read the same Q and K rows at nearly the same time; each slice
+// walks the 64-byte column blocks (Q) and 16-row blocks (K) starting at its own index, so that the
+// simultaneous requests of sibling slices fall on different cache lines.
+struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32((ks+slice)%4) + 8g .. +7
 struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
 
 template <int MODE>
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, tile_bytes(tile));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int c = st_id + 256 * m;
+            const int c = st_id + 256 * ((m + slice) & 3);
             R.k[m] = buf_load16(rk, (uint32_t)(c >> 4) * row_bytes + 16u * (c & 15));
         }
         R.v = buf_load16(rv, (uint32_t)(st_id >> 2) * row_bytes + 16u * (st_id & 3));
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int L = tile_len(tile);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int c = st_id + 256 * m;
+            const int c = st_id + 256 * ((m + slice) & 3);
             *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + 8 * (c & 15)]) = R.k[m];
         }
         const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, tile_bytes(tile));
         const uint32_t off = (uint32_t)(16 * w + lr) * row_bytes + 16u * g;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ks);
+        for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ((ks + slice) & 3));
     };
     // Outputs of tile `tile` from LDS buffer `buf`; R.q is refilled with tile next_q once consumed.
     auto compute_out = [&](auto wc, QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
@@ -342,14 +345,15 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int off = ss_off(16 * jt + lr, 32 * ks + 8 * g);
+                const int off = ss_off(16 * jt + lr, 32 * ((ks + slice) & 3) + 8 * g);
                 sh[jt][ks] = lds8(&sSh[buf][off]);
                 sl[jt][ks] = lds8(&sSl[buf][off]);
             }
 #pragma unroll
         for (int ct = 0; ct <= W; ++ct)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kop[ct][ks] = lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ks + 8 * g]);
+            for (int ks = 0; ks < 4; ++ks)
+                kop[ct][ks] = lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ((ks + slice) & 3) + 8 * g]);
         __builtin_amdgcn_sched_barrier(0);
         // inter-tile term: Q KV, rows scaled by lambda^(r+1)
         f32x4 acc[2];
