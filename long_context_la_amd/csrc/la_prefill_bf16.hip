@@ -29,7 +29,10 @@
 // other's work).  Output waves 0..3: wave w owns query rows 16w..16w+15 of
 // each 64-token tile -- scores, masking, P V, the inter-tile term and the
 // output store; Q goes straight from global memory into registers in operand
-// layout (B operand of S^T, A operand of Q KV).  State waves 4..7: the global
+// layout (B operand of S^T and of the transposed inter product).  The outputs
+// are accumulated transposed, O^T = KV^T Q^T + V^T P^T, so a lane holds four
+// consecutive value columns of one row and stages them with one 8-byte LDS
+// write before the 16-byte global stores.  State waves 4..7: the global
 // loads and LDS staging of K and V, the decay-weighted W V, and the state
 // update, with the state's 16 tiles of 16x16 split 6/5/3/2 so that each SIMD
 // (output wave w + state wave w) issues the same 48 MFMAs per tile.  The state
@@ -43,8 +46,8 @@
 // as A and B agree, which is used twice:
 //   * S is computed transposed (S^T = K Q^T), so a lane's accumulators hold
 //     one query row r and keys {4g..4g+3} and {16+4g..16+4g+3} of two
-//     adjacent 16-key tiles -- an A operand of P.V over a 32-key step in that
-//     k order, with no data movement;
+//     adjacent 16-key tiles -- the B operand of V^T P^T over a 32-key step in
+//     that k order, with no data movement;
 //   * the k = token operands (V for P.V; K^T and W V for the state update) are
 //     read from row-major LDS tiles with the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16): within each 16-lane group, the lane that supplies
@@ -54,9 +57,11 @@
 //     staged as plain row copies and any k order is available.
 // Global traffic uses buffer loads/stores on a per-tile resource whose size
 // ends at the tile's last valid row, so the rows of a ragged last tile read as
-// zero without branches.  Loads run two tiles ahead (two register sets), tiles
-// are double-buffered in LDS, one barrier per tile.  Per-element decay factors
-// come from per-lane tables computed once per workgroup.
+// zero without branches.  Loads run two tiles ahead (two register sets) and are
+// issued every step, also past the end of the chunk (zero-size resource), so the
+// compiler's waits cover exactly the loads a step consumes; tiles are double-
+// buffered in LDS, one barrier per tile.  Per-element decay factors come from
+// per-lane tables computed once per workgroup.
 #include "la_common.h"
 
 namespace la {
@@ -75,7 +80,9 @@ constexpr int KS = D + 16;  // row stride (elements) of the row-major K tile: 28
 constexpr int VS = SW + 16;  // row stride of the V, W V tiles: 96 B (same reason)
 constexpr int SS = D;       // row stride of the state copies (stored KV^T: [value col][key row]); the
                             // 16-byte chunk index is XORed with row % 16 (see ss_off)
-constexpr int OS = SW + 8;  // row stride of the output staging tile
+constexpr int OS = SW + 16;  // row stride of the output staging tile: 96 B, so that 16 rows x 32 B of
+                             // 8-byte writes and 16 rows x 64 B of 16-byte reads spread evenly over
+                             // the banks
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descriptor word 3
 
 __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -310,8 +317,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 
     // ------------------------------------------------------------------ output waves
     // dmask[ct][t] = lambda^(r - c) for query r = 16w + lr and key c = 16ct + 4g + t (0 if c > r);
-    // drow[t] = lambda^(r+1) for output rows r = 16w + 4g + t.
-    float dmask[4][4], drow[4];
+    // drow = lambda^(r+1) for this lane's output row r = 16w + lr.
+    float dmask[4][4], drow = 0.f;
     if (OUT && !is_state) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
@@ -320,8 +327,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
                 const int e = 16 * (w - ct) + lr - 4 * g - t;
                 dmask[ct][t] = (e >= 0) ? decay_pow(nsl, (float)e) : 0.f;
             }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) drow[t] = decay_pow(nsl, (float)(16 * w + 4 * g + t + 1));
+        drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
     auto load_q = [&](QRegs& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_start(tile);
@@ -355,15 +361,16 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             for (int ks = 0; ks < 4; ++ks)
                 kop[ct][ks] = lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ((ks + slice) & 3) + 8 * g]);
         __builtin_amdgcn_sched_barrier(0);
-        // inter-tile term: Q KV, rows scaled by lambda^(r+1)
+        // inter-tile term, transposed: (Q KV)^T = KV^T Q^T, so a lane's accumulators hold one output
+        // row (query lr) and four consecutive value columns 16jt + 4g..+3; rows scaled by lambda^(r+1)
         f32x4 acc[2];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
             acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                acc[jt] = mfma(qf[ks], sh[jt][ks], acc[jt]);
-                acc[jt] = mfma(qf[ks], sl[jt][ks], acc[jt]);
+                acc[jt] = mfma(sh[jt][ks], qf[ks], acc[jt]);
+                acc[jt] = mfma(sl[jt][ks], qf[ks], acc[jt]);
             }
         }
         // intra-tile scores S^T for key tiles 0..W (later key tiles are fully masked)
@@ -382,15 +389,14 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
         }
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[jt][t] *= drow[t];
+        for (int jt = 0; jt < 2; ++jt) acc[jt] *= drow;
         // (the fences keep the refill in program order: were it hoisted above the products that
         // read the old values, the two would need separate registers and a copy that waits)
         __builtin_amdgcn_sched_barrier(0);
         load_q(R, next_q);
         __builtin_amdgcn_sched_barrier(0);
-        // intra-tile output P V (keys 32k2 + {4g..4g+3, 16+4g..16+4g+3} in each 32-key step)
+        // intra-tile output, transposed like the inter term: (P V)^T = V^T P^T (keys 32k2 +
+        // {4g..4g+3, 16+4g..16+4g+3} in each 32-key step; the S^T accumulators are P^T's operand)
         constexpr int NK2 = W / 2 + 1;
         bf16x8 vop[NK2][2];
 #pragma unroll
@@ -411,16 +417,15 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
-                acc[jt] = mfma(ph, vop[k2][jt], acc[jt]);
-                acc[jt] = mfma(pl, vop[k2][jt], acc[jt]);
+                acc[jt] = mfma(vop[k2][jt], ph, acc[jt]);
+                acc[jt] = mfma(vop[k2][jt], pl, acc[jt]);
             }
         }
-        // output tile: stage this wave's 16 rows, then 16-byte stores
+        // output tile: stage this wave's 16 rows (8-byte runs of 4 columns), then 16-byte stores
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                sO[(16 * W + 4 * g + t) * OS + 16 * jt + lr] = (u16)f32_to_bits(acc[jt][t]);
+            *reinterpret_cast<uint2*>(&sO[(16 * W + lr) * OS + 16 * jt + 4 * g]) =
+                make_uint2(cvt2(acc[jt][0], acc[jt][1]), cvt2(acc[jt][2], acc[jt][3]));
         wave_lds_sync();
         {
             const int rr = 16 * W + (l >> 2), cc = 8 * (l & 3);
