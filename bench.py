@@ -31,6 +31,12 @@ BYTES_PER_TOKEN_HEAD = 4 * 128 * 2   # q, k, v read + o write, bf16, d = 128
 DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 4 * 128 * 2   # state read + write, q/k/v/o
 
 
+# Packed variable-length leg: the full layer's 131072-token budget split into 18 sequences of
+# halving lengths (65536 ... 1, plus one more single token), packed back to back in one launch.
+VARLEN_LENGTHS = [65536 >> i for i in range(17)] + [1]
+# Mixed batch of the pages' example: 20 cached inputs, two of them 50 tokens, the rest one token.
+MIXED_LENGTHS = [50, 50] + [1] * 18
+
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_SOURCE = os.path.join(ROOT, "long_context_la_amd", "csrc", "la_prefill_bf16.hip")
 
@@ -148,8 +154,108 @@ def time_prefill(w, steps, warmup, device):
     torch.cuda.synchronize()
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     n_chunks = -(-w.n // la.la_prefill_chunk_tokens(la.LA_BF16, w.batch, w.heads, w.n, w.d))
+    varlen = None
+    if w.batch == 1 and sum(VARLEN_LENGTHS) == w.n:
+        varlen = time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device)
     del q, k, v, o, ws
-    return ms, kernel_ms, n_chunks
+    return ms, kernel_ms, n_chunks, varlen
+
+
+def time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device):
+    """The same tokens cut into VARLEN_LENGTHS sequences: la_prefill_varlen on head-major views
+    ([T,H,d] with stride_h = T*d), every sequence from a zero state."""
+    import torch
+
+    import long_context_la_amd as la
+
+    qv, kv_, vv, ov = (t[0].permute(1, 0, 2) for t in (q, k, v, o))
+    cu = [0] + list(np.cumsum(VARLEN_LENGTHS))
+    n_seq = len(VARLEN_LENGTHS)
+    kv = torch.zeros(n_seq, w.heads, w.d, w.d, dtype=torch.float32, device=device)
+    ws = torch.empty(la.la_prefill_varlen_workspace_size(la.LA_BF16, cu, w.heads, w.d), dtype=torch.uint8,
+                     device=device)
+    stream = torch.cuda.current_stream(device)
+    for _ in range(warmup):
+        la.la_prefill_varlen(qv, kv_, vv, slopes, kv, cu, o=ov, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        la.la_state_init(kv)
+        a.record(stream)
+        la.la_prefill_varlen(qv, kv_, vv, slopes, kv, cu, o=ov, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    chunk = la.la_prefill_varlen_chunk_tokens(la.LA_BF16, cu, w.heads, w.d)
+    log(f"varlen packed: {n_seq} sequences, {w.n} tokens: {ms:.3f} ms (chunk {chunk})")
+    return {"workload": f"{n_seq} packed sequences ({VARLEN_LENGTHS[0]}..1 tokens, halving) = {w.n} tokens, "
+                        f"{w.heads} heads, d={w.d}, bf16, zero incoming states",
+            "ms_per_step": ms, "tokens_per_s": w.n / (ms * 1e-3),
+            "hbm_GBs": BYTES_PER_TOKEN_HEAD * w.heads * w.n / (ms * 1e-3) / 1e9,
+            "hbm_frac": BYTES_PER_TOKEN_HEAD * w.heads * w.n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "chunk_tokens": chunk}
+
+
+def time_mixed(device, heads=64, d=128, iters=200):
+    """MIXED_LENGTHS for one layer: (a) all 20 sequences through one varlen prefill launch, (b) the
+    18 single-token ones through la_decode and the two 50-token ones through la_prefill_varlen on
+    two streams (mixed_step with two streams), (c) the same two calls one after the other on one
+    stream (mixed_step's default)."""
+    import torch
+
+    import long_context_la_amd as la
+    import synth
+
+    def packed(lengths, seed):
+        cu = [0] + list(np.cumsum(lengths))
+        arrs = []
+        for t in (synth.Q, synth.K, synth.V):
+            parts = [synth.generate(t, seed, d, b0=s, nb=1, nh=heads, nt=n, dtype="bf16")[0].transpose(1, 0, 2)
+                     for s, n in enumerate(lengths)]
+            arrs.append(upload_bf16(np.ascontiguousarray(np.concatenate(parts, axis=0)), device))
+        return arrs, cu
+
+    slopes = torch.from_numpy(np.array([2.0 ** (-(h + 1) / 8) for h in range(heads)], dtype=np.float32)).to(device)
+    long_n = [n for n in MIXED_LENGTHS if n > 1]
+    n_short = len(MIXED_LENGTHS) - len(long_n)
+    (qa, ka, va), cu_all = packed(MIXED_LENGTHS, 31)
+    oa = torch.empty_like(qa)
+    kv_all = torch.zeros(len(MIXED_LENGTHS), heads, d, d, dtype=torch.float32, device=device)
+    ws_all = torch.empty(la.la_prefill_varlen_workspace_size(la.LA_BF16, cu_all, heads, d), dtype=torch.uint8,
+                         device=device)
+    (qp, kp, vp), cu_p = packed(long_n, 32)
+    op = torch.empty_like(qp)
+    kv_p = torch.zeros(len(long_n), heads, d, d, dtype=torch.float32, device=device)
+    ws_p = torch.empty(la.la_prefill_varlen_workspace_size(la.LA_BF16, cu_p, heads, d), dtype=torch.uint8,
+                       device=device)
+    qd, kd, vd = (upload_bf16(synth.generate(t, 33, d, nb=n_short, nh=heads, nt=1, dtype="bf16")[:, :, 0], device)
+                  for t in (synth.Q, synth.K, synth.V))
+    od = torch.empty_like(qd)
+    kv_d = torch.zeros(n_short, heads, d, d, dtype=torch.float32, device=device)
+    streams = (torch.cuda.Stream(device), torch.cuda.Stream(device))
+    variants = {
+        "us_one_varlen_launch": lambda: la.la_prefill_varlen(qa, ka, va, slopes, kv_all, cu_all, o=oa, workspace=ws_all),
+        "us_separate_streams": lambda: la.mixed_step(slopes, decode=(qd, kd, vd, od, kv_d),
+                                                     prefill=(qp, kp, vp, op, kv_p, cu_p, ws_p), streams=streams),
+        "us_separate_kernels_one_stream": lambda: la.mixed_step(slopes, decode=(qd, kd, vd, od, kv_d),
+                                                                prefill=(qp, kp, vp, op, kv_p, cu_p, ws_p)),
+    }
+    res = {"workload": f"{len(MIXED_LENGTHS)} cached inputs: {len(long_n)} x {long_n[0]} tokens + {n_short} x 1 token, "
+                       f"{heads} heads, d={d}, bf16 (one layer)"}
+    stream = torch.cuda.current_stream(device)
+    for name, fn in variants.items():
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / iters
+    log("mixed batch: " + ", ".join(f"{k} {v:.1f}" for k, v in res.items() if k.startswith("us")))
+    return res
 
 
 def time_decode(w, steps, device, prefix_slab=16):
@@ -247,7 +353,7 @@ def main():
         return
     la.lib()
     w = synth.WORKLOADS[args.workload]
-    ms, kernel_ms, n_chunks = time_prefill(w, args.steps, args.warmup, device)
+    ms, kernel_ms, n_chunks, varlen = time_prefill(w, args.steps, args.warmup, device)
     token_heads = w.batch * w.heads * w.n
     tokens_s = w.batch * w.n / (ms * 1e-3)
     flops = model_flops_per_token_head(w.d) * token_heads
@@ -275,7 +381,10 @@ def main():
                      "unit": "GB/s", "frac": alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": measured_traffic(w.name)},
     }
+    if varlen is not None:
+        result["varlen"] = varlen
     if not args.no_decode:
+        result["mixed_batch"] = time_mixed(device)
         wd = synth.WORKLOADS["decode"]
         us = time_decode(wd, args.decode_steps, device)
         gbs = wd.batch * wd.heads * DECODE_BYTES_PER_UNIT / (us * 1e-6) / 1e9

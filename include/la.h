@@ -122,6 +122,45 @@ la_status la_prefill_ex(la_dtype dt, const void* q, const void* k, const void* v
                         int64_t chunk_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Packed variable-length prefill: n_seq sequences concatenated along the token
+ * axis without padding (section 3.2 of the page above packs variable-length
+ * samples back to back and tracks each one's offsets; section 3.3 runs long
+ * and short inputs with separate work sizes).  Sequence s owns packed tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1; each sequence starts from its own state
+ * kv[s][h] and leaves its final state there.  One launch (plus, when a long
+ * sequence is cut into chunks, a chunk-summary launch and a prefix combine)
+ * covers the whole batch, so short and long sequences share the GPU.
+ *   q, k, v, o : element (t, h, e) at base + t*stride_n + h*stride_h + e, t =
+ *                packed token index (e.g. [total][heads][d] has stride_n =
+ *                heads*d, stride_h = d); rules as for la_prefill.
+ *   cu_seqlens : HOST array of n_seq + 1 int64, cu_seqlens[0] = 0,
+ *                nondecreasing (empty sequences allowed: their state is left
+ *                unchanged).  Read during the call only.
+ *   kv         : [n_seq][heads][d][d] float32, read then overwritten.
+ *   workspace  : device scratch of at least la_prefill_varlen_workspace_size()
+ *                bytes (never 0 bytes: it also receives the chunk tables);
+ *                the call enqueues an asynchronous host-to-device copy of
+ *                those tables into it, so it must not be in use by other
+ *                work on other streams.
+ * No checkpoints.  Supported dtypes and d as for la_prefill.
+ */
+size_t la_prefill_varlen_workspace_size(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                        int64_t d);
+/* Chunk length the varlen prefill uses (sequences longer than it are chunked), -1 if invalid. */
+int64_t la_prefill_varlen_chunk_tokens(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                       int64_t d);
+la_status la_prefill_varlen(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                            int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
+                            int64_t stride_h, int64_t stride_n, const float* slopes, float* kv,
+                            void* workspace, size_t workspace_bytes, void* stream);
+/* As la_prefill_varlen with an explicit chunk length (0 = default, else a positive multiple of 64). */
+size_t la_prefill_varlen_workspace_size_ex(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                           int64_t d, int64_t chunk_tokens);
+la_status la_prefill_varlen_ex(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                               int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
+                               int64_t stride_h, int64_t stride_n, const float* slopes, float* kv,
+                               int64_t chunk_tokens, void* workspace, size_t workspace_bytes, void* stream);
+/*
  * One decode step per (b, h) (section 3.3 of the page above runs single-token
  * generation as its own kernel): kv <- lambda_h * kv + k^T v, then o = q . kv.
  *   q, k, v, o : contiguous [batch][heads][d] of dtype dt (o must not overlap

@@ -7,8 +7,10 @@ step of the computation runs in the library's gfx950 kernels -- there is no
 fallback: if the library is missing, every call raises.
 
 Names follow the C entry points: la_state_init, la_prefill,
-la_prefill_workspace_size, la_prefill_chunk_tokens, la_decode,
-la_status_string, la_last_error.
+la_prefill_workspace_size, la_prefill_chunk_tokens, la_prefill_varlen,
+la_prefill_varlen_workspace_size, la_prefill_varlen_chunk_tokens, la_decode,
+la_status_string, la_last_error.  mixed_step issues a decode group and a
+varlen prefill group on two streams (two library calls, nothing else).
 """
 from __future__ import annotations
 
@@ -28,7 +30,9 @@ LA_F32 = 0
 LA_BF16 = 1
 
 EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_size",
-            "la_prefill_workspace_size_ex", "la_prefill", "la_prefill_ex", "la_decode",
+            "la_prefill_workspace_size_ex", "la_prefill", "la_prefill_ex",
+            "la_prefill_varlen_workspace_size", "la_prefill_varlen_workspace_size_ex",
+            "la_prefill_varlen_chunk_tokens", "la_prefill_varlen", "la_prefill_varlen_ex", "la_decode",
             "la_status_string", "la_last_error"]
 
 _lib = None
@@ -62,6 +66,16 @@ def lib():
     L.la_prefill.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, p, sz, p]
     L.la_prefill_ex.restype = i32
     L.la_prefill_ex.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, i64, p, sz, p]
+    L.la_prefill_varlen_workspace_size.restype = sz
+    L.la_prefill_varlen_workspace_size.argtypes = [i32, i64, p, i64, i64]
+    L.la_prefill_varlen_workspace_size_ex.restype = sz
+    L.la_prefill_varlen_workspace_size_ex.argtypes = [i32, i64, p, i64, i64, i64]
+    L.la_prefill_varlen_chunk_tokens.restype = i64
+    L.la_prefill_varlen_chunk_tokens.argtypes = [i32, i64, p, i64, i64]
+    L.la_prefill_varlen.restype = i32
+    L.la_prefill_varlen.argtypes = [i32, p, p, p, p, i64, p, i64, i64, i64, i64, p, p, p, sz, p]
+    L.la_prefill_varlen_ex.restype = i32
+    L.la_prefill_varlen_ex.argtypes = [i32, p, p, p, p, i64, p, i64, i64, i64, i64, p, p, i64, p, sz, p]
     L.la_decode.restype = i32
     L.la_decode.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, p]
     L.la_status_string.restype = ctypes.c_char_p
@@ -168,3 +182,78 @@ def la_decode(q, k, v, slopes, kv, o, stream=None) -> None:
     st = lib().la_decode(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d, _ptr(slopes), _ptr(kv),
                          _stream_ptr(stream, q.device))
     _check(st, "la_decode")
+
+
+def _cu_array(cu_seqlens):
+    """cu_seqlens (list / numpy / CPU tensor) as a ctypes int64 array (host memory)."""
+    vals = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    return (ctypes.c_int64 * len(vals))(*vals), len(vals) - 1
+
+
+def la_prefill_varlen_workspace_size(dtype: int, cu_seqlens, heads: int, d: int, chunk_tokens: int = 0) -> int:
+    cu, n_seq = _cu_array(cu_seqlens)
+    return int(lib().la_prefill_varlen_workspace_size_ex(dtype, n_seq, cu, heads, d, chunk_tokens))
+
+
+def la_prefill_varlen_chunk_tokens(dtype: int, cu_seqlens, heads: int, d: int) -> int:
+    cu, n_seq = _cu_array(cu_seqlens)
+    return int(lib().la_prefill_varlen_chunk_tokens(dtype, n_seq, cu, heads, d))
+
+
+def la_prefill_varlen(q, k, v, slopes, kv, cu_seqlens, o=None, workspace=None, chunk_tokens: int = 0,
+                      stream=None) -> None:
+    """Packed variable-length prefill over q, k, v [total, H, d] (or any view with strides
+    (stride_n, stride_h, 1)); sequence s is rows cu_seqlens[s]:cu_seqlens[s+1].  Updates
+    kv [n_seq, H, d, d] in place and writes o (same shape/strides as q) unless it is None.
+    The workspace (la_prefill_varlen_workspace_size bytes) is allocated here if not given."""
+    import torch
+
+    _require_cuda(q, k, v, slopes, kv, o, workspace)
+    dt = _dtype_code(q)
+    T, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(-1) != 1:
+        raise ValueError("q, k, v must share strides with a contiguous last dimension")
+    if o is not None and (o.shape != q.shape or o.stride() != q.stride() or o.dtype != q.dtype):
+        raise ValueError("o must match q in shape, strides and dtype")
+    if slopes.dtype != torch.float32 or kv.dtype != torch.float32:
+        raise ValueError("slopes and kv must be float32")
+    cu, n_seq = _cu_array(cu_seqlens)
+    if cu[n_seq] != T:
+        raise ValueError("cu_seqlens[-1] must equal the packed token count")
+    need = int(lib().la_prefill_varlen_workspace_size_ex(dt, n_seq, cu, H, d, chunk_tokens))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sn, sh, _ = q.stride()
+    st = lib().la_prefill_varlen_ex(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), n_seq, cu, H, d, sh, sn,
+                                    _ptr(slopes), _ptr(kv), chunk_tokens, _ptr(workspace), ws_bytes,
+                                    _stream_ptr(stream, q.device))
+    _check(st, "la_prefill_varlen")
+
+
+def mixed_step(slopes, decode=None, prefill=None, streams=None) -> None:
+    """One step of a mixed batch, separated as section 3.3 of the MiniMax-01 summary page does:
+    the single-token sequences go to la_decode and the multi-token ones to la_prefill_varlen.
+    decode = (q, k, v, o, kv) with [B,H,d] tensors; prefill = (q, k, v, o, kv, cu_seqlens,
+    workspace or None).  With streams = (s0, s1) the two calls are issued on two streams that
+    first wait for, and are then joined back into, the current stream; with streams = None both
+    run on the current stream, one after the other (for small batches the cross-stream
+    synchronisation costs more than the overlap gains)."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+    if streams is not None:
+        for s in streams:
+            s.wait_stream(cur)
+    sd, sp = (None, None) if streams is None else streams
+    if decode is not None:
+        q, k, v, o, kv = decode
+        la_decode(q, k, v, slopes, kv, o, stream=sd)
+    if prefill is not None:
+        q, k, v, o, kv, cu, ws = prefill
+        la_prefill_varlen(q, k, v, slopes, kv, cu, o=o, workspace=ws, stream=sp)
+    if streams is not None:
+        for s in streams:
+            cur.wait_stream(s)

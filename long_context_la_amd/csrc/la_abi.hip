@@ -4,6 +4,7 @@
 
 #include <exception>
 #include <string>
+#include <vector>
 
 #include "la_common.h"
 
@@ -163,9 +164,194 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     return launch_status(run(o ? kModeOut : kModeState, p.n_chunks), "prefill launch");
 }
 
+// ---------------------------------------------------------------- packed variable-length batches
+// Page "MiniMax-01: Scaling Foundation Models with Lightning Attention | Summary", section 3.2
+// (data packing: samples concatenated without padding, each with its own offsets) and section
+// 3.3 (separate handling of long and short inputs): one launch covers every sequence; long
+// sequences are cut into chunks (the LASP+ combine of section 3.2), short ones run whole.
+struct VarPlan {
+    int64_t chunk = 0;         // chunk length (tokens) of every chunk but a sequence's last
+    int64_t total_chunks = 0;  // over all sequences
+    bool chunked = false;      // some sequence has more than one chunk
+    int slices = 0;
+    std::vector<int64_t> tab;  // ctab (5 per chunk) followed by stab (2 per sequence)
+};
+
+size_t varlen_table_bytes(const VarPlan& p) { return ((p.tab.size() * sizeof(int64_t) + 255) / 256) * 256; }
+
+size_t varlen_workspace_bytes(const VarPlan& p, int64_t heads, int64_t d)
+{
+    size_t b = varlen_table_bytes(p);
+    if (p.chunked) b += (size_t)p.total_chunks * (size_t)heads * (size_t)d * (size_t)d * sizeof(float);
+    return b;
+}
+
+la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
+                           int64_t chunk_override, VarPlan& p)
+{
+    if (n_seq < 1 || n_seq > (int64_t(1) << 24)) return fail(LA_ERR_INVALID_ARGUMENT, "n_seq must be in [1, 2^24]");
+    if (!cu) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens must not be NULL");
+    if (cu[0] != 0) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+    int64_t longest = 0, nonempty = 0;
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t n = cu[s + 1] - cu[s];
+        if (n < 0) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens must be nondecreasing");
+        longest = n > longest ? n : longest;
+        nonempty += n > 0;
+    }
+    la_status st = check_shape(dt, n_seq, heads, longest, d);
+    if (st != LA_OK) return st;
+    if (chunk_override < 0 || (chunk_override > 0 && chunk_override % kBlock != 0))
+        return fail(LA_ERR_INVALID_ARGUMENT, "chunk_tokens must be 0 or a positive multiple of 64");
+    p.slices = (int)(d / kSliceW);
+    const int64_t total = cu[n_seq];
+    int64_t chunk = longest;
+    if (chunk_override > 0) {
+        chunk = chunk_override;
+    } else if (nonempty * heads * p.slices < kTargetGroups && longest > kMinChunk) {
+        // about kTargetGroups workgroups over the whole batch, chunks no shorter than kMinChunk
+        int64_t c = (total * heads * p.slices + kTargetGroups - 1) / kTargetGroups;
+        c = ((c + kBlock - 1) / kBlock) * kBlock;
+        if (c < kMinChunk) c = kMinChunk;
+        chunk = c;
+    }
+    p.chunk = chunk > 0 ? chunk : kBlock;
+    p.tab.clear();
+    std::vector<int64_t> stab((size_t)(2 * n_seq));
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t n = cu[s + 1] - cu[s];
+        const int64_t nc = n == 0 ? 0 : (n <= p.chunk ? 1 : (n + p.chunk - 1) / p.chunk);
+        stab[2 * s] = p.total_chunks;
+        stab[2 * s + 1] = nc;
+        for (int64_t jj = 0; jj < nc; ++jj) {
+            const int64_t b = cu[s] + jj * p.chunk;
+            const int64_t e = (jj == nc - 1) ? cu[s + 1] : b + p.chunk;
+            p.tab.insert(p.tab.end(), {b, e, s, jj, stab[2 * s]});
+        }
+        p.total_chunks += nc;
+        if (nc > 1) p.chunked = true;
+    }
+    p.tab.insert(p.tab.end(), stab.begin(), stab.end());
+    return LA_OK;
+}
+
+la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                              int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
+                              int64_t sh, int64_t sn, const float* slopes, float* kv, int64_t chunk_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    VarPlan p;
+    la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, chunk_tokens, p);
+    if (s != LA_OK) return s;
+    if (!kv || !slopes) return fail(LA_ERR_INVALID_ARGUMENT, "kv and slopes must not be NULL");
+    if (p.total_chunks == 0) return LA_OK;  // every sequence empty
+    if (!q || !k || !v) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v must not be NULL");
+    const int64_t align = (dt == LA_BF16) ? 8 : 4;
+    if (sn < d || sh < 0 || sh % align || sn % align)
+        return fail(LA_ERR_INVALID_ARGUMENT, "strides must be >= 0, multiples of 16 bytes, stride_n >= d");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) || !aligned16(kv))
+        return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    const size_t need = varlen_workspace_bytes(p, heads, d);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "workspace missing, misaligned or smaller than la_prefill_varlen_workspace_size");
+    s = device_check();
+    if (s != LA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the chunk and sequence tables go to the front of the workspace (a copy from pageable host
+    // memory: HIP stages it before the call returns, so the host table may go out of scope)
+    s = launch_status(hipMemcpyAsync(workspace, p.tab.data(), p.tab.size() * sizeof(int64_t),
+                                     hipMemcpyHostToDevice, st),
+                      "table upload");
+    if (s != LA_OK) return s;
+    const int64_t* ctab = static_cast<const int64_t*>(workspace);
+    FwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.sh = sh;
+    a.sn = sn;
+    a.heads = heads;
+    a.chunk = p.chunk;
+    a.slices = p.slices;
+    a.slopes = slopes;
+    a.kv = kv;
+    a.ws = p.chunked ? reinterpret_cast<float*>(static_cast<char*>(workspace) + varlen_table_bytes(p)) : nullptr;
+    a.ctab = ctab;
+    a.stab = ctab + 5 * p.total_chunks;
+    a.groups = p.total_chunks * heads;
+    auto run = [&](int mode) -> hipError_t {
+        return dt == LA_BF16 ? launch_fwd_bf16(a, mode, st) : launch_fwd_f32(a, (int)d, mode, st);
+    };
+    if (p.chunked) {
+        s = launch_status(run(kModeLocal), "chunk-summary launch");
+        if (s != LA_OK) return s;
+        s = launch_status(launch_scan_varlen(a.ws, kv, slopes, a.stab, n_seq, heads, p.chunk, (int)d, st),
+                          "prefix-combine launch");
+        if (s != LA_OK) return s;
+    }
+    return launch_status(run(o ? kModeOut : kModeState), "prefill launch");
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t la_prefill_varlen_workspace_size_ex(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                           int64_t d, int64_t chunk_tokens)
+{
+    try {
+        VarPlan p;
+        if (make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, chunk_tokens, p) != LA_OK) return 0;
+        return varlen_workspace_bytes(p, heads, d);
+    } catch (...) {
+        return 0;
+    }
+}
+
+size_t la_prefill_varlen_workspace_size(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                        int64_t d)
+{
+    return la_prefill_varlen_workspace_size_ex(dt, n_seq, cu_seqlens, heads, d, 0);
+}
+
+int64_t la_prefill_varlen_chunk_tokens(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                       int64_t d)
+{
+    try {
+        VarPlan p;
+        if (make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, 0, p) != LA_OK) return -1;
+        return p.chunk;
+    } catch (...) {
+        return -1;
+    }
+}
+
+la_status la_prefill_varlen_ex(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                               int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
+                               int64_t stride_h, int64_t stride_n, const float* slopes, float* kv,
+                               int64_t chunk_tokens, void* workspace, size_t workspace_bytes, void* stream)
+{
+    try {
+        return prefill_varlen_impl(dt, q, k, v, o, n_seq, cu_seqlens, heads, d, stride_h, stride_n, slopes, kv,
+                                   chunk_tokens, workspace, workspace_bytes, stream);
+    } catch (const std::exception& e) {
+        return fail(LA_ERR_INTERNAL, e.what());
+    } catch (...) {
+        return fail(LA_ERR_INTERNAL, "unknown error");
+    }
+}
+
+la_status la_prefill_varlen(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                            int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
+                            int64_t stride_h, int64_t stride_n, const float* slopes, float* kv,
+                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    return la_prefill_varlen_ex(dt, q, k, v, o, n_seq, cu_seqlens, heads, d, stride_h, stride_n, slopes, kv, 0,
+                                workspace, workspace_bytes, stream);
+}
+
 
 la_status la_state_init(float* kv, const float* kv0, int64_t batch, int64_t heads, int64_t d, void* stream)
 {

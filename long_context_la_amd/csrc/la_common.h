@@ -50,13 +50,65 @@ struct FwdArgs {
     float* ckpt;             // [B*H][n_ckpt][d][d] or null
     int64_t ckpt_every;
     int64_t n_ckpt;
+    // Packed variable-length batches (null for the fixed-length batch): ctab[5c..5c+4] = token
+    // range begin and end (packed indices), sequence, chunk index within the sequence and first
+    // chunk of that sequence, for global chunk c; stab[2s..2s+1] = first chunk and chunk count of
+    // sequence s.  Workspace slot (c, h) = c*heads + h.
+    const int64_t* ctab;
+    const int64_t* stab;
 };
+
+// What one workgroup processes: a chunk of one (sequence, head).
+struct Work {
+    int64_t u;         // state index: sequence * heads + head
+    int64_t h;
+    int64_t j;         // chunk index within the sequence
+    int64_t nck;       // chunks of this sequence
+    int64_t base;      // element offset of the (sequence, head) rows in q/k/v/o (t indexes rows)
+    int64_t t_begin;   // token range of the chunk, [t_begin, t_end)
+    int64_t t_end;
+    int64_t slot_in;   // workspace slot with the chunk's incoming prefix (chunked sequences)
+    int64_t slot_out;  // workspace slot that receives the chunk's local state (kModeLocal)
+};
+
+__device__ inline Work decode_work(const FwdArgs& a, int64_t group)
+{
+    Work w;
+    if (a.ctab) {
+        const int64_t c = group / a.heads;
+        w.h = group % a.heads;
+        const int64_t* e = a.ctab + 5 * c;
+        w.t_begin = e[0];
+        w.t_end = e[1];
+        const int64_t s = e[2];
+        w.j = e[3];
+        w.nck = a.stab[2 * s + 1];
+        w.u = s * a.heads + w.h;
+        w.base = w.h * a.sh;
+        w.slot_in = c * a.heads + w.h;
+        w.slot_out = (c + 1) * a.heads + w.h;
+    } else {
+        w.u = group / a.chunks_launched;
+        w.j = group % a.chunks_launched;
+        const int64_t bb = w.u / a.heads;
+        w.h = w.u % a.heads;
+        w.t_begin = w.j * a.chunk;
+        w.t_end = (w.t_begin + a.chunk < a.n) ? w.t_begin + a.chunk : a.n;
+        w.nck = a.n_chunks;
+        w.base = bb * a.sb + w.h * a.sh;
+        w.slot_in = w.u * a.n_chunks + w.j;
+        w.slot_out = w.slot_in + 1;
+    }
+    return w;
+}
 
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream);
 hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
                        int64_t n_chunks, int64_t chunk, int d, hipStream_t stream);
+hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
+                              int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream);
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);
 hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                          int64_t bh, int64_t heads, int d, const float* slopes, float* kv,

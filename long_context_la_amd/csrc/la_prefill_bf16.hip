@@ -171,11 +171,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     int slice;
     xcd_decode(blockIdx.x, a.slices, group, slice);
     if (group >= a.groups) return;
-    const int64_t u = group / a.chunks_launched;
-    const int64_t j = group % a.chunks_launched;
-    const int64_t bb = u / a.heads, h = u % a.heads;
-    const int64_t t_begin = j * a.chunk;
-    const int64_t t_end = (t_begin + a.chunk < a.n) ? t_begin + a.chunk : a.n;
+    const Work wk = decode_work(a, group);
+    if (MODE == kModeLocal && wk.j == wk.nck - 1) return;  // last chunks need no summary
+    const int64_t u = wk.u, j = wk.j, h = wk.h;
+    const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int64_t d2 = (int64_t)D * D;
     const int n_tiles = (int)((t_end - t_begin + BK - 1) / BK);
 
@@ -184,7 +183,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const bool is_state = w >= SW0;
     const int l = tid & 63, lr = l & 15, g = l >> 4;
     const float nsl = neg_slope_log2e(a.slopes, h);
-    const int64_t base = bb * a.sb + h * a.sh;
+    const int64_t base = wk.base;
     const u16* Qg = static_cast<const u16*>(a.q) + base;
     const u16* Kg = static_cast<const u16*>(a.k) + base;
     const u16* Vg = static_cast<const u16*>(a.v) + base + slice * SW;
@@ -443,7 +442,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     auto state_loop = [&](auto swc) __attribute__((always_inline)) {
         f32x4 st[st_count(decltype(swc)::value)];
         const float* src = nullptr;
-        if (MODE != kModeLocal) src = (a.n_chunks > 1) ? a.ws + (u * a.n_chunks + j) * d2 : a.kv + u * d2;
+        if (MODE != kModeLocal) src = (wk.nck > 1) ? a.ws + wk.slot_in * d2 : a.kv + u * d2;
         load_state(swc, st, src);
         KVRegs RA, RB;
         load_kv(RA, 0);
@@ -474,8 +473,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             __syncthreads();
         }
         if (tile < n_tiles) step(RA, RB, 0, tile);
-        if (MODE == kModeLocal) store_state(swc, st, a.ws + (u * a.n_chunks + j + 1) * d2);
-        else if (j == a.n_chunks - 1) store_state(swc, st, a.kv + u * d2);
+        if (MODE == kModeLocal) store_state(swc, st, a.ws + wk.slot_out * d2);
+        else if (j == wk.nck - 1) store_state(swc, st, a.kv + u * d2);
     };
     auto out_loop = [&](auto wc) __attribute__((always_inline)) {
         QRegs QA, QB;

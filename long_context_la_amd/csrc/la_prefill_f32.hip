@@ -33,16 +33,15 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     int slice;
     xcd_decode(blockIdx.x, a.slices, group, slice);
     if (group >= a.groups) return;
-    const int64_t u = group / a.chunks_launched;      // batch*heads + head
-    const int64_t j = group % a.chunks_launched;      // chunk index
-    const int64_t b = u / a.heads, h = u % a.heads;
-    const int64_t t_begin = j * a.chunk;
-    const int64_t t_end = (t_begin + a.chunk < a.n) ? t_begin + a.chunk : a.n;
+    const Work wk = decode_work(a, group);
+    if (MODE == kModeLocal && wk.j == wk.nck - 1) return;  // last chunks need no summary
+    const int64_t u = wk.u, j = wk.j, h = wk.h;
+    const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int tid = threadIdx.x;
     const int col = tid % SW;
     const int row0 = tid / SW;
     const float nsl = neg_slope_log2e(a.slopes, h);
-    const int64_t base = b * a.sb + h * a.sh;
+    const int64_t base = wk.base;
     const float* Q = static_cast<const float*>(a.q) + base;
     const float* K = static_cast<const float*>(a.k) + base;
     const float* V = static_cast<const float*>(a.v) + base;
@@ -52,7 +51,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     // incoming state slice
     float st[RPT];
     const float* src = nullptr;
-    if (MODE != kModeLocal) src = (a.n_chunks > 1) ? a.ws + (u * a.n_chunks + j) * d2 : a.kv + u * d2;
+    if (MODE != kModeLocal) src = (wk.nck > 1) ? a.ws + wk.slot_in * d2 : a.kv + u * d2;
 #pragma unroll
     for (int m = 0; m < RPT; ++m) st[m] = src ? src[(row0 + 8 * m) * D + slice * SW + col] : 0.f;
 #pragma unroll
@@ -126,8 +125,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     }
 
     float* dst = nullptr;
-    if (MODE == kModeLocal) dst = a.ws + (u * a.n_chunks + j + 1) * d2;
-    else if (j == a.n_chunks - 1) dst = a.kv + u * d2;
+    if (MODE == kModeLocal) dst = a.ws + wk.slot_out * d2;
+    else if (j == wk.nck - 1) dst = a.kv + u * d2;
     if (dst) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) dst[(row0 + 8 * m) * D + slice * SW + col] = st[m];

@@ -40,6 +40,37 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ ws, const floa
     }
 }
 
+// Packed variable-length batches: the chunks of sequence s are global chunks c0..c0+nc-1 (stab)
+// and slot (c, h) = c*heads + h; slot (c0+j+1, h) holds the local state of chunk j.
+__global__ __launch_bounds__(256) void k_scan_varlen(float* __restrict__ ws, const float* __restrict__ kv,
+                                                     const float* __restrict__ slopes,
+                                                     const int64_t* __restrict__ stab, int64_t n_seq,
+                                                     int64_t heads, int64_t chunk, int d2)
+{
+    const int64_t per = d2 / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n_seq * heads * per) return;
+    const int64_t u = idx / per;
+    const int64_t e = idx % per;
+    const int64_t sq = u / heads, h = u % heads;
+    const int64_t c0 = stab[2 * sq], nc = stab[2 * sq + 1];
+    if (nc <= 1) return;
+    const float nsl = neg_slope_log2e(slopes, h);
+    const float lc = decay_pow(nsl, (float)chunk);
+    const int64_t step = heads * per;  // float4s between slots (c, h) and (c+1, h)
+    float4* base = reinterpret_cast<float4*>(ws + (c0 * heads + h) * (int64_t)d2) + e;
+    float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
+    base[0] = p;
+    for (int64_t j = 1; j < nc; ++j) {
+        const float4 s = base[j * step];
+        p.x = lc * p.x + s.x;
+        p.y = lc * p.y + s.y;
+        p.z = lc * p.z + s.z;
+        p.w = lc * p.w + s.w;
+        base[j * step] = p;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_state_init(float* __restrict__ kv, const float* __restrict__ kv0,
                                                     int64_t count4)
 {
@@ -58,6 +89,16 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
     const int64_t threads = bh * (d2 / 4);
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     hipLaunchKernelGGL(k_scan, grid, block, 0, stream, ws, kv, slopes, bh, heads, n_chunks, chunk, d2);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
+                              int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream)
+{
+    const int d2 = d * d;
+    const int64_t threads = n_seq * heads * (d2 / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_scan_varlen, grid, block, 0, stream, ws, kv, slopes, stab, n_seq, heads, chunk, d2);
     return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import long_context_la_amd as la
@@ -101,3 +102,60 @@ def test_plan_and_workspace_sizes():
     assert la.la_prefill_workspace_size(la.LA_F32, 1, 2, 512, 64, chunk_tokens=128) == 2 * 4 * 64 * 64 * 4
     assert la.la_prefill_workspace_size(la.LA_F32, 1, 2, 512, 64, chunk_tokens=1024) == 0
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 100, 96) == -1
+
+
+def _cu(lengths):
+    return [0] + list(np.cumsum(lengths).astype(int))
+
+
+def _varlen(lengths, **kw):
+    cu, n_seq = la._cu_array(kw.pop("cu", _cu(lengths)))
+    a = dict(dt=la.LA_BF16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, H=8, d=128, sh=128, sn=8 * 128, slopes=FAKE, kv=FAKE,
+             chunk=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return la.lib().la_prefill_varlen_ex(a["dt"], a["q"], a["k"], a["v"], a["o"], n_seq, cu, a["H"], a["d"],
+                                         a["sh"], a["sn"], a["slopes"], a["kv"], a["chunk"], a["ws"],
+                                         a["ws_bytes"], None)
+
+
+def test_varlen_plan_and_workspace_sizes():
+    table = lambda n_chunks, n_seq: ((5 * n_chunks + 2 * n_seq) * 8 + 255) // 256 * 256
+    # 20 sequences x 64 heads x 4 slices fill the GPU: one chunk each, tables only
+    lengths = [50, 50] + [1] * 18
+    assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16, _cu(lengths), 64, 128) == 50
+    assert la.la_prefill_varlen_workspace_size(la.LA_BF16, _cu(lengths), 64, 128) == table(20, 20)
+    # one long and two short sequences on 8 heads: the long one is chunked
+    lengths = [32768, 100, 7]
+    c = la.la_prefill_varlen_chunk_tokens(la.LA_BF16, _cu(lengths), 8, 128)
+    assert c % 64 == 0 and 1024 <= c < 32768
+    n_chunks = (32768 + c - 1) // c + 2
+    assert la.la_prefill_varlen_workspace_size(la.LA_BF16, _cu(lengths), 8, 128) == \
+        table(n_chunks, 3) + n_chunks * 8 * 128 * 128 * 4
+    # explicit chunking, empty sequences take no chunk
+    lengths = [300, 0, 64, 65]
+    n_chunks = 3 + 0 + 1 + 1
+    assert la.la_prefill_varlen_workspace_size(la.LA_F32, _cu(lengths), 2, 64, chunk_tokens=128) == \
+        table(n_chunks, 4) + n_chunks * 2 * 64 * 64 * 4
+    # invalid inputs
+    assert la.la_prefill_varlen_workspace_size(la.LA_BF16, [1, 5], 8, 128) == 0      # cu[0] != 0
+    assert la.la_prefill_varlen_workspace_size(la.LA_BF16, [0, 5, 3], 8, 128) == 0   # decreasing
+    assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16, [0, 5], 8, 96) == -1
+
+
+def test_varlen_validation_codes():
+    assert _varlen([10, 20], q=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], kv=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], cu=[3, 10, 20]) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], cu=[0, 10, 5]) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], d=64, sh=64, sn=512) == la.LA_ERR_UNSUPPORTED
+    assert _varlen([10, 20], sn=100) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], chunk=100) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
+    assert _varlen([10, 20], ws_bytes=8) == la.LA_ERR_WORKSPACE
+    # every sequence empty: a no-op that touches nothing
+    assert _varlen([0, 0], q=None, k=None, v=None, ws=None, ws_bytes=0) == la.LA_OK
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
+def test_varlen_no_device_is_reported_not_fatal():
+    assert _varlen([10, 20]) == la.LA_ERR_DEVICE

@@ -5,6 +5,8 @@
 * long   (1 x 8 heads x 1,048,576 tokens, bf16, checkpoints every 65536): checkpoints, final
   states and output windows (including the chunk boundaries of the LASP+-style split).
 * decode (128 sequences x 64 heads, 4096-token prefix then decode steps): sampled (seq, head).
+* varlen (the full layer's tokens cut into 18 packed sequences of 65536, 32768, ..., 1, 1 tokens,
+  as the benchmark times them): every final state and sampled output windows of every sequence.
 
 Windows use the oracle's windowing pin: for slopes s >= 2^-8 the state is fixed by the last
 W = 8192 tokens up to lambda^W <= e^-32 (relative), far below the bars, so a window's outputs are
@@ -173,3 +175,56 @@ def test_decode_workload_sampled_units(device):
     for r, (b, h) in enumerate(units):
         assert_close(o_all[b:b + 1, h:h + 1], o_ref[:, r:r + 1, P:], "bf16", f"decode o ({b},{h})", stored="bf16")
         assert_close(kv_h[b:b + 1, h:h + 1], kv_ref[:, r:r + 1], "bf16", f"decode KV ({b},{h})")
+
+
+def seq_windows_reference(w, items, length, slopes):
+    """Like windows_reference for sequences packed inside the workload's token axis: item
+    (h, seq_start, end) restarts the recurrence from zero at seq_start, so a window's reference
+    runs from max(seq_start, end - length - WINDOW); zero tokens pad the front of short ones."""
+    span = length + WINDOW
+    rows = [[], [], []]
+    row_slopes = []
+    for h, seq_start, end in items:
+        start = max(seq_start, end - span)
+        parts = exact(w, 0, h, start, end - start)
+        for i in range(3):
+            x = parts[i][0, 0]
+            if x.shape[0] < span:
+                x = np.concatenate([np.zeros((span - x.shape[0], w.d), np.float32), x])
+            rows[i].append(x)
+        row_slopes.append(slopes[h])
+    q, k, v = (np.stack(r)[None] for r in rows)
+    o, kv, _ = oracle.recurrent(q, k, v, np.array(row_slopes, dtype=np.float64))
+    return [(o[0, r, -length:], kv[0, r]) for r in range(len(items))]
+
+
+def test_varlen_packed_full_layer(device):
+    import bench
+
+    torch = _torch()
+    w = synth.WORKLOADS["full"]
+    slopes = w.slopes()
+    q, k, v = upload(w, device)
+    o = torch.empty_like(q)
+    lengths = bench.VARLEN_LENGTHS
+    cu = [0] + list(np.cumsum(lengths))
+    n_seq = len(lengths)
+    kv = torch.zeros(n_seq, w.heads, w.d, w.d, dtype=torch.float32, device=device)
+    la.la_prefill_varlen(q[0].permute(1, 0, 2), k[0].permute(1, 0, 2), v[0].permute(1, 0, 2),
+                         torch.from_numpy(slopes).to(device), kv, cu, o=o[0].permute(1, 0, 2))
+    torch.cuda.synchronize()
+    del q, k, v
+    kv_h = kv.cpu().numpy()
+    heads = (0, 9, 33, 63)
+    # final states of every sequence (four heads each)
+    items = [(h, cu[s], cu[s + 1]) for s in range(n_seq) for h in heads]
+    for (h, s0, end), (_, kv_ref) in zip(items, seq_windows_reference(w, items, 1, slopes)):
+        s = cu.index(s0)
+        assert_close(kv_h[s:s + 1, h:h + 1], kv_ref[None, None], "bf16", f"varlen KV seq {s} head {h}")
+    # the last (up to) 64 outputs of every sequence, and a window inside the longest
+    items = [(h, cu[s], cu[s + 1]) for s in range(n_seq) for h in heads[:2]] + [(21, 0, 40000)]
+    for (h, s0, end), (o_ref, _) in zip(items, seq_windows_reference(w, items, 64, slopes)):
+        n = min(64, end - s0)
+        got = to_host(o[0:1, h:h + 1, end - n:end])
+        assert_close(got, o_ref[None, None, 64 - n:], "bf16", f"varlen O head {h} tokens ..{end}", stored="bf16")
+
