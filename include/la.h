@@ -127,9 +127,12 @@ la_status la_prefill_ex(la_dtype dt, const void* q, const void* k, const void* v
  * samples back to back and tracks each one's offsets; section 3.3 runs long
  * and short inputs with separate work sizes).  Sequence s owns packed tokens
  * cu_seqlens[s] .. cu_seqlens[s+1]-1; each sequence starts from its own state
- * kv[s][h] and leaves its final state there.  One launch (plus, when a long
- * sequence is cut into chunks, a chunk-summary launch and a prefix combine)
- * covers the whole batch, so short and long sequences share the GPU.
+ * kv[s][h] and leaves its final state there.  One launch of the 64-token tile
+ * kernel (plus, when a long sequence is cut into chunks, a chunk-summary launch
+ * and a prefix combine) covers every sequence longer than 8 tokens; sequences
+ * of 1..8 tokens run token by token in one more launch that reads and writes
+ * their states once (the smallest of the work sizes section 3.3 uses for short
+ * inputs), so short and long sequences share the GPU without padding.
  *   q, k, v, o : element (t, h, e) at base + t*stride_n + h*stride_h + e, t =
  *                packed token index (e.g. [total][heads][d] has stride_n =
  *                heads*d, stride_h = d); rules as for la_prefill.

@@ -171,10 +171,11 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
 // sequences are cut into chunks (the LASP+ combine of section 3.2), short ones run whole.
 struct VarPlan {
     int64_t chunk = 0;         // chunk length (tokens) of every chunk but a sequence's last
-    int64_t total_chunks = 0;  // over all sequences
+    int64_t total_chunks = 0;  // over the sequences that run in 64-token tiles
+    int64_t n_short = 0;       // sequences of 1..kShortTokens tokens, run token by token
     bool chunked = false;      // some sequence has more than one chunk
     int slices = 0;
-    std::vector<int64_t> tab;  // ctab (5 per chunk) followed by stab (2 per sequence)
+    std::vector<int64_t> tab;  // ctab (5 per chunk), stab (2 per sequence), rtab (3 per short sequence)
 };
 
 size_t varlen_table_bytes(const VarPlan& p) { return ((p.tab.size() * sizeof(int64_t) + 255) / 256) * 256; }
@@ -217,9 +218,16 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
     }
     p.chunk = chunk > 0 ? chunk : kBlock;
     p.tab.clear();
-    std::vector<int64_t> stab((size_t)(2 * n_seq));
+    std::vector<int64_t> stab((size_t)(2 * n_seq)), rtab;
     for (int64_t s = 0; s < n_seq; ++s) {
         const int64_t n = cu[s + 1] - cu[s];
+        if (n >= 1 && n <= kShortTokens) {  // short: token by token, no tile
+            rtab.insert(rtab.end(), {cu[s], n, s});
+            ++p.n_short;
+            stab[2 * s] = p.total_chunks;
+            stab[2 * s + 1] = 0;
+            continue;
+        }
         const int64_t nc = n == 0 ? 0 : (n <= p.chunk ? 1 : (n + p.chunk - 1) / p.chunk);
         stab[2 * s] = p.total_chunks;
         stab[2 * s + 1] = nc;
@@ -232,6 +240,7 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
         if (nc > 1) p.chunked = true;
     }
     p.tab.insert(p.tab.end(), stab.begin(), stab.end());
+    p.tab.insert(p.tab.end(), rtab.begin(), rtab.end());
     return LA_OK;
 }
 
@@ -244,7 +253,7 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, chunk_tokens, p);
     if (s != LA_OK) return s;
     if (!kv || !slopes) return fail(LA_ERR_INVALID_ARGUMENT, "kv and slopes must not be NULL");
-    if (p.total_chunks == 0) return LA_OK;  // every sequence empty
+    if (p.total_chunks == 0 && p.n_short == 0) return LA_OK;  // every sequence empty
     if (!q || !k || !v) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v must not be NULL");
     const int64_t align = (dt == LA_BF16) ? 8 : 4;
     if (sn < d || sh < 0 || sh % align || sn % align)
@@ -284,6 +293,13 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     auto run = [&](int mode) -> hipError_t {
         return dt == LA_BF16 ? launch_fwd_bf16(a, mode, st) : launch_fwd_f32(a, (int)d, mode, st);
     };
+    if (p.n_short > 0) {
+        const int64_t* rtab = a.stab + 2 * n_seq;
+        s = launch_status(launch_recur_short(dt, q, k, v, o, p.n_short, heads, (int)d, sn, sh, slopes, kv, rtab, st),
+                          "short-sequence launch");
+        if (s != LA_OK) return s;
+    }
+    if (p.total_chunks == 0) return LA_OK;
     if (p.chunked) {
         s = launch_status(run(kModeLocal), "chunk-summary launch");
         if (s != LA_OK) return s;

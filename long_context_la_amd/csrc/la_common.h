@@ -14,6 +14,7 @@ constexpr int kBlock = 64;       // tokens per kernel tile (the model's tile of 
 constexpr int kSliceW = 32;      // value columns per workgroup (value-dim slicing)
 constexpr int kTargetGroups = 256;  // workgroups that fill one MI355X (256 CUs, one resident each)
 constexpr int kMinChunk = 1024;  // shortest chunk worth a 64 KiB state exchange
+constexpr int kShortTokens = 8;  // packed sequences this short run token by token (no 64-token tile)
 
 // How a prefill is split: value-column slices x sequence chunks per (batch, head).
 struct Plan {
@@ -110,6 +111,9 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
 hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
                               int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream);
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);
+hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                              int64_t n_short, int64_t heads, int d, int64_t sn, int64_t sh,
+                              const float* slopes, float* kv, const int64_t* tab, hipStream_t stream);
 hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                          int64_t bh, int64_t heads, int d, const float* slopes, float* kv,
                          hipStream_t stream);

@@ -77,7 +77,96 @@ __global__ __launch_bounds__(256) void k_decode(const T* __restrict__ q, const T
     }
 }
 
+// Short packed sequences, token by token (the smallest of the work sizes that section 3.3 of the
+// page above uses for short inputs; longer sequences go through the 64-token tile kernels).  One
+// workgroup per (short sequence, head): the state stays in registers across the sequence's
+// tokens, each token updates it and reads o_t = q_t . KV_t out through an LDS reduction; the
+// state is read and written once.  tab[3e..3e+2] = first packed token, token count and sequence
+// index of short sequence e; q, k, v, o rows at t*sn + h*sh (o may be null: state only).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_recur_short(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, T* __restrict__ o,
+                                                     const float* __restrict__ slopes, float* __restrict__ kv,
+                                                     int64_t heads, int64_t sn, int64_t sh,
+                                                     const int64_t* __restrict__ tab)
+{
+    constexpr int CG = D / 4;
+    constexpr int RG = 256 / CG;
+    constexpr int RPT = D / RG;
+    const int64_t e = blockIdx.x / heads, h = blockIdx.x % heads;
+    const int64_t tok0 = tab[3 * e], n = tab[3 * e + 1], sq_idx = tab[3 * e + 2];
+    const int tid = threadIdx.x;
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+
+    __shared__ float sq[D];
+    __shared__ float sk[D];
+    __shared__ f32x4 red[RG][CG];
+
+    float* S = kv + (sq_idx * heads + h) * (int64_t)(D * D);
+    f32x4 st[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) st[m] = reinterpret_cast<const f32x4*>(S + (rg + RG * m) * D)[cg];
+    const float lam = (float)exp(-(double)slopes[h]);
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t row = (tok0 + i) * sn + h * sh;
+        if (tid < D) {
+            sq[tid] = to_f32(q[row + tid]);
+            sk[tid] = to_f32(k[row + tid]);
+        }
+        const T* vu = v + row + 4 * cg;
+        const f32x4 vv = {to_f32(vu[0]), to_f32(vu[1]), to_f32(vu[2]), to_f32(vu[3])};
+        __syncthreads();
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int r = rg + RG * m;
+            st[m] = lam * st[m] + sk[r] * vv;
+            acc += sq[r] * st[m];
+        }
+        red[rg][cg] = acc;
+        __syncthreads();
+        if (tid < CG && o) {
+            f32x4 rr = red[0][tid];
+            for (int g = 1; g < RG; ++g) rr += red[g][tid];
+            T* ou = o + row + 4 * tid;
+            ou[0] = from_f32<T>(rr[0]);
+            ou[1] = from_f32<T>(rr[1]);
+            ou[2] = from_f32<T>(rr[2]);
+            ou[3] = from_f32<T>(rr[3]);
+        }
+        __syncthreads();  // sq, sk and red are rewritten by the next token
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) reinterpret_cast<f32x4*>(S + (rg + RG * m) * D)[cg] = st[m];
+}
+
 }  // namespace
+
+hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                              int64_t n_short, int64_t heads, int d, int64_t sn, int64_t sh,
+                              const float* slopes, float* kv, const int64_t* tab, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(n_short * heads)), block(256);
+    if (dt == LA_BF16) {
+        auto qq = static_cast<const __bf16*>(q), kk = static_cast<const __bf16*>(k),
+             vv = static_cast<const __bf16*>(v);
+        auto oo = static_cast<__bf16*>(o);
+        if (d == 128)
+            hipLaunchKernelGGL((k_recur_short<__bf16, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+        else
+            hipLaunchKernelGGL((k_recur_short<__bf16, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+    } else {
+        auto qq = static_cast<const float*>(q), kk = static_cast<const float*>(k),
+             vv = static_cast<const float*>(v);
+        auto oo = static_cast<float*>(o);
+        if (d == 128)
+            hipLaunchKernelGGL((k_recur_short<float, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+        else
+            hipLaunchKernelGGL((k_recur_short<float, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                          int64_t bh, int64_t heads, int d, const float* slopes, float* kv,

@@ -119,23 +119,27 @@ def _varlen(lengths, **kw):
 
 
 def test_varlen_plan_and_workspace_sizes():
-    table = lambda n_chunks, n_seq: ((5 * n_chunks + 2 * n_seq) * 8 + 255) // 256 * 256
-    # 20 sequences x 64 heads x 4 slices fill the GPU: one chunk each, tables only
+    def table(n_chunks, n_seq, n_short=0):
+        return ((5 * n_chunks + 2 * n_seq + 3 * n_short) * 8 + 255) // 256 * 256
+    # the pages' mixed batch: two 50-token inputs run in tiles (one chunk each, 64 heads fill the
+    # GPU), the 18 single-token inputs token by token; tables only
     lengths = [50, 50] + [1] * 18
     assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16, _cu(lengths), 64, 128) == 50
-    assert la.la_prefill_varlen_workspace_size(la.LA_BF16, _cu(lengths), 64, 128) == table(20, 20)
-    # one long and two short sequences on 8 heads: the long one is chunked
+    assert la.la_prefill_varlen_workspace_size(la.LA_BF16, _cu(lengths), 64, 128) == table(2, 20, 18)
+    # one long, one medium and one short sequence on 8 heads: the long one is chunked
     lengths = [32768, 100, 7]
     c = la.la_prefill_varlen_chunk_tokens(la.LA_BF16, _cu(lengths), 8, 128)
     assert c % 64 == 0 and 1024 <= c < 32768
-    n_chunks = (32768 + c - 1) // c + 2
+    n_chunks = (32768 + c - 1) // c + 1
     assert la.la_prefill_varlen_workspace_size(la.LA_BF16, _cu(lengths), 8, 128) == \
-        table(n_chunks, 3) + n_chunks * 8 * 128 * 128 * 4
-    # explicit chunking, empty sequences take no chunk
-    lengths = [300, 0, 64, 65]
+        table(n_chunks, 3, 1) + n_chunks * 8 * 128 * 128 * 4
+    # explicit chunking; empty sequences take no chunk, 9+ token ones run in tiles
+    lengths = [300, 0, 64, 9]
     n_chunks = 3 + 0 + 1 + 1
     assert la.la_prefill_varlen_workspace_size(la.LA_F32, _cu(lengths), 2, 64, chunk_tokens=128) == \
         table(n_chunks, 4) + n_chunks * 2 * 64 * 64 * 4
+    # only short sequences: no tiles, no state slots
+    assert la.la_prefill_varlen_workspace_size(la.LA_F32, _cu([8, 1, 3]), 2, 64, chunk_tokens=128) == table(0, 3, 3)
     # invalid inputs
     assert la.la_prefill_varlen_workspace_size(la.LA_BF16, [1, 5], 8, 128) == 0      # cu[0] != 0
     assert la.la_prefill_varlen_workspace_size(la.LA_BF16, [0, 5, 3], 8, 128) == 0   # decreasing

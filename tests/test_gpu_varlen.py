@@ -156,3 +156,13 @@ def test_mixed_step_two_streams(device):
         assert_close(np.transpose(o_h[cu[s]:cu[s + 1]], (1, 0, 2))[None], o_r, dtype, f"mixed step prefill O {s}",
                      stored=dtype)
         assert_close(kvp.cpu().numpy()[s:s + 1], kv_r, dtype, f"mixed step prefill KV {s}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_varlen_short_sequences(device, dtype, d):
+    # 1..8 tokens run token by token, 9 and more in 64-token tiles; the boundary on both sides
+    run_varlen([1, 8, 9, 2, 0, 7, 3], 3, d, dtype, device)
+
+
+def test_varlen_short_sequences_state_only(device):
+    run_varlen([4, 1, 8], 2, 128, "bf16", device, want_o=False)
