@@ -28,6 +28,11 @@ Forms provided (each a separate, literal transcription of one definition):
   decode     -- one step of the recurrence
   chunk states / LASP+ combine -- local summaries from a zero state, then
                 prefixes P_{j+1} = lambda^{C_j} P_j + S_j.
+  prologue / epilogue -- the pieces the derivation leaves out (section 2.2
+                names normalisation, SiLU and gating; section 3.3 fuses such
+                memory-bound steps into the attention kernels): SiLU on q, k, v
+                before attention, and after it an RMS normalisation over the
+                head dimension followed by an elementwise sigmoid gate.
 Every power of lambda is exp(-s*k) with k >= 0.  No part is "parity unpinned":
 the pins live in tests/test_oracle_pins.py.
 """
@@ -225,3 +230,45 @@ def lasp_plus_prefixes(local_states, slopes, chunk_lens, kv_in=None):
             for j in range(n):
                 P[b, h, j + 1] = decay_powers(s, chunk_lens[j]) * P[b, h, j] + S[b, h, j]
     return P
+
+
+# ---------------------------------------------------------------- prologue / epilogue
+# Our reading of the pieces the derivation omits (section 2.2 lists them without formulas):
+#   SiLU(x) = x * sigmoid(x), elementwise, applied to q, k and/or v before attention;
+#   Norm(o) = o / sqrt(mean_e(o_e^2) + eps) * w_e, over the d features of one (token, head),
+#             the plain RMS normalisation, with an optional per-feature weight w (default 1);
+#   gate:     o * sigmoid(g) for a gate tensor g of the output's shape.
+
+def sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    """x * sigmoid(x) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def rms_norm(o, eps, weight=None):
+    """RMS normalisation over the last axis (the head dimension) in float64."""
+    o = np.asarray(o, dtype=np.float64)
+    r = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return r if weight is None else r * np.asarray(weight, dtype=np.float64)
+
+
+def fused(q, k, v, slopes, kv_in=None, silu_q=False, silu_k=False, silu_v=False, norm_eps=None,
+          norm_weight=None, gate=None):
+    """The attention of ``recurrent`` wrapped in the optional prologue and epilogue, step by step:
+    SiLU on the selected inputs, the recurrence, RMS normalisation (when norm_eps is given), then
+    the sigmoid gate (when gate is given).  Returns (o, final state)."""
+    q = silu(q) if silu_q else np.asarray(q, dtype=np.float64)
+    k = silu(k) if silu_k else np.asarray(k, dtype=np.float64)
+    v = silu(v) if silu_v else np.asarray(v, dtype=np.float64)
+    o, kv, _ = recurrent(q, k, v, slopes, kv_in=kv_in)
+    if norm_eps is not None:
+        o = rms_norm(o, norm_eps, norm_weight)
+    if gate is not None:
+        o = o * sigmoid(gate)
+    return o, kv
+

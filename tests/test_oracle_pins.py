@@ -307,3 +307,63 @@ def test_planted_mistakes_are_caught(kind):
     assert np.abs(got - np.array(g["o_zero_state"])).max() > 0.1
     ok = _mutant_recurrent(q, k, v, g["slope"], "correct")
     np.testing.assert_allclose(ok, g["o_zero_state"], atol=1e-12)
+
+
+# ---------------------------------------------------------------- prologue / epilogue pins
+def test_p10_sigmoid_and_silu_values():
+    # sigmoid(1) = 1 / (1 + e^-1); SiLU(x) - SiLU(-x) = x; limits; SiLU(0) = 0
+    assert oracle.sigmoid(0.0) == 0.5
+    assert abs(float(oracle.sigmoid(1.0)) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(float(oracle.sigmoid(1.0)) - 0.7310585786300049) < 1e-15
+    x = np.linspace(-30.0, 30.0, 121)
+    np.testing.assert_allclose(oracle.sigmoid(x) + oracle.sigmoid(-x), 1.0, atol=1e-15)
+    np.testing.assert_allclose(oracle.silu(x) - oracle.silu(-x), x, atol=1e-12)
+    assert float(oracle.silu(0.0)) == 0.0
+    assert abs(float(oracle.silu(40.0)) - 40.0) < 1e-12
+    assert abs(float(oracle.silu(-40.0))) < 1e-14
+    assert abs(float(oracle.silu(-1.0)) + 0.2689414213699951) < 1e-15
+
+
+def test_p11_rms_norm_values_and_invariants():
+    # [3, 4]: mean square 12.5, so the normalised row is [3, 4] / sqrt(12.5)
+    np.testing.assert_allclose(oracle.rms_norm(np.array([3.0, 4.0]), 0.0), [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)],
+                               rtol=1e-15)
+    rng = np.random.default_rng(0)
+    o = rng.standard_normal((3, 5, 128))
+    r = oracle.rms_norm(o, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(r * r, axis=-1)), 1.0, rtol=1e-12)   # unit RMS per row
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * o, 0.0), r, rtol=1e-12)          # scale invariant
+    w = rng.standard_normal(128)
+    np.testing.assert_allclose(oracle.rms_norm(o, 0.0, w), r * w, rtol=1e-12)          # per-feature weight
+    # eps only matters for small rows: a zero row stays zero
+    assert np.all(oracle.rms_norm(np.zeros(8), 1e-6) == 0.0)
+    # the axis is the feature axis: normalising over tokens instead changes the result
+    assert np.abs(oracle.rms_norm(o, 0.0) - np.swapaxes(oracle.rms_norm(np.swapaxes(o, -1, -2), 0.0), -1, -2)).max() > 0.1
+
+
+def test_p12_fused_hand_worked_example():
+    # d = 2, one token: k = [1, 0], v = [3, 4], q = [1, 0] -> o = q . (k^T v) = [3, 4];
+    # RMS normalisation -> [3, 4] / sqrt(12.5); gate g = [0, 60] -> times [1/2, ~1]
+    q = np.array([1.0, 0.0], dtype=np.float32)[None, None, None]
+    k = np.array([1.0, 0.0], dtype=np.float32)[None, None, None]
+    v = np.array([3.0, 4.0], dtype=np.float32)[None, None, None]
+    g = np.array([0.0, 60.0])[None, None, None]
+    o, kv = oracle.fused(q, k, v, [0.5], norm_eps=0.0, gate=g)
+    r = math.sqrt(12.5)
+    np.testing.assert_allclose(o[0, 0, 0], [3 / r * 0.5, 4 / r], rtol=1e-12)
+    np.testing.assert_allclose(kv[0, 0], [[3.0, 4.0], [0.0, 0.0]], rtol=0, atol=0)
+    # SiLU on v only: v -> [3 sigmoid(3), 4 sigmoid(4)]
+    o, _ = oracle.fused(q, k, v, [0.5], silu_v=True)
+    np.testing.assert_allclose(o[0, 0, 0], [3 / (1 + math.exp(-3)), 4 / (1 + math.exp(-4))], rtol=1e-7)
+
+
+def test_p13_fused_without_options_is_the_recurrence():
+    exact, _ = (lambda r: (r, None))([synth.generate(t, 9, 64, nb=1, nh=2, nt=70) for t in (synth.Q, synth.K, synth.V)])
+    slopes = np.array([0.1, 0.01])
+    o, kv = oracle.fused(*exact, slopes)
+    o_r, kv_r, _ = oracle.recurrent(*exact, slopes)
+    assert np.array_equal(o, o_r) and np.array_equal(kv, kv_r)
+    # each option is the plain composition of its piece with the recurrence
+    o, _ = oracle.fused(*exact, slopes, silu_q=True, silu_k=True)
+    o_r, _, _ = oracle.recurrent(oracle.silu(exact[0]), oracle.silu(exact[1]), exact[2], slopes)
+    np.testing.assert_allclose(o, o_r, rtol=1e-12, atol=1e-12)
