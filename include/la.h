@@ -57,6 +57,32 @@ typedef enum {
 } la_dtype;
 
 /*
+ * Optional prologue and epilogue fused into the attention kernels.  Section 2.2
+ * of the page above leaves normalisation, SiLU and gating out of the
+ * derivation; section 3.3 fuses memory-bound steps into the attention kernels
+ * ("batched kernel fusion").  Our reading of the three pieces:
+ *   LA_SILU_Q/K/V : x -> x * sigmoid(x), elementwise, on q, k and/or v as they
+ *                   are loaded (the bf16 paths round the activated value to
+ *                   bf16 before the matrix products);
+ *   LA_NORM       : o -> o / sqrt(mean_e(o_e^2) + norm_eps) * w_e over the d
+ *                   features of one (token, head), w = norm_weight (NULL = 1);
+ *   LA_GATE       : o -> o * sigmoid(g), g = gate, after the normalisation.
+ */
+enum {
+    LA_SILU_Q = 1,
+    LA_SILU_K = 2,
+    LA_SILU_V = 4,
+    LA_NORM = 8,
+    LA_GATE = 16
+};
+typedef struct {
+    uint32_t flags;           /* OR of the LA_SILU_* / LA_NORM / LA_GATE bits above */
+    const void* gate;         /* LA_GATE: device tensor of o's dtype, shape and strides */
+    const float* norm_weight; /* LA_NORM: [d] float32 device array, or NULL for all ones */
+    float norm_eps;           /* LA_NORM: > 0 */
+} la_fusion;
+
+/*
  * kv[batch][heads][d][d] (float32) := 0 when kv0 == NULL, else a copy of kv0
  * (same layout; kv0 may not overlap kv).  The state a prefill or decode
  * starts from, e.g. a cached prefix (section 3 of the page above reuses the
@@ -163,6 +189,29 @@ la_status la_prefill_varlen_ex(la_dtype dt, const void* q, const void* k, const 
                                int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
                                int64_t stride_h, int64_t stride_n, const float* slopes, float* kv,
                                int64_t chunk_tokens, void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * la_prefill with the prologue/epilogue of `fusion` (NULL = none; then it is
+ * la_prefill without checkpoints).  The SiLU flags act inside the prefill
+ * kernels.  LA_GATE alone is applied in the prefill kernel's output store.
+ * With LA_NORM, whose mean runs over all d features while each prefill
+ * workgroup owns a slice of 32 value columns, the prefill writes o and one
+ * more memory-bound pass normalises (and gates) it in place.  o must not be
+ * NULL when LA_NORM or LA_GATE is set; gate must not overlap o.  Workspace as
+ * for la_prefill.
+ */
+la_status la_prefill_fused(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                           int64_t batch, int64_t heads, int64_t n, int64_t d,
+                           int64_t stride_b, int64_t stride_h, int64_t stride_n,
+                           const float* slopes, float* kv, const la_fusion* fusion,
+                           void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * la_decode with the prologue/epilogue of `fusion` (NULL = none), all of it in
+ * the decode kernel (one workgroup holds a whole output row).  gate is a
+ * contiguous [batch][heads][d] tensor of dtype dt.
+ */
+la_status la_decode_fused(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                          int64_t batch, int64_t heads, int64_t d,
+                          const float* slopes, float* kv, const la_fusion* fusion, void* stream);
 /*
  * One decode step per (b, h) (section 3.3 of the page above runs single-token
  * generation as its own kernel): kv <- lambda_h * kv + k^T v, then o = q . kv.

@@ -33,7 +33,19 @@ EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_si
             "la_prefill_workspace_size_ex", "la_prefill", "la_prefill_ex",
             "la_prefill_varlen_workspace_size", "la_prefill_varlen_workspace_size_ex",
             "la_prefill_varlen_chunk_tokens", "la_prefill_varlen", "la_prefill_varlen_ex", "la_decode",
-            "la_status_string", "la_last_error"]
+            "la_prefill_fused", "la_decode_fused", "la_status_string", "la_last_error"]
+
+LA_SILU_Q = 1
+LA_SILU_K = 2
+LA_SILU_V = 4
+LA_NORM = 8
+LA_GATE = 16
+
+
+class la_fusion(ctypes.Structure):
+    """The C struct la_fusion (include/la.h)."""
+    _fields_ = [("flags", ctypes.c_uint32), ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
 
 _lib = None
 
@@ -76,6 +88,11 @@ def lib():
     L.la_prefill_varlen.argtypes = [i32, p, p, p, p, i64, p, i64, i64, i64, i64, p, p, p, sz, p]
     L.la_prefill_varlen_ex.restype = i32
     L.la_prefill_varlen_ex.argtypes = [i32, p, p, p, p, i64, p, i64, i64, i64, i64, p, p, i64, p, sz, p]
+    L.la_prefill_fused.restype = i32
+    L.la_prefill_fused.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p,
+                                   ctypes.POINTER(la_fusion), p, sz, p]
+    L.la_decode_fused.restype = i32
+    L.la_decode_fused.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, ctypes.POINTER(la_fusion), p]
     L.la_decode.restype = i32
     L.la_decode.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, p]
     L.la_status_string.restype = ctypes.c_char_p
@@ -257,3 +274,64 @@ def mixed_step(slopes, decode=None, prefill=None, streams=None) -> None:
     if streams is not None:
         for s in streams:
             cur.wait_stream(s)
+
+
+def _fusion(silu_q=False, silu_k=False, silu_v=False, norm_eps=None, norm_weight=None, gate=None):
+    flags = (LA_SILU_Q if silu_q else 0) | (LA_SILU_K if silu_k else 0) | (LA_SILU_V if silu_v else 0)
+    if norm_eps is not None:
+        flags |= LA_NORM
+    if gate is not None:
+        flags |= LA_GATE
+    return la_fusion(flags, None if gate is None else gate.data_ptr(),
+                     None if norm_weight is None else norm_weight.data_ptr(),
+                     0.0 if norm_eps is None else float(norm_eps))
+
+
+def la_prefill_fused(q, k, v, slopes, kv, o, silu_q=False, silu_k=False, silu_v=False, norm_eps=None,
+                     norm_weight=None, gate=None, workspace=None, stream=None) -> None:
+    """la_prefill with the fused prologue/epilogue: SiLU on the selected inputs, then (optionally)
+    RMS normalisation over d with weight norm_weight [d] (float32) and eps norm_eps, then the gate
+    o * sigmoid(gate) (gate: q's shape, strides and dtype).  o is required."""
+    import torch
+
+    _require_cuda(q, k, v, slopes, kv, o, workspace, norm_weight, gate)
+    dt = _dtype_code(q)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(-1) != 1:
+        raise ValueError("q, k, v must share strides with a contiguous last dimension")
+    for t in (o, gate):
+        if t is not None and (t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype):
+            raise ValueError("o and gate must match q in shape, strides and dtype")
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d):
+        raise ValueError("norm_weight must be a float32 tensor of d elements")
+    need = la_prefill_workspace_size(dt, B, H, N, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sb, sh, sn, _ = q.stride()
+    fu = _fusion(silu_q, silu_k, silu_v, norm_eps, norm_weight, gate)
+    st = lib().la_prefill_fused(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, sb, sh, sn, _ptr(slopes),
+                                _ptr(kv), ctypes.byref(fu), _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
+    _check(st, "la_prefill_fused")
+
+
+def la_decode_fused(q, k, v, slopes, kv, o, silu_q=False, silu_k=False, silu_v=False, norm_eps=None,
+                    norm_weight=None, gate=None, stream=None) -> None:
+    """la_decode with the fused prologue/epilogue (see la_prefill_fused); gate is [B,H,d]."""
+    import torch
+
+    _require_cuda(q, k, v, slopes, kv, o, norm_weight, gate)
+    dt = _dtype_code(q)
+    B, H, d = q.shape
+    for t in (q, k, v, o) + ((gate,) if gate is not None else ()):
+        if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o (and gate) must be contiguous [B,H,d] tensors of one dtype")
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d):
+        raise ValueError("norm_weight must be a float32 tensor of d elements")
+    fu = _fusion(silu_q, silu_k, silu_v, norm_eps, norm_weight, gate)
+    st = lib().la_decode_fused(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d, _ptr(slopes), _ptr(kv),
+                               ctypes.byref(fu), _stream_ptr(stream, q.device))
+    _check(st, "la_decode_fused")
+

@@ -94,13 +94,31 @@ size_t workspace_bytes_for(const Plan& p, int64_t batch, int64_t heads, int64_t 
     return (size_t)batch * (size_t)heads * (size_t)p.n_chunks * (size_t)d * (size_t)d * sizeof(float);
 }
 
+la_status check_fusion(const la_fusion* fu, const void* o)
+{
+    if (!fu) return LA_OK;
+    if (fu->flags & ~(uint32_t)(LA_SILU_Q | LA_SILU_K | LA_SILU_V | LA_NORM | LA_GATE))
+        return fail(LA_ERR_INVALID_ARGUMENT, "unknown fusion flag");
+    if ((fu->flags & (LA_NORM | LA_GATE)) && !o)
+        return fail(LA_ERR_INVALID_ARGUMENT, "LA_NORM and LA_GATE need an output tensor");
+    if ((fu->flags & LA_GATE) && (!fu->gate || !aligned16(fu->gate)))
+        return fail(LA_ERR_INVALID_ARGUMENT, "LA_GATE needs a 16-byte aligned gate tensor");
+    if ((fu->flags & LA_NORM) && !(fu->norm_eps > 0.f))
+        return fail(LA_ERR_INVALID_ARGUMENT, "LA_NORM needs norm_eps > 0");
+    if ((fu->flags & LA_NORM) && fu->norm_weight && !aligned16(fu->norm_weight))
+        return fail(LA_ERR_INVALID_ARGUMENT, "norm_weight must be 16-byte aligned");
+    return LA_OK;
+}
+
 la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                        int64_t batch, int64_t heads, int64_t n, int64_t d,
                        int64_t sb, int64_t sh, int64_t sn, const float* slopes, float* kv,
                        float* ckpt, int64_t ckpt_every, int64_t chunk_tokens,
-                       void* workspace, size_t workspace_bytes, void* stream)
+                       void* workspace, size_t workspace_bytes, void* stream, const la_fusion* fu = nullptr)
 {
     la_status s = check_shape(dt, batch, heads, n, d);
+    if (s != LA_OK) return s;
+    s = check_fusion(fu, o);
     if (s != LA_OK) return s;
     if (!kv || !slopes) return fail(LA_ERR_INVALID_ARGUMENT, "kv and slopes must not be NULL");
     if (chunk_tokens < 0 || (chunk_tokens > 0 && chunk_tokens % kBlock != 0))
@@ -144,6 +162,9 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     a.ckpt = ckpt;
     a.ckpt_every = ckpt ? ckpt_every : 0;
     a.n_ckpt = ckpt ? n / ckpt_every : 0;
+    const uint32_t ff = fu ? fu->flags : 0u;
+    a.act = ff & (LA_SILU_Q | LA_SILU_K | LA_SILU_V);
+    a.gate = ((ff & LA_GATE) && !(ff & LA_NORM)) ? fu->gate : nullptr;  // gate alone: in the store
     const int64_t bh = batch * heads;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -161,7 +182,12 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
                           "prefix-combine launch");
         if (s != LA_OK) return s;
     }
-    return launch_status(run(o ? kModeOut : kModeState, p.n_chunks), "prefill launch");
+    s = launch_status(run(o ? kModeOut : kModeState, p.n_chunks), "prefill launch");
+    if (s != LA_OK || !(ff & LA_NORM)) return s;
+    // the normalisation needs all d features of a row: one more pass over o (gate included)
+    return launch_status(launch_norm_gate(dt, o, (ff & LA_GATE) ? fu->gate : nullptr, fu->norm_weight, fu->norm_eps,
+                                          true, batch, heads, n, (int)d, sb, sh, sn, st),
+                         "normalisation launch");
 }
 
 // ---------------------------------------------------------------- packed variable-length batches
@@ -434,10 +460,13 @@ la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, v
                          ckpt_every, 0, workspace, workspace_bytes, stream);
 }
 
-la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
-                    int64_t batch, int64_t heads, int64_t d, const float* slopes, float* kv, void* stream)
+la_status la_decode_fused(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                          int64_t batch, int64_t heads, int64_t d, const float* slopes, float* kv,
+                          const la_fusion* fusion, void* stream)
 {
     try {
+        la_status s = check_fusion(fusion, o);
+        if (s != LA_OK) return s;
         if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_INVALID_ARGUMENT, "dtype must be LA_F32 or LA_BF16");
         if (!q || !k || !v || !o || !slopes || !kv)
             return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, o, slopes and kv must not be NULL");
@@ -445,11 +474,33 @@ la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, vo
         if (d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d must be 64 or 128");
         if (batch * heads > (int64_t(1) << 31) - 1) return fail(LA_ERR_INVALID_ARGUMENT, "too many (batch, head) pairs");
         if (!aligned16(kv)) return fail(LA_ERR_INVALID_ARGUMENT, "kv must be 16-byte aligned");
-        la_status s = device_check();
+        s = device_check();
         if (s != LA_OK) return s;
-        return launch_status(launch_decode(dt, q, k, v, o, batch * heads, heads, (int)d, slopes, kv,
+        return launch_status(launch_decode(dt, q, k, v, o, batch * heads, heads, (int)d, slopes, kv, fusion,
                                            static_cast<hipStream_t>(stream)),
                              "decode launch");
+    } catch (const std::exception& e) {
+        return fail(LA_ERR_INTERNAL, e.what());
+    } catch (...) {
+        return fail(LA_ERR_INTERNAL, "unknown error");
+    }
+}
+
+la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                    int64_t batch, int64_t heads, int64_t d, const float* slopes, float* kv, void* stream)
+{
+    return la_decode_fused(dt, q, k, v, o, batch, heads, d, slopes, kv, nullptr, stream);
+}
+
+la_status la_prefill_fused(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                           int64_t batch, int64_t heads, int64_t n, int64_t d,
+                           int64_t stride_b, int64_t stride_h, int64_t stride_n,
+                           const float* slopes, float* kv, const la_fusion* fusion,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    try {
+        return prefill_impl(dt, q, k, v, o, batch, heads, n, d, stride_b, stride_h, stride_n, slopes, kv,
+                            nullptr, 0, 0, workspace, workspace_bytes, stream, fusion);
     } catch (const std::exception& e) {
         return fail(LA_ERR_INTERNAL, e.what());
     } catch (...) {

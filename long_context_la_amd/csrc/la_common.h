@@ -57,7 +57,22 @@ struct FwdArgs {
     // sequence s.  Workspace slot (c, h) = c*heads + h.
     const int64_t* ctab;
     const int64_t* stab;
+    // Fused prologue/epilogue (la_fusion): act = LA_SILU_Q | LA_SILU_K | LA_SILU_V applied to the
+    // inputs as they are loaded; gate (same layout as o, or null) multiplies each output by
+    // sigmoid(gate) before it is stored.
+    uint32_t act;
+    const void* gate;
 };
+
+// SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), in float32.
+__device__ inline float silu_f32(float x)
+{
+    return x / (1.f + __expf(-x));
+}
+__device__ inline float sigmoid_f32(float x)
+{
+    return 1.f / (1.f + __expf(-x));
+}
 
 // What one workgroup processes: a chunk of one (sequence, head).
 struct Work {
@@ -114,9 +129,15 @@ hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStre
 hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_short, int64_t heads, int d, int64_t sn, int64_t sh,
                               const float* slopes, float* kv, const int64_t* tab, hipStream_t stream);
+// Decode step; `fu` (optional) adds the SiLU prologue, RMS normalisation and gate epilogue.
 hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                          int64_t bh, int64_t heads, int d, const float* slopes, float* kv,
-                         hipStream_t stream);
+                         const la_fusion* fu, hipStream_t stream);
+// RMS normalisation over d (optional weight) and/or sigmoid gate, in place on o, for the rows
+// (b, h, t) of a [batch][heads][n] prefill output with o's strides (gate shares them).
+hipError_t launch_norm_gate(la_dtype dt, void* o, const void* gate, const float* weight, float eps, bool norm,
+                            int64_t batch, int64_t heads, int64_t n, int d, int64_t sb, int64_t sh, int64_t sn,
+                            hipStream_t stream);
 
 // Workgroup index -> (group, slice) with the slices of one group on one XCD.  Consecutive
 // workgroup ids are dispatched round-robin over the 8 XCDs, so slices that share Q/K rows

@@ -112,6 +112,24 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
     lo = cvt2(a - bits_to_f32(hi & 0xffffu), b - hi_to_f32(hi));
 }
 
+// SiLU of 8 packed bf16 values (float32 arithmetic, rounded back to bf16).
+__device__ __forceinline__ uint4 silu8(uint4 x)
+{
+    const uint32_t in[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = cvt2(silu_f32(bits_to_f32(in[e] & 0xffffu)), silu_f32(hi_to_f32(in[e])));
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+// acc[e] * sigmoid(g_e) for 4 float32 outputs and their 4 packed bf16 gate values.
+__device__ __forceinline__ void gate4(f32x4& acc, uint2 g)
+{
+    acc[0] *= sigmoid_f32(bits_to_f32(g.x & 0xffffu));
+    acc[1] *= sigmoid_f32(hi_to_f32(g.x));
+    acc[2] *= sigmoid_f32(bits_to_f32(g.y & 0xffffu));
+    acc[3] *= sigmoid_f32(hi_to_f32(g.y));
+}
+
 // Transposing LDS read (see the header comment): returns rows k0..k0+3 of column c0 + (lane % 16)
 // when this lane passes the address of row k0 + (lane%16)/4, column c0 + 4*(lane%4).
 __device__ __forceinline__ s16x4 lds_tr(const u16* p)
@@ -145,6 +163,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 
 template <int N> struct IntC { static constexpr int value = N; };
 
@@ -154,7 +176,7 @@ template <int N> struct IntC { static constexpr int value = N; };
 struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32((ks+slice)%4) + 8g .. +7
 struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
 
-template <int MODE>
+template <int MODE, bool GATE>
 __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
     constexpr bool OUT = MODE == kModeOut;
@@ -188,6 +210,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const u16* Kg = static_cast<const u16*>(a.k) + base;
     const u16* Vg = static_cast<const u16*>(a.v) + base + slice * SW;
     u16* Og = OUT ? static_cast<u16*>(a.o) + base + slice * SW : nullptr;
+    const u16* Gg = GATE ? static_cast<const u16*>(a.gate) + base + slice * SW : nullptr;
+    const bool silu_q = a.act & LA_SILU_Q, silu_k = a.act & LA_SILU_K, silu_v = a.act & LA_SILU_V;
     const int64_t sn = a.sn;
     const uint32_t row_bytes = (uint32_t)(sn * 2);
     // transposing-read address pieces: row k0 + lr/4, column c0 + 4*(lr%4)
@@ -231,12 +255,13 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int c = st_id + 256 * ((m + slice) & 3);
-            *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + 8 * (c & 15)]) = R.k[m];
+            *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + 8 * (c & 15)]) = silu_k ? silu8(R.k[m]) : R.k[m];
         }
         const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
-        *reinterpret_cast<uint4*>(&sV[buf][off]) = R.v;
+        const uint4 vx = silu_v ? silu8(R.v) : R.v;
+        *reinterpret_cast<uint4*>(&sV[buf][off]) = vx;
         const float wt = (r < L) ? decay_pow(nsl, (float)(L - 1 - r)) : 0.f;
-        const uint32_t in[4] = {R.v.x, R.v.y, R.v.z, R.v.w};
+        const uint32_t in[4] = {vx.x, vx.y, vx.z, vx.w};
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
@@ -341,7 +366,16 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int64_t t0 = tile_start(tile);
         bf16x8 qf[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, R.q[ks]);
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, silu_q ? silu8(R.q[ks]) : R.q[ks]);
+        // the gate values of this lane's outputs (row 16W + lr, columns 16jt + 4g..+3), read early
+        // so the loads are long done when the products are
+        uint2 gx[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+        if constexpr (GATE) {
+            const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gg + t0 * sn, tile_bytes(tile));
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+                gx[jt] = buf_load8(rg, (uint32_t)(16 * W + lr) * row_bytes + 2u * (16 * jt + 4 * g));
+        }
         // Issue every LDS operand read of the inter and score products up front (the fence keeps
         // the scheduler from sinking them next to their MFMAs, which would expose each read's
         // latency in turn).
@@ -420,6 +454,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
                 acc[jt] = mfma(vop[k2][jt], pl, acc[jt]);
             }
         }
+        // gate in float32, so the output is rounded to bf16 once
+        if constexpr (GATE)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) gate4(acc[jt], gx[jt]);
         // output tile: stage this wave's 16 rows (8-byte runs of 4 columns), then 16-byte stores
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
@@ -511,9 +549,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
-    if (mode == kModeOut) hipLaunchKernelGGL(k_fwd_bf16<kModeOut>, grid, dim3(512), 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL(k_fwd_bf16<kModeState>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(k_fwd_bf16<kModeLocal>, grid, dim3(256), 0, stream, a);
+    if (mode == kModeOut && a.gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

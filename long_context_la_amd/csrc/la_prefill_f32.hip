@@ -66,13 +66,16 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
             if (r < L) {
                 kx = *reinterpret_cast<const float4*>(K + (t0 + r) * a.sn + 4 * c4);
                 if (MODE == kModeOut) qx = *reinterpret_cast<const float4*>(Q + (t0 + r) * a.sn + 4 * c4);
+                if (a.act & LA_SILU_K) kx = make_float4(silu_f32(kx.x), silu_f32(kx.y), silu_f32(kx.z), silu_f32(kx.w));
+                if (a.act & LA_SILU_Q) qx = make_float4(silu_f32(qx.x), silu_f32(qx.y), silu_f32(qx.z), silu_f32(qx.w));
             }
             sK[r][4 * c4] = kx.x; sK[r][4 * c4 + 1] = kx.y; sK[r][4 * c4 + 2] = kx.z; sK[r][4 * c4 + 3] = kx.w;
             sQ[r][4 * c4] = qx.x; sQ[r][4 * c4 + 1] = qx.y; sQ[r][4 * c4 + 2] = qx.z; sQ[r][4 * c4 + 3] = qx.w;
         }
         for (int e = tid; e < BK * SW; e += 256) {
             const int r = e / SW, c = e % SW;
-            sV[r][c] = (r < L) ? V[(t0 + r) * a.sn + slice * SW + c] : 0.f;
+            const float x = (r < L) ? V[(t0 + r) * a.sn + slice * SW + c] : 0.f;
+            sV[r][c] = (a.act & LA_SILU_V) ? silu_f32(x) : x;
         }
         if (tid < BK) sW[tid] = (tid < L) ? decay_pow(nsl, (float)(L - 1 - tid)) : 0.f;
         __syncthreads();
@@ -97,6 +100,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
                 for (int i = 0; i < D; ++i) inter += sQ[r][i] * sKV[i][col];
                 float acc = decay_pow(nsl, (float)(r + 1)) * inter;
                 for (int c = 0; c <= r; ++c) acc += sP[r][c] * sV[c][col];
+                if (a.gate) acc *= sigmoid_f32(static_cast<const float*>(a.gate)[base + (t0 + r) * a.sn + slice * SW + col]);
                 O[(t0 + r) * a.sn + slice * SW + col] = acc;
             }
         }
