@@ -28,6 +28,10 @@ Forms provided (each a separate, literal transcription of one definition):
   decode     -- one step of the recurrence
   chunk states / LASP+ combine -- local summaries from a zero state, then
                 prefixes P_{j+1} = lambda^{C_j} P_j + S_j.
+  backward   -- gradients of a scalar loss through the recurrence (dq, dk, dv and the
+                incoming state's gradient, given dL/dO and optionally dL/dKV_final), as the
+                reverse-order state recurrence and as the n x n masked form; LASP+'s
+                training side (section 3.2) runs this reverse recurrence across partitions.
   prologue / epilogue -- the pieces the derivation leaves out (section 2.2
                 names normalisation, SiLU and gating; section 3.3 fuses such
                 memory-bound steps into the attention kernels): SiLU on q, k, v
@@ -39,6 +43,7 @@ the pins live in tests/test_oracle_pins.py.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -272,3 +277,74 @@ def fused(q, k, v, slopes, kv_in=None, silu_q=False, silu_k=False, silu_v=False,
         o = o * sigmoid(gate)
     return o, kv
 
+
+
+# ---------------------------------------------------------------- backward (training)
+# For a scalar loss L with dO = dL/dO and G_out = dL/dKV_final (zero when not given), differentiate
+#     KV_t = lambda KV_{t-1} + k_t^T v_t,   o_t = q_t KV_t,   KV_{-1} = KV_in.
+# The gradient reaching the state after token t, G_t = dL/dKV_t (all paths), obeys the reverse
+# recurrence
+#     G_{N-1} = q_{N-1}^T do_{N-1} + G_out,   G_t = q_t^T do_t + lambda G_{t+1},
+# and then  dq_t = do_t KV_t^T,  dk_t = v_t G_t^T,  dv_t = k_t G_t,  dL/dKV_in = lambda G_0
+# (= G_out for N = 0).  The slopes are constants (not differentiated).
+
+def backward_recurrent(q, k, v, do, slopes, kv_in=None, dkv_out=None):
+    """Token-by-token form: a forward pass for the states KV_t, then the reverse pass for G_t.
+
+    q, k, v, do: [B, H, N, d]; kv_in, dkv_out: [B, H, d, d] or None.
+    Returns (dq, dk, dv, dkv_in), float64."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, H, N, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    dkv_in = np.empty((B, H, d, d))
+    for b in range(B):
+        for h in range(H):
+            lam = math.exp(-float(slopes[h]))
+            KV = np.zeros((d, d)) if kv_in is None else np.array(kv_in[b, h], dtype=np.float64)
+            for t in range(N):
+                KV = lam * KV + np.outer(k[b, h, t], v[b, h, t])
+                dq[b, h, t] = do[b, h, t] @ KV.T
+            # `arriving` is what later tokens (or G_out, for the last one) pass back to G_t
+            arriving = np.zeros((d, d)) if dkv_out is None else np.array(dkv_out[b, h], dtype=np.float64)
+            for t in range(N - 1, -1, -1):
+                G = np.outer(q[b, h, t], do[b, h, t]) + arriving
+                dk[b, h, t] = v[b, h, t] @ G.T
+                dv[b, h, t] = k[b, h, t] @ G
+                arriving = lam * G
+            dkv_in[b, h] = arriving
+    return dq, dk, dv, dkv_in
+
+
+def backward_quadratic(q, k, v, do, slopes, kv_in=None, dkv_out=None):
+    """The n x n form of the same gradients, with A = (dO V^T) . M and P = (Q K^T) . M:
+        dQ = A K + diag(lambda^(t+1)) dO KV_in^T
+        dK = A^T Q + diag(lambda^(N-1-s)) V G_out^T
+        dV = P^T dO + diag(lambda^(N-1-s)) K G_out
+        dKV_in = Q^T diag(lambda^(t+1)) dO + lambda^N G_out.
+    Returns (dq, dk, dv, dkv_in), float64."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, H, N, d = q.shape
+    t = np.arange(N)
+    diff = t[:, None] - t[None, :]
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    dkv_in = np.empty((B, H, d, d))
+    for b in range(B):
+        for h in range(H):
+            s = float(slopes[h])
+            M = np.where(diff >= 0, np.exp(-s * np.maximum(diff, 0)), 0.0)
+            Q, K, Vm, dO = q[b, h], k[b, h], v[b, h], do[b, h]
+            A = (dO @ Vm.T) * M
+            P = (Q @ K.T) * M
+            dq[b, h] = A @ K
+            dk[b, h] = A.T @ Q
+            dv[b, h] = P.T @ dO
+            dkv_in[b, h] = (Q * decay_powers(s, t + 1)[:, None]).T @ dO
+            if kv_in is not None:
+                dq[b, h] += decay_powers(s, t + 1)[:, None] * (dO @ np.asarray(kv_in[b, h], dtype=np.float64).T)
+            if dkv_out is not None:
+                Gout = np.asarray(dkv_out[b, h], dtype=np.float64)
+                w = decay_powers(s, N - 1 - t)[:, None]
+                dk[b, h] += w * (Vm @ Gout.T)
+                dv[b, h] += w * (K @ Gout)
+                dkv_in[b, h] += decay_powers(s, N) * Gout
+    return dq, dk, dv, dkv_in

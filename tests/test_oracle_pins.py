@@ -367,3 +367,129 @@ def test_p13_fused_without_options_is_the_recurrence():
     o, _ = oracle.fused(*exact, slopes, silu_q=True, silu_k=True)
     o_r, _, _ = oracle.recurrent(oracle.silu(exact[0]), oracle.silu(exact[1]), exact[2], slopes)
     np.testing.assert_allclose(o, o_r, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward pins
+# The backward oracle (reverse state recurrence and n x n form) is tied to the forward definition by
+# automatic differentiation (torch, float64, CPU, of the token recurrence written out below) and by
+# central finite differences of the oracle's own forward; mutants show the pins bite.
+
+def _bwd_inputs(seed, B, H, N, d, with_state=True):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    kv = rng.standard_normal((B, H, d, d)) if with_state else None
+    g = rng.standard_normal((B, H, d, d)) if with_state else None
+    slopes = np.array([0.05 + 0.6 * h for h in range(H)])
+    return q, k, v, do, kv, g, slopes
+
+
+def _loss(q, k, v, do, slopes, kv, g):
+    """L = sum(dO . O) + sum(G_out . KV_final) through the oracle's forward (quadratic form)."""
+    o, kv_out = oracle.quadratic(q, k, v, slopes, kv_in=kv)
+    return float(np.sum(do * o) + (0.0 if g is None else np.sum(g * kv_out)))
+
+
+@pytest.mark.parametrize("form", ["recurrent", "quadratic"])
+def test_p14_backward_matches_autograd(form):
+    torch = pytest.importorskip("torch")
+    q, k, v, do, kv, g, slopes = _bwd_inputs(5, 1, 2, 23, 6)
+    want = getattr(oracle, "backward_" + form)(q, k, v, do, slopes, kv_in=kv, dkv_out=g)
+    T = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, kv)]
+    tq, tk, tv, tkv = T
+    loss = torch.zeros((), dtype=torch.float64)
+    for h in range(2):
+        lam = math.exp(-slopes[h])
+        S = tkv[0, h]
+        for t in range(q.shape[2]):
+            S = lam * S + torch.outer(tk[0, h, t], tv[0, h, t])
+            loss = loss + torch.dot(tq[0, h, t] @ S, torch.tensor(do[0, h, t]))
+        loss = loss + torch.sum(S * torch.tensor(g[0, h]))
+    grads = torch.autograd.grad(loss, T)
+    for name, got, ref in zip(("dq", "dk", "dv", "dkv_in"), want, grads):
+        assert _rel(got, ref.numpy()) < 1e-12, name
+
+
+def test_p15_backward_matches_finite_differences():
+    q, k, v, do, kv, g, slopes = _bwd_inputs(6, 1, 2, 7, 3)
+    grads = oracle.backward_recurrent(q, k, v, do, slopes, kv_in=kv, dkv_out=g)
+    rng = np.random.default_rng(11)
+    eps = 1e-5
+    for which in range(4):
+        for _ in range(3):
+            x = [q, k, v, kv]
+            u = rng.standard_normal(x[which].shape)
+            xp, xm = list(x), list(x)
+            xp[which] = x[which] + eps * u
+            xm[which] = x[which] - eps * u
+            fd = (_loss(xp[0], xp[1], xp[2], do, slopes, xp[3], g) -
+                  _loss(xm[0], xm[1], xm[2], do, slopes, xm[3], g)) / (2 * eps)
+            an = float(np.sum(grads[which] * u))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 4), (2, 2, 65, 8), (1, 3, 130, 5)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_p16_backward_forms_agree(shape, with_state):
+    q, k, v, do, kv, g, slopes = _bwd_inputs(7, *shape, with_state=with_state)
+    a = oracle.backward_recurrent(q, k, v, do, slopes, kv_in=kv, dkv_out=g)
+    b = oracle.backward_quadratic(q, k, v, do, slopes, kv_in=kv, dkv_out=g)
+    for x, y in zip(a, b):
+        assert _rel(x, y) < 1e-12
+
+
+def test_p17_backward_empty_sequence_and_no_decay():
+    # N = 0: the incoming state's gradient is the outgoing one, untouched
+    q, k, v, do, kv, g, slopes = _bwd_inputs(8, 1, 2, 0, 4)
+    dq, dk, dv, dkv = oracle.backward_recurrent(q, k, v, do, slopes, kv_in=kv, dkv_out=g)
+    assert dq.shape == (1, 2, 0, 4) and np.array_equal(dkv, g)
+    # lambda = 1: dV_s = sum_{t >= s} (q_t . k_s) do_t + k_s G_out -- reverse cumulative sums
+    q, k, v, do, kv, g, _ = _bwd_inputs(9, 1, 1, 12, 3)
+    _, _, dv, dkv = oracle.backward_recurrent(q, k, v, do, np.zeros(1), kv_in=kv, dkv_out=g)
+    Q, K, dO = q[0, 0], k[0, 0], do[0, 0]
+    rev = np.cumsum((Q[:, :, None] * dO[:, None, :])[::-1], axis=0)[::-1]  # sum_{t >= s} q_t^T do_t
+    want = np.einsum("si,sij->sj", K, rev) + K @ g[0, 0]
+    assert _rel(dv[0, 0], want) < 1e-12
+    assert _rel(dkv[0, 0], Q.T @ dO + g[0, 0]) < 1e-12
+
+
+def _mutant_backward(q, k, v, do, slopes, kv, g, kind):
+    """Deliberately wrong variants of the reverse recurrence (one (b, h) of index 0 only)."""
+    lam = math.exp(-float(slopes[0]))
+    Q, K, Vm, dO = (x[0, 0] for x in (q, k, v, do))
+    N, d = Q.shape
+    arriving = g[0, 0].copy() if kind != "drop_g_out" else np.zeros((d, d))
+    dk, dv = np.empty_like(Q), np.empty_like(Q)
+    for t in range(N - 1, -1, -1):
+        if kind == "decay_before_add":
+            G = lam * (np.outer(Q[t], dO[t]) + arriving)
+        else:
+            G = np.outer(Q[t], dO[t]) + arriving
+        dk[t] = Vm[t] @ (G if kind == "untransposed_dk" else G.T)
+        dv[t] = K[t] @ G
+        arriving = lam * G
+    return dk, dv
+
+
+@pytest.mark.parametrize("kind", ["drop_g_out", "decay_before_add", "untransposed_dk"])
+def test_backward_planted_mistakes_are_caught(kind):
+    q, k, v, do, kv, g, slopes = _bwd_inputs(10, 1, 1, 6, 3)
+    rng = np.random.default_rng(12)
+    eps = 1e-5
+
+    def fd(which):
+        u = rng.standard_normal(q.shape)
+        x = [q, k, v]
+        xp, xm = list(x), list(x)
+        xp[which] = x[which] + eps * u
+        xm[which] = x[which] - eps * u
+        return u, (_loss(*xp, do, slopes, kv, g) - _loss(*xm, do, slopes, kv, g)) / (2 * eps)
+
+    def caught(dk, dv):
+        bad = False
+        for which, grad in ((1, dk), (2, dv)):
+            u, f = fd(which)
+            bad |= abs(f - float(np.sum(grad * u[0, 0]))) > 1e-3 * max(1.0, abs(f))
+        return bad
+
+    assert caught(*_mutant_backward(q, k, v, do, slopes, kv, g, kind))
+    assert not caught(*_mutant_backward(q, k, v, do, slopes, kv, g, "correct"))
