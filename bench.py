@@ -28,6 +28,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 MODEL_TILE = 256               # the pages' tile: flop model 4*B*d + 4*d^2 per token-head
 BYTES_PER_TOKEN_HEAD = 4 * 128 * 2   # q, k, v read + o write, bf16, d = 128
+BWD_BYTES_PER_TOKEN_HEAD = 7 * 128 * 2  # backward: q, k, v, dO read + dq, dk, dv write, bf16
 DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 4 * 128 * 2   # state read + write, q/k/v/o
 
 
@@ -114,7 +115,7 @@ def make_prefill_inputs(w, device, head_group=8):
     return out
 
 
-def time_prefill(w, steps, warmup, device):
+def time_prefill(w, steps, warmup, device, with_backward=True):
     import torch
 
     import long_context_la_amd as la
@@ -157,8 +158,48 @@ def time_prefill(w, steps, warmup, device):
     varlen = None
     if w.batch == 1 and sum(VARLEN_LENGTHS) == w.n:
         varlen = time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device)
+    backward = time_backward(q, k, v, o, slopes, w, steps, warmup, device) if with_backward else None
     del q, k, v, o, ws
-    return ms, kernel_ms, n_chunks, varlen
+    return ms, kernel_ms, n_chunks, varlen, backward
+
+
+def time_backward(q, k, v, dout, slopes, w, steps, warmup, device):
+    """la_backward over the same layer (the prefill's output stands in for dL/dO), with a
+    dL/dKV_final, timed per call on the launch stream."""
+    import torch
+
+    import long_context_la_amd as la
+
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    g = torch.ones(w.batch, w.heads, w.d, w.d, dtype=torch.float32, device=device)
+    dkv = torch.empty_like(g)
+    ws = torch.empty(la.la_backward_workspace_size(la.LA_BF16, w.batch, w.heads, w.n, w.d), dtype=torch.uint8,
+                     device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def call():
+        la.la_backward(q, k, v, dout, slopes, dkv_out=g, dq=dq, dk=dk, dv=dv, dkv_in=dkv, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    th = w.batch * w.heads * w.n
+    log(f"backward: {ms:.3f} ms ({th * BWD_BYTES_PER_TOKEN_HEAD / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic)")
+    del dq, dk, dv, ws
+    return {"workload": f"backward of the {w.name} prefill: dq, dk, dv (bf16) and dL/dKV_in from dL/dO and "
+                        f"dL/dKV_final",
+            "ms_per_step": ms, "tokens_per_s": w.batch * w.n / (ms * 1e-3),
+            "hbm_GBs": th * BWD_BYTES_PER_TOKEN_HEAD / (ms * 1e-3) / 1e9,
+            "hbm_frac": th * BWD_BYTES_PER_TOKEN_HEAD / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "bytes_per_token_head": BWD_BYTES_PER_TOKEN_HEAD,
+            "passes": 3, "pass_bytes_per_token_head": 3 * BYTES_PER_TOKEN_HEAD}
 
 
 def time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device):
@@ -334,6 +375,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
@@ -353,7 +395,8 @@ def main():
         return
     la.lib()
     w = synth.WORKLOADS[args.workload]
-    ms, kernel_ms, n_chunks, varlen = time_prefill(w, args.steps, args.warmup, device)
+    ms, kernel_ms, n_chunks, varlen, backward = time_prefill(w, args.steps, args.warmup, device,
+                                                             with_backward=not args.no_backward)
     token_heads = w.batch * w.heads * w.n
     tokens_s = w.batch * w.n / (ms * 1e-3)
     flops = model_flops_per_token_head(w.d) * token_heads
@@ -383,6 +426,8 @@ def main():
     }
     if varlen is not None:
         result["varlen"] = varlen
+    if backward is not None:
+        result["backward"] = backward
     if not args.no_decode:
         result["mixed_batch"] = time_mixed(device)
         wd = synth.WORKLOADS["decode"]

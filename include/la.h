@@ -223,6 +223,37 @@ la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, vo
                     int64_t batch, int64_t heads, int64_t d,
                     const float* slopes, float* kv, void* stream);
 
+/*
+ * Backward pass (training): gradients of a scalar loss L through la_prefill's
+ * computation, given dout = dL/dO and optionally dkv_out = dL/dKV_final.  The
+ * training side of LASP+ (section 3.2 of the page above) passes the state's
+ * gradient backwards between partitions; here dkv_out is what a later
+ * partition passes back and dkv_in what this one passes on.  With
+ * G_t = dL/dKV_t (G_t = q_t^T do_t + lambda G_{t+1}, G_{n-1} = q^T do + dkv_out):
+ *   dq_t = do_t KV_t^T,  dk_t = v_t G_t^T,  dv_t = k_t G_t,  dkv_in = lambda G_0.
+ * The slopes are constants (no gradient).  Computed as three runs of the
+ * prefill kernels (one forward, two walking the sequence backwards), so it
+ * costs about three prefills.
+ *   q, k, v, dout       : inputs of the forward pass and dL/dO, layout and
+ *                         strides as for la_prefill (read-only, may alias).
+ *   kv_in               : the forward pass's incoming state, or NULL (zero).
+ *   dkv_out             : dL/dKV_final [batch][heads][d][d] float32, or NULL (zero).
+ *                         Requires s_h < 80 (lambda > e^-80): it is scaled by 1/lambda.
+ *   dq, dk, dv          : outputs, same layout and dtype; must not overlap the
+ *                         inputs or each other.
+ *   dkv_in              : output dL/dKV_in [batch][heads][d][d] float32, or NULL
+ *                         (not wanted); may alias kv_in or dkv_out.
+ *   workspace           : at least la_backward_workspace_size() bytes (never 0).
+ * No fused prologue/epilogue.  Supported dtypes and d as for la_prefill.
+ * n == 0 gives dkv_in = dkv_out.  Asynchronous on `stream`.
+ */
+size_t la_backward_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d);
+la_status la_backward(la_dtype dt, const void* q, const void* k, const void* v, const void* dout,
+                      int64_t batch, int64_t heads, int64_t n, int64_t d,
+                      int64_t stride_b, int64_t stride_h, int64_t stride_n, const float* slopes,
+                      const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 

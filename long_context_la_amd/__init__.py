@@ -33,7 +33,8 @@ EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_si
             "la_prefill_workspace_size_ex", "la_prefill", "la_prefill_ex",
             "la_prefill_varlen_workspace_size", "la_prefill_varlen_workspace_size_ex",
             "la_prefill_varlen_chunk_tokens", "la_prefill_varlen", "la_prefill_varlen_ex", "la_decode",
-            "la_prefill_fused", "la_decode_fused", "la_status_string", "la_last_error"]
+            "la_prefill_fused", "la_decode_fused", "la_backward_workspace_size", "la_backward",
+            "la_status_string", "la_last_error"]
 
 LA_SILU_Q = 1
 LA_SILU_K = 2
@@ -93,6 +94,10 @@ def lib():
                                    ctypes.POINTER(la_fusion), p, sz, p]
     L.la_decode_fused.restype = i32
     L.la_decode_fused.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, ctypes.POINTER(la_fusion), p]
+    L.la_backward_workspace_size.restype = sz
+    L.la_backward_workspace_size.argtypes = [i32, i64, i64, i64, i64]
+    L.la_backward.restype = i32
+    L.la_backward.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
     L.la_decode.restype = i32
     L.la_decode.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, p]
     L.la_status_string.restype = ctypes.c_char_p
@@ -335,3 +340,47 @@ def la_decode_fused(q, k, v, slopes, kv, o, silu_q=False, silu_k=False, silu_v=F
                                ctypes.byref(fu), _stream_ptr(stream, q.device))
     _check(st, "la_decode_fused")
 
+
+
+def la_backward_workspace_size(dtype: int, batch: int, heads: int, n: int, d: int) -> int:
+    return int(lib().la_backward_workspace_size(dtype, batch, heads, n, d))
+
+
+def la_backward(q, k, v, dout, slopes, kv_in=None, dkv_out=None, dq=None, dk=None, dv=None, dkv_in=None,
+                workspace=None, stream=None):
+    """Gradients of a loss through la_prefill: given dout = dL/dO (q's shape, strides, dtype) and
+    optionally dkv_out = dL/dKV_final [B,H,d,d] float32, returns (dq, dk, dv, dkv_in) with
+    dkv_in = dL/dKV_in [B,H,d,d] float32.  kv_in is the forward pass's incoming state (None:
+    zero).  Outputs are allocated when not given (dq, dk, dv like q)."""
+    import torch
+
+    _require_cuda(q, k, v, dout, slopes, kv_in, dkv_out, dq, dk, dv, dkv_in, workspace)
+    dt = _dtype_code(q)
+    B, H, N, d = q.shape
+    for t in (k, v, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or t.stride() != q.stride():
+            raise ValueError("q, k, v, dout must share shape, strides and dtype")
+    if q.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    outs = []
+    for t in (dq, dk, dv):
+        if t is None:
+            t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        elif t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+            raise ValueError("dq, dk, dv must match q in shape, strides and dtype")
+        outs.append(t)
+    for t in (kv_in, dkv_out, dkv_in):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, d, d) or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [B,H,d,d]")
+    if dkv_in is None:
+        dkv_in = torch.empty(B, H, d, d, dtype=torch.float32, device=q.device)
+    need = la_backward_workspace_size(dt, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    sb, sh, sn, _ = q.stride()
+    st = lib().la_backward(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, sb, sh, sn, _ptr(slopes),
+                           _ptr(kv_in), _ptr(dkv_out), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(dkv_in),
+                           _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
+    _check(st, "la_backward")
+    return outs[0], outs[1], outs[2], dkv_in

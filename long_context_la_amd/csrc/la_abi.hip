@@ -114,7 +114,8 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
                        int64_t batch, int64_t heads, int64_t n, int64_t d,
                        int64_t sb, int64_t sh, int64_t sn, const float* slopes, float* kv,
                        float* ckpt, int64_t ckpt_every, int64_t chunk_tokens,
-                       void* workspace, size_t workspace_bytes, void* stream, const la_fusion* fu = nullptr)
+                       void* workspace, size_t workspace_bytes, void* stream, const la_fusion* fu = nullptr,
+                       bool rev = false)
 {
     la_status s = check_shape(dt, batch, heads, n, d);
     if (s != LA_OK) return s;
@@ -165,6 +166,7 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     const uint32_t ff = fu ? fu->flags : 0u;
     a.act = ff & (LA_SILU_Q | LA_SILU_K | LA_SILU_V);
     a.gate = ((ff & LA_GATE) && !(ff & LA_NORM)) ? fu->gate : nullptr;  // gate alone: in the store
+    a.rev = rev ? 1 : 0;
     const int64_t bh = batch * heads;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -188,6 +190,67 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     return launch_status(launch_norm_gate(dt, o, (ff & LA_GATE) ? fu->gate : nullptr, fu->norm_weight, fu->norm_eps,
                                           true, batch, heads, n, (int)d, sb, sh, sn, st),
                          "normalisation launch");
+}
+
+// ---------------------------------------------------------------- backward pass
+// Gradients of a loss through the recurrence (the reverse state recurrence that the training side
+// of LASP+, page "MiniMax-01: Scaling Foundation Models with Lightning Attention | Summary",
+// section 3.2, passes between partitions).  With G_t = dL/dKV_t:
+//   dq_t = do_t KV_t^T                          -- the forward recurrence of (dO, V, K) from KV_in^T
+//   dv_t = k_t G_t,  G_t = q_t^T do_t + l G_{t+1} -- the recurrence of (K, Q, dO) walked backwards,
+//   dk_t = v_t G_t^T                            -- and of (V, dO, Q) backwards for G^T,
+// each started from dL/dKV_final / lambda (the first reversed token adds it undecayed), and
+// dL/dKV_in = lambda G_0.  So the three gradients are three runs of the prefill kernels.
+size_t state_bytes(int64_t batch, int64_t heads, int64_t d)
+{
+    return (size_t)batch * (size_t)heads * (size_t)d * (size_t)d * sizeof(float);
+}
+
+la_status backward_impl(la_dtype dt, const void* q, const void* k, const void* v, const void* dout,
+                        int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t sb, int64_t sh, int64_t sn,
+                        const float* slopes, const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv,
+                        float* dkv_in, void* workspace, size_t workspace_bytes, void* stream)
+{
+    la_status s = check_shape(dt, batch, heads, n, d);
+    if (s != LA_OK) return s;
+    if (!slopes) return fail(LA_ERR_INVALID_ARGUMENT, "slopes must not be NULL");
+    if (n > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
+        return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk, dv must not be NULL");
+    if ((kv_in && !aligned16(kv_in)) || (dkv_out && !aligned16(dkv_out)) || (dkv_in && !aligned16(dkv_in)))
+        return fail(LA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
+    const Plan p = make_plan(batch, heads, n, d, 0);
+    const size_t sbytes = state_bytes(batch, heads, d);
+    const size_t need = sbytes + workspace_bytes_for(p, batch, heads, d);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "workspace missing, misaligned or smaller than la_backward_workspace_size");
+    s = device_check();
+    if (s != LA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* S = static_cast<float*>(workspace);
+    void* chunk_ws = static_cast<char*>(workspace) + sbytes;
+    const size_t chunk_bytes = workspace_bytes - sbytes;
+    const int64_t bh = batch * heads;
+    auto prep = [&](float* dst, const float* src, bool tr, int power) {
+        return launch_status(launch_state_prep(dst, src, slopes, bh, heads, (int)d, tr, power, st), "state set-up launch");
+    };
+    if (n == 0) return dkv_in ? prep(dkv_in, dkv_out, false, 0) : LA_OK;
+    // dQ: (dO, V, K) forward from KV_in^T
+    s = prep(S, kv_in, true, 0);
+    if (s == LA_OK)
+        s = prefill_impl(dt, dout, v, k, dq, batch, heads, n, d, sb, sh, sn, slopes, S, nullptr, 0, 0, chunk_ws,
+                         chunk_bytes, stream);
+    // dK: (V, dO, Q) backwards from (dL/dKV_final / lambda)^T
+    if (s == LA_OK) s = prep(S, dkv_out, true, dkv_out ? 1 : 0);
+    if (s == LA_OK)
+        s = prefill_impl(dt, v, dout, q, dk, batch, heads, n, d, sb, sh, sn, slopes, S, nullptr, 0, 0, chunk_ws,
+                         chunk_bytes, stream, nullptr, true);
+    // dV: (K, Q, dO) backwards from dL/dKV_final / lambda; the final state is G_0
+    if (s == LA_OK) s = prep(S, dkv_out, false, dkv_out ? 1 : 0);
+    if (s == LA_OK)
+        s = prefill_impl(dt, k, q, dout, dv, batch, heads, n, d, sb, sh, sn, slopes, S, nullptr, 0, 0, chunk_ws,
+                         chunk_bytes, stream, nullptr, true);
+    if (s == LA_OK && dkv_in) s = prep(dkv_in, S, false, -1);
+    return s;
 }
 
 // ---------------------------------------------------------------- packed variable-length batches
@@ -501,6 +564,28 @@ la_status la_prefill_fused(la_dtype dt, const void* q, const void* k, const void
     try {
         return prefill_impl(dt, q, k, v, o, batch, heads, n, d, stride_b, stride_h, stride_n, slopes, kv,
                             nullptr, 0, 0, workspace, workspace_bytes, stream, fusion);
+    } catch (const std::exception& e) {
+        return fail(LA_ERR_INTERNAL, e.what());
+    } catch (...) {
+        return fail(LA_ERR_INTERNAL, "unknown error");
+    }
+}
+
+size_t la_backward_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)
+{
+    if (check_shape(dt, batch, heads, n, d) != LA_OK) return 0;
+    return state_bytes(batch, heads, d) + workspace_bytes_for(make_plan(batch, heads, n, d, 0), batch, heads, d);
+}
+
+la_status la_backward(la_dtype dt, const void* q, const void* k, const void* v, const void* dout,
+                      int64_t batch, int64_t heads, int64_t n, int64_t d,
+                      int64_t stride_b, int64_t stride_h, int64_t stride_n, const float* slopes,
+                      const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    try {
+        return backward_impl(dt, q, k, v, dout, batch, heads, n, d, stride_b, stride_h, stride_n, slopes, kv_in,
+                             dkv_out, dq, dk, dv, dkv_in, workspace, workspace_bytes, stream);
     } catch (const std::exception& e) {
         return fail(LA_ERR_INTERNAL, e.what());
     } catch (...) {

@@ -62,6 +62,9 @@ struct FwdArgs {
     // sigmoid(gate) before it is stored.
     uint32_t act;
     const void* gate;
+    // Reverse walk (fixed-length batches only): token t of the recurrence is memory row n-1-t
+    // of its sequence; outputs are written to the same rows.  Used by the backward pass.
+    int rev;
 };
 
 // SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), in float32.
@@ -126,6 +129,11 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
 hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
                               int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream);
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);
+// dst[u] := scale_u * src[u] (or its transpose), for the bh d x d states u; src == NULL gives
+// zeros.  scale_u = exp(power * s_h), h = u % heads, power in {-1, 0, 1}.  dst may equal src
+// only without the transpose.
+hipError_t launch_state_prep(float* dst, const float* src, const float* slopes, int64_t bh, int64_t heads,
+                             int d, bool transpose, int power, hipStream_t stream);
 hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_short, int64_t heads, int d, int64_t sn, int64_t sh,
                               const float* slopes, float* kv, const int64_t* tab, hipStream_t stream);

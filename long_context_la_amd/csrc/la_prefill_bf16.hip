@@ -176,9 +176,12 @@ template <int N> struct IntC { static constexpr int value = N; };
 struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32((ks+slice)%4) + 8g .. +7
 struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
 
-template <int MODE, bool GATE>
+// REV walks each sequence from its last token to its first (token index t of the recurrence is
+// memory row n-1-t), the order of the reverse state recurrence of the backward pass.
+template <int MODE, bool GATE, bool REV>
 __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
+    static_assert(!(GATE && REV), "the reverse walk has no epilogue");
     constexpr bool OUT = MODE == kModeOut;
     constexpr int SW0 = OUT ? 4 : 0;  // first state wave
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
@@ -230,6 +233,21 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int L = tile_len(tile);
         return (int64_t)(L > 0 ? L : 0) * row_bytes;
     };
+    // Memory row of a tile's first byte, and the byte offset of its row r.  In the reverse walk
+    // the tile's L rows lie backwards from memory row n - t0 - 1, so row r sits at L-1-r from
+    // memory row n - t0 - L; rows r >= L wrap to offsets far above the tile's byte count, which
+    // the buffer range check turns into zero loads and dropped stores, as for forward rows >= L.
+    auto tile_row0 = [&](int tile) __attribute__((always_inline)) {
+        const int64_t t0 = tile_start(tile);
+        if constexpr (!REV) return t0;
+        const int L = tile_len(tile);
+        const int64_t r0 = a.n - t0 - (L > 0 ? L : 0);
+        return r0 > 0 ? r0 : (int64_t)0;
+    };
+    auto row_off = [&](int tile, int r) __attribute__((always_inline)) {
+        if constexpr (!REV) return (uint32_t)r * row_bytes;
+        return (uint32_t)(tile_len(tile) - 1 - r) * row_bytes;
+    };
 
     // ------------------------------------------------------------------ state waves
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
@@ -239,15 +257,15 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     auto st_count = [](int sw) constexpr { return OUT ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : 4; };
 
     auto load_kv = [&](KVRegs& R, int tile) __attribute__((always_inline)) {
-        const int64_t t0 = tile_start(tile);
+        const int64_t t0 = tile_row0(tile);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, tile_bytes(tile));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, tile_bytes(tile));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int c = st_id + 256 * ((m + slice) & 3);
-            R.k[m] = buf_load16(rk, (uint32_t)(c >> 4) * row_bytes + 16u * (c & 15));
+            R.k[m] = buf_load16(rk, row_off(tile, c >> 4) + 16u * (c & 15));
         }
-        R.v = buf_load16(rv, (uint32_t)(st_id >> 2) * row_bytes + 16u * (st_id & 3));
+        R.v = buf_load16(rv, row_off(tile, st_id >> 2) + 16u * (st_id & 3));
     };
     // K and V rows into LDS buffer `buf`, with the decay-weighted V as bf16 hi + lo.
     auto stage_tile = [&](const KVRegs& R, int buf, int tile) __attribute__((always_inline)) {
@@ -354,16 +372,16 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
     auto load_q = [&](QRegs& R, int tile) __attribute__((always_inline)) {
-        const int64_t t0 = tile_start(tile);
+        const int64_t t0 = tile_row0(tile);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, tile_bytes(tile));
-        const uint32_t off = (uint32_t)(16 * w + lr) * row_bytes + 16u * g;
+        const uint32_t off = row_off(tile, 16 * w + lr) + 16u * g;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ((ks + slice) & 3));
     };
     // Outputs of tile `tile` from LDS buffer `buf`; R.q is refilled with tile next_q once consumed.
     auto compute_out = [&](auto wc, QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
-        const int64_t t0 = tile_start(tile);
+        const int64_t t0 = tile_row0(tile);
         bf16x8 qf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, silu_q ? silu8(R.q[ks]) : R.q[ks]);
@@ -469,7 +487,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + t0 * sn, tile_bytes(tile));
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
-                                                   (int)((uint32_t)rr * row_bytes + 2u * cc), 0, 0);
+                                                   (int)(row_off(tile, rr) + 2u * cc), 0, 0);
         }
     };
 
@@ -549,10 +567,14 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
-    if (mode == kModeOut && a.gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true>), grid, dim3(512), 0, stream, a);
-    else if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false>), grid, dim3(512), 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false>), grid, dim3(256), 0, stream, a);
+    if (a.rev) {  // the backward pass: no epilogue, no checkpoints, fixed-length batches
+        if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, true>), grid, dim3(512), 0, stream, a);
+        else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, true>), grid, dim3(256), 0, stream, a);
+    } else if (mode == kModeOut && a.gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true, false>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, false>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -47,6 +47,9 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     const float* V = static_cast<const float*>(a.v) + base;
     float* O = static_cast<float*>(a.o) + base;
     const int64_t d2 = (int64_t)D * D;
+    // memory row of token t of the recurrence: t, or n-1-t when the sequence is walked backwards
+    // (the reverse state recurrence of the backward pass)
+    auto mrow = [&](int64_t t) { return a.rev ? a.n - 1 - t : t; };
 
     // incoming state slice
     float st[RPT];
@@ -64,8 +67,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
             const int r = e / (D / 4), c4 = e % (D / 4);
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), qx = kx;
             if (r < L) {
-                kx = *reinterpret_cast<const float4*>(K + (t0 + r) * a.sn + 4 * c4);
-                if (MODE == kModeOut) qx = *reinterpret_cast<const float4*>(Q + (t0 + r) * a.sn + 4 * c4);
+                kx = *reinterpret_cast<const float4*>(K + mrow(t0 + r) * a.sn + 4 * c4);
+                if (MODE == kModeOut) qx = *reinterpret_cast<const float4*>(Q + mrow(t0 + r) * a.sn + 4 * c4);
                 if (a.act & LA_SILU_K) kx = make_float4(silu_f32(kx.x), silu_f32(kx.y), silu_f32(kx.z), silu_f32(kx.w));
                 if (a.act & LA_SILU_Q) qx = make_float4(silu_f32(qx.x), silu_f32(qx.y), silu_f32(qx.z), silu_f32(qx.w));
             }
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
         }
         for (int e = tid; e < BK * SW; e += 256) {
             const int r = e / SW, c = e % SW;
-            const float x = (r < L) ? V[(t0 + r) * a.sn + slice * SW + c] : 0.f;
+            const float x = (r < L) ? V[mrow(t0 + r) * a.sn + slice * SW + c] : 0.f;
             sV[r][c] = (a.act & LA_SILU_V) ? silu_f32(x) : x;
         }
         if (tid < BK) sW[tid] = (tid < L) ? decay_pow(nsl, (float)(L - 1 - tid)) : 0.f;
@@ -100,8 +103,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
                 for (int i = 0; i < D; ++i) inter += sQ[r][i] * sKV[i][col];
                 float acc = decay_pow(nsl, (float)(r + 1)) * inter;
                 for (int c = 0; c <= r; ++c) acc += sP[r][c] * sV[c][col];
-                if (a.gate) acc *= sigmoid_f32(static_cast<const float*>(a.gate)[base + (t0 + r) * a.sn + slice * SW + col]);
-                O[(t0 + r) * a.sn + slice * SW + col] = acc;
+                if (a.gate) acc *= sigmoid_f32(static_cast<const float*>(a.gate)[base + mrow(t0 + r) * a.sn + slice * SW + col]);
+                O[mrow(t0 + r) * a.sn + slice * SW + col] = acc;
             }
         }
 

@@ -80,7 +80,35 @@ __global__ __launch_bounds__(256) void k_state_init(float* __restrict__ kv, cons
         kv0 ? reinterpret_cast<const float4*>(kv0)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Backward-pass state set-up: a state (or its transpose) scaled by exp(power * s_h).
+__global__ __launch_bounds__(256) void k_state_prep(float* __restrict__ dst, const float* __restrict__ src,
+                                                    const float* __restrict__ slopes, int64_t bh, int64_t heads,
+                                                    int d, int transpose, int power)
+{
+    const int64_t d2 = (int64_t)d * d;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= bh * d2) return;
+    const int64_t u = idx / d2, e = idx % d2;
+    float x = 0.f;
+    if (src) {
+        const int64_t r = e / d, c = e % d;
+        x = src[u * d2 + (transpose ? c * d + r : e)];
+        if (power != 0) x *= exp2f(-(float)power * neg_slope_log2e(slopes, u % heads));
+    }
+    dst[idx] = x;
+}
+
 }  // namespace
+
+hipError_t launch_state_prep(float* dst, const float* src, const float* slopes, int64_t bh, int64_t heads,
+                             int d, bool transpose, int power, hipStream_t stream)
+{
+    const int64_t count = bh * (int64_t)d * d;
+    const dim3 grid((unsigned)((count + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_state_prep, grid, block, 0, stream, dst, src, slopes, bh, heads, d, transpose ? 1 : 0,
+                       power);
+    return hipGetLastError();
+}
 
 hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
                        int64_t n_chunks, int64_t chunk, int d, hipStream_t stream)

@@ -1,0 +1,90 @@
+"""GPU parity of la_backward (gradients through the prefill) against the oracle's reverse state
+recurrence (oracle.backward_recurrent, float64), element by element per (batch, head) with the
+bars of test_gpu_parity.py: dq, dk, dv stored in the input dtype (half an ulp of it allowed),
+dL/dKV_in in float32."""
+import numpy as np
+import pytest
+
+import long_context_la_amd as la
+import oracle
+import synth
+from common import assert_close, inputs, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, layout="bhnd"):
+    torch = _torch()
+    exact, raw = inputs(seed, B, H, N, d, dtype)
+    dout_raw = synth.generate(synth.V, seed + 500, d, nb=B, nh=H, nt=N, dtype=dtype)
+    dout_exact = synth.bf16_bits_to_f32(dout_raw) if dtype == "bf16" else dout_raw
+    if slopes is None:
+        slopes = np.array([2.0 ** (-2 - 3 * h) for h in range(H)], dtype=np.float32)
+    rng = np.random.default_rng(seed + 1)
+    kv_in = rng.standard_normal((B, H, d, d)).astype(np.float32) if states else None
+    dkv_out = rng.standard_normal((B, H, d, d)).astype(np.float32) if states else None
+
+    def dev(x):
+        t = to_device(x, dtype, device)
+        if layout == "bnhd":  # [B,N,H,d] storage viewed as [B,H,N,d]
+            t = t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        return t
+
+    q, k, v, do = (dev(x) for x in (*raw, dout_raw))
+    dq, dk, dv, dkv = la.la_backward(
+        q, k, v, do, torch.from_numpy(slopes).to(device),
+        kv_in=None if kv_in is None else torch.from_numpy(kv_in).to(device),
+        dkv_out=None if dkv_out is None else torch.from_numpy(dkv_out).to(device))
+    torch.cuda.synchronize()
+    want = oracle.backward_recurrent(*exact, dout_exact, slopes, kv_in=kv_in, dkv_out=dkv_out)
+    what = f"(B={B}, H={H}, N={N}, d={d}, {dtype}, states={states}, {layout})"
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want[:3]):
+        assert_close(to_host(got), ref, dtype, f"{name} {what}", stored=dtype)
+    assert_close(dkv.cpu().numpy(), want[3], dtype, f"dkv_in {what}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("states", [False, True])
+def test_backward_small(device, dtype, d, states):
+    run_backward(1, 2, 200, d, dtype, device, states=states)
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 129])
+def test_backward_tile_edges_bf16(device, n):
+    run_backward(2, 2, n, 128, "bf16", device, states=True, seed=80 + n)
+
+
+def test_backward_chunked_bf16(device):
+    # 2 heads x 4 value slices do not fill the GPU: every pass is cut into chunks, the two reverse
+    # walks combine their chunk summaries in reverse order
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 2, 5000, 128) < 5000
+    run_backward(1, 2, 5000, 128, "bf16", device, states=True, seed=90)
+
+
+def test_backward_chunked_f32(device):
+    run_backward(1, 1, 3000, 64, "f32", device, states=True, seed=91)
+
+
+def test_backward_strided_layout(device):
+    run_backward(2, 3, 150, 128, "bf16", device, states=True, seed=92, layout="bnhd")
+
+
+def test_backward_slow_and_fast_decay(device):
+    slopes = np.array([2.0 ** -8, 0.9], dtype=np.float32)
+    run_backward(1, 2, 700, 128, "bf16", device, states=True, seed=93, slopes=slopes)
+
+
+def test_backward_empty_sequence(device):
+    torch = _torch()
+    B, H, d = 1, 2, 128
+    q = torch.zeros(B, H, 0, d, dtype=torch.bfloat16, device=device)
+    g = torch.randn(B, H, d, d, device=device)
+    dq, dk, dv, dkv = la.la_backward(q, q, q, q, torch.full((H,), 0.1, device=device), dkv_out=g)
+    torch.cuda.synchronize()
+    assert dq.shape == q.shape and torch.equal(dkv, g)
