@@ -115,7 +115,7 @@ def make_prefill_inputs(w, device, head_group=8):
     return out
 
 
-def time_prefill(w, steps, warmup, device, with_backward=True):
+def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True):
     import torch
 
     import long_context_la_amd as la
@@ -156,7 +156,7 @@ def time_prefill(w, steps, warmup, device, with_backward=True):
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     n_chunks = -(-w.n // la.la_prefill_chunk_tokens(la.LA_BF16, w.batch, w.heads, w.n, w.d))
     varlen = None
-    if w.batch == 1 and sum(VARLEN_LENGTHS) == w.n:
+    if with_varlen and w.batch == 1 and sum(VARLEN_LENGTHS) == w.n:
         varlen = time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device)
     backward = time_backward(q, k, v, o, slopes, w, steps, warmup, device) if with_backward else None
     del q, k, v, o, ws
@@ -376,6 +376,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
@@ -396,7 +397,8 @@ def main():
     la.lib()
     w = synth.WORKLOADS[args.workload]
     ms, kernel_ms, n_chunks, varlen, backward = time_prefill(w, args.steps, args.warmup, device,
-                                                             with_backward=not args.no_backward)
+                                                             with_backward=not args.no_backward,
+                                                             with_varlen=not args.no_varlen)
     token_heads = w.batch * w.heads * w.n
     tokens_s = w.batch * w.n / (ms * 1e-3)
     flops = model_flops_per_token_head(w.d) * token_heads
