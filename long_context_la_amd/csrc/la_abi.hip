@@ -60,12 +60,17 @@ Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk
         if (c < kMinChunk) c = kMinChunk;
         chunk = c;
     }
+    p.sub = 1;
     if (chunk >= n) {
         p.chunk = n > 0 ? n : 1;
         p.n_chunks = 1;
     } else {
         p.chunk = chunk;
         p.n_chunks = (n + chunk - 1) / chunk;
+        const int64_t local_groups = units * (p.n_chunks - 1);
+        while (local_groups * p.sub < kLocalTargetGroups && p.chunk % (2 * p.sub * kBlock) == 0 &&
+               p.chunk / (2 * p.sub) >= kMinSubChunk)
+            p.sub *= 2;
     }
     return p;
 }
@@ -88,10 +93,12 @@ la_status check_shape(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int6
     return LA_OK;
 }
 
+// Prefix slots [B*H][n_chunks][d][d], then (with sub-chunks) summary slots [B*H][1 + n_sub][d][d].
 size_t workspace_bytes_for(const Plan& p, int64_t batch, int64_t heads, int64_t d)
 {
     if (p.n_chunks <= 1) return 0;
-    return (size_t)batch * (size_t)heads * (size_t)p.n_chunks * (size_t)d * (size_t)d * sizeof(float);
+    const int64_t slots = p.n_chunks + (p.sub > 1 ? 1 + (p.n_chunks - 1) * p.sub : 0);
+    return (size_t)batch * (size_t)heads * (size_t)slots * (size_t)d * (size_t)d * sizeof(float);
 }
 
 la_status check_fusion(const la_fusion* fu, const void* o)
@@ -177,10 +184,26 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
         return dt == LA_BF16 ? launch_fwd_bf16(b, mode, st) : launch_fwd_f32(b, (int)d, mode, st);
     };
 
-    if (p.n_chunks > 1) {
+    if (p.n_chunks > 1 && p.sub == 1) {
         s = launch_status(run(kModeLocal, p.n_chunks - 1), "chunk-summary launch");
         if (s != LA_OK) return s;
         s = launch_status(launch_scan(a.ws, kv, slopes, bh, heads, p.n_chunks, p.chunk, (int)d, st),
+                          "prefix-combine launch");
+        if (s != LA_OK) return s;
+    } else if (p.n_chunks > 1) {
+        // summaries per sub-chunk of every chunk but the last (all full length), into their own
+        // slots; the scan folds them into the chunk prefixes
+        const int64_t n_sub = (p.n_chunks - 1) * p.sub;
+        FwdArgs b = a;
+        b.ws = a.ws + bh * p.n_chunks * d * d;
+        b.chunk = p.chunk / p.sub;
+        b.n_chunks = n_sub + 1;  // the summary pass skips a sequence's last (sub-)chunk
+        b.chunks_launched = n_sub;
+        b.groups = bh * n_sub;
+        s = launch_status(dt == LA_BF16 ? launch_fwd_bf16(b, kModeLocal, st) : launch_fwd_f32(b, (int)d, kModeLocal, st),
+                          "chunk-summary launch");
+        if (s != LA_OK) return s;
+        s = launch_status(launch_scan_sub(a.ws, b.ws, kv, slopes, bh, heads, p.n_chunks, p.sub, b.chunk, (int)d, st),
                           "prefix-combine launch");
         if (s != LA_OK) return s;
     }

@@ -15,12 +15,22 @@ constexpr int kSliceW = 32;      // value columns per workgroup (value-dim slici
 constexpr int kTargetGroups = 256;  // workgroups that fill one MI355X (256 CUs, one resident each)
 constexpr int kMinChunk = 1024;  // shortest chunk worth a 64 KiB state exchange
 constexpr int kShortTokens = 8;  // packed sequences this short run token by token (no 64-token tile)
+#ifndef LA_LOCAL_TARGET_GROUPS
+#define LA_LOCAL_TARGET_GROUPS 256
+#endif
+// Chunk summaries are computed per sub-chunk (halving) until the summary pass has at least this
+// many workgroups.  The summary kernel runs four waves, so with one workgroup per CU each SIMD
+// holds a single latency-bound wave; two sub-chunks per chunk let most CUs hold two.  (Measured on
+// 8 heads: 1M tokens 4.82 -> 4.33 ms; more sub-chunks gain <= 2% there and cost up to 25% at 32K.)
+constexpr int kLocalTargetGroups = LA_LOCAL_TARGET_GROUPS;
+constexpr int kMinSubChunk = 256;  // shortest sub-chunk worth a 64 KiB summary
 
 // How a prefill is split: value-column slices x sequence chunks per (batch, head).
 struct Plan {
     int64_t chunk;     // tokens per chunk (multiple of kBlock unless a single chunk)
     int64_t n_chunks;  // >= 1
     int slices;        // d / kSliceW
+    int64_t sub;       // sub-chunks per chunk in the summary pass (power of two, chunk / sub a multiple of kBlock)
 };
 
 Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk_override);
@@ -126,6 +136,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream)
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream);
 hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
                        int64_t n_chunks, int64_t chunk, int d, hipStream_t stream);
+// Prefixes from sub-chunk summaries: pref[u][0] = kv[u]; pref[u][j] = the state after chunks
+// 0..j-1, folding sub[u][1 + (j-1)*n_sub_per + f] (sub-chunks of sub_len tokens) in order.
+hipError_t launch_scan_sub(float* pref, const float* sub, const float* kv, const float* slopes, int64_t bh,
+                           int64_t heads, int64_t n_chunks, int64_t n_sub_per, int64_t sub_len, int d,
+                           hipStream_t stream);
 hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
                               int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream);
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);

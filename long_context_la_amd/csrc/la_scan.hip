@@ -40,6 +40,38 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ ws, const floa
     }
 }
 
+// Chunk prefixes from sub-chunk summaries (the summary pass runs on sub-chunks to fill the GPU):
+// the recurrence P <- lambda^sub_len P + S runs over the sub-chunks in order and P is stored at
+// every chunk boundary.
+__global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, const float* __restrict__ sub,
+                                                  const float* __restrict__ kv, const float* __restrict__ slopes,
+                                                  int64_t bh, int64_t heads, int64_t n_chunks, int64_t n_sub_per,
+                                                  int64_t sub_len, int d2)
+{
+    const int64_t per = d2 / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= bh * per) return;
+    const int64_t u = idx / per;
+    const int64_t e = idx % per;
+    const float nsl = neg_slope_log2e(slopes, u % heads);
+    const float ls = decay_pow(nsl, (float)sub_len);
+    const int64_t n_sub = (n_chunks - 1) * n_sub_per;
+    const float4* S = reinterpret_cast<const float4*>(sub + u * (n_sub + 1) * (int64_t)d2) + e;
+    float4* P = reinterpret_cast<float4*>(pref + u * n_chunks * (int64_t)d2) + e;
+    float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
+    P[0] = p;
+    for (int64_t j = 1; j < n_chunks; ++j) {
+        for (int64_t f = 0; f < n_sub_per; ++f) {
+            const float4 s = S[((j - 1) * n_sub_per + f + 1) * per];
+            p.x = ls * p.x + s.x;
+            p.y = ls * p.y + s.y;
+            p.z = ls * p.z + s.z;
+            p.w = ls * p.w + s.w;
+        }
+        P[j * per] = p;
+    }
+}
+
 // Packed variable-length batches: the chunks of sequence s are global chunks c0..c0+nc-1 (stab)
 // and slot (c, h) = c*heads + h; slot (c0+j+1, h) holds the local state of chunk j.
 __global__ __launch_bounds__(256) void k_scan_varlen(float* __restrict__ ws, const float* __restrict__ kv,
@@ -117,6 +149,18 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
     const int64_t threads = bh * (d2 / 4);
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     hipLaunchKernelGGL(k_scan, grid, block, 0, stream, ws, kv, slopes, bh, heads, n_chunks, chunk, d2);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_sub(float* pref, const float* sub, const float* kv, const float* slopes, int64_t bh,
+                           int64_t heads, int64_t n_chunks, int64_t n_sub_per, int64_t sub_len, int d,
+                           hipStream_t stream)
+{
+    const int d2 = d * d;
+    const int64_t threads = bh * (d2 / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    hipLaunchKernelGGL(k_scan_sub, grid, block, 0, stream, pref, sub, kv, slopes, bh, heads, n_chunks, n_sub_per,
+                       sub_len, d2);
     return hipGetLastError();
 }
 
