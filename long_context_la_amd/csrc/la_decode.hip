@@ -33,12 +33,14 @@ struct Fu {
     float eps;
 };
 
-template <typename T, int D>
+// FUSED compiles the prologue/epilogue in; the plain step carries none of it.
+template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(256) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
                                                 const T* __restrict__ v, T* __restrict__ o,
                                                 const float* __restrict__ slopes,
                                                 float* __restrict__ kv, int64_t heads, Fu fu)
 {
+    const uint32_t flags = FUSED ? fu.flags : 0u;
     constexpr int CG = D / 4;       // float4 column groups per row
     constexpr int RG = 256 / CG;    // row groups
     constexpr int RPT = D / RG;     // rows per thread
@@ -59,12 +61,12 @@ __global__ __launch_bounds__(256) void k_decode(const T* __restrict__ q, const T
 
     if (tid < D) {
         const float xq = to_f32(q[u * D + tid]), xk = to_f32(k[u * D + tid]);
-        sq[tid] = (fu.flags & LA_SILU_Q) ? act_round<T>(silu_f32(xq)) : xq;
-        sk[tid] = (fu.flags & LA_SILU_K) ? act_round<T>(silu_f32(xk)) : xk;
+        sq[tid] = (flags & LA_SILU_Q) ? act_round<T>(silu_f32(xq)) : xq;
+        sk[tid] = (flags & LA_SILU_K) ? act_round<T>(silu_f32(xk)) : xk;
     }
     const T* vu = v + u * D + 4 * cg;
     f32x4 vv = {to_f32(vu[0]), to_f32(vu[1]), to_f32(vu[2]), to_f32(vu[3])};
-    if (fu.flags & LA_SILU_V)
+    if (flags & LA_SILU_V)
         vv = f32x4{act_round<T>(silu_f32(vv[0])), act_round<T>(silu_f32(vv[1])), act_round<T>(silu_f32(vv[2])),
                    act_round<T>(silu_f32(vv[3]))};
     const float lam = (float)exp(-(double)slopes[u % heads]);
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void k_decode(const T* __restrict__ q, const T
     if (tid < CG) {
         f32x4 r = red[0][tid];
         for (int g = 1; g < RG; ++g) r += red[g][tid];
-        if (fu.flags & LA_NORM) {
+        if (flags & LA_NORM) {
             // mean square over the d features: the CG threads of this row are lanes 0..CG-1
             float ss = r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
 #pragma unroll
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void k_decode(const T* __restrict__ q, const T
             const f32x4 wv = fu.weight ? reinterpret_cast<const f32x4*>(fu.weight)[tid] : f32x4{1.f, 1.f, 1.f, 1.f};
             r = r * sc * wv;
         }
-        if (fu.flags & LA_GATE) {
+        if (flags & LA_GATE) {
             const T* gu = static_cast<const T*>(fu.gate) + u * D + 4 * tid;
             r = r * f32x4{sigmoid_f32(to_f32(gu[0])), sigmoid_f32(to_f32(gu[1])), sigmoid_f32(to_f32(gu[2])),
                           sigmoid_f32(to_f32(gu[3]))};
@@ -257,6 +259,17 @@ hipError_t launch_norm_gate(la_dtype dt, void* o, const void* gate, const float*
     return hipGetLastError();
 }
 
+template <typename T>
+void launch_decode_t(const T* q, const T* k, const T* v, T* o, int64_t bh, int64_t heads, int d, const float* slopes,
+                     float* kv, Fu fu, dim3 grid, dim3 block, hipStream_t stream)
+{
+    (void)bh;
+    if (fu.flags && d == 128) hipLaunchKernelGGL((k_decode<T, 128, true>), grid, block, 0, stream, q, k, v, o, slopes, kv, heads, fu);
+    else if (fu.flags) hipLaunchKernelGGL((k_decode<T, 64, true>), grid, block, 0, stream, q, k, v, o, slopes, kv, heads, fu);
+    else if (d == 128) hipLaunchKernelGGL((k_decode<T, 128, false>), grid, block, 0, stream, q, k, v, o, slopes, kv, heads, fu);
+    else hipLaunchKernelGGL((k_decode<T, 64, false>), grid, block, 0, stream, q, k, v, o, slopes, kv, heads, fu);
+}
+
 hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                          int64_t bh, int64_t heads, int d, const float* slopes, float* kv,
                          const la_fusion* fusion, hipStream_t stream)
@@ -264,19 +277,14 @@ hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* 
     const dim3 grid((unsigned)bh), block(256);
     Fu fu{0u, nullptr, nullptr, 0.f};
     if (fusion) fu = Fu{fusion->flags, fusion->gate, fusion->norm_weight, fusion->norm_eps};
-    if (dt == LA_BF16) {
-        auto qq = static_cast<const __bf16*>(q), kk = static_cast<const __bf16*>(k),
-             vv = static_cast<const __bf16*>(v);
-        auto oo = static_cast<__bf16*>(o);
-        if (d == 128) hipLaunchKernelGGL((k_decode<__bf16, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, fu);
-        else hipLaunchKernelGGL((k_decode<__bf16, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, fu);
-    } else {
-        auto qq = static_cast<const float*>(q), kk = static_cast<const float*>(k),
-             vv = static_cast<const float*>(v);
-        auto oo = static_cast<float*>(o);
-        if (d == 128) hipLaunchKernelGGL((k_decode<float, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, fu);
-        else hipLaunchKernelGGL((k_decode<float, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, fu);
-    }
+    if (dt == LA_BF16)
+        launch_decode_t<__bf16>(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                                static_cast<const __bf16*>(v), static_cast<__bf16*>(o), bh, heads, d, slopes, kv, fu,
+                                grid, block, stream);
+    else
+        launch_decode_t<float>(static_cast<const float*>(q), static_cast<const float*>(k),
+                               static_cast<const float*>(v), static_cast<float*>(o), bh, heads, d, slopes, kv, fu,
+                               grid, block, stream);
     return hipGetLastError();
 }
 

@@ -177,8 +177,10 @@ struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, feat
 struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
 
 // REV walks each sequence from its last token to its first (token index t of the recurrence is
-// memory row n-1-t), the order of the reverse state recurrence of the backward pass.
-template <int MODE, bool GATE, bool REV>
+// memory row n-1-t), the order of the reverse state recurrence of the backward pass.  ACT enables
+// the SiLU prologue (which of q, k, v is chosen at run time); without it no activation code is
+// compiled in, since untaken branches inside the tile loops still cost about 10% here.
+template <int MODE, bool GATE, bool REV, bool ACT>
 __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
     static_assert(!(GATE && REV), "the reverse walk has no epilogue");
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const u16* Vg = static_cast<const u16*>(a.v) + base + slice * SW;
     u16* Og = OUT ? static_cast<u16*>(a.o) + base + slice * SW : nullptr;
     const u16* Gg = GATE ? static_cast<const u16*>(a.gate) + base + slice * SW : nullptr;
-    const bool silu_q = a.act & LA_SILU_Q, silu_k = a.act & LA_SILU_K, silu_v = a.act & LA_SILU_V;
+    const bool silu_q = ACT && (a.act & LA_SILU_Q), silu_k = ACT && (a.act & LA_SILU_K),
+               silu_v = ACT && (a.act & LA_SILU_V);
     const int64_t sn = a.sn;
     const uint32_t row_bytes = (uint32_t)(sn * 2);
     // transposing-read address pieces: row k0 + lr/4, column c0 + 4*(lr%4)
@@ -562,19 +565,25 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     }
 }
 
+template <bool GATE, bool REV, bool ACT>
+void launch_mode(const FwdArgs& a, int mode, dim3 grid, hipStream_t stream)
+{
+    if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT>), grid, dim3(256), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
-    if (a.rev) {  // the backward pass: no epilogue, no checkpoints, fixed-length batches
-        if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, true>), grid, dim3(512), 0, stream, a);
-        else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, true>), grid, dim3(256), 0, stream, a);
-    } else if (mode == kModeOut && a.gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true, false>), grid, dim3(512), 0, stream, a);
-    else if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, false>), grid, dim3(512), 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, false>), grid, dim3(256), 0, stream, a);
+    const bool gate = a.gate && mode == kModeOut, act = a.act != 0;
+    if (a.rev) launch_mode<false, true, false>(a, mode, grid, stream);  // the backward pass: plain inputs
+    else if (gate && act) launch_mode<true, false, true>(a, mode, grid, stream);
+    else if (gate) launch_mode<true, false, false>(a, mode, grid, stream);
+    else if (act) launch_mode<false, false, true>(a, mode, grid, stream);
+    else launch_mode<false, false, false>(a, mode, grid, stream);
     return hipGetLastError();
 }
 
