@@ -7,6 +7,8 @@
 * decode (128 sequences x 64 heads, 4096-token prefix then decode steps): sampled (seq, head).
 * varlen (the full layer's tokens cut into 18 packed sequences of 65536, 32768, ..., 1, 1 tokens,
   as the benchmark times them): every final state and sampled output windows of every sequence.
+* backward of the full layer: dq on forward windows, dk and dv on reverse windows (G_t depends on
+  the next W tokens), dL/dKV_in on the first W tokens.
 
 Windows use the oracle's windowing pin: for slopes s >= 2^-8 the state is fixed by the last
 W = 8192 tokens up to lambda^W <= e^-32 (relative), far below the bars, so a window's outputs are
@@ -228,3 +230,44 @@ def test_varlen_packed_full_layer(device):
         got = to_host(o[0:1, h:h + 1, end - n:end])
         assert_close(got, o_ref[None, None, 64 - n:], "bf16", f"varlen O head {h} tokens ..{end}", stored="bf16")
 
+
+
+def test_backward_full_layer_windows(device):
+    """la_backward on the full layer as the benchmark times it (64 heads x 131072 tokens, bf16,
+    dL/dO from the generator).  dq at token t depends on the forward state (the last W tokens), dk
+    and dv on G_t (the next W tokens), dL/dKV_in on G_0 (the first W tokens), so each is checked
+    on windows: forward windows for dq, reverse windows for dk and dv."""
+    torch = _torch()
+    w = synth.WORKLOADS["full"]
+    slopes = w.slopes()
+    q, k, v = upload(w, device)
+    seed_do = w.seed + 1000
+    do = torch.empty_like(q)
+    for h0 in range(0, w.heads, 8):
+        bits = synth.generate(synth.V, seed_do, w.d, h0=h0, nh=8, nt=w.n, dtype="bf16")
+        do[:, h0:h0 + 8] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+    dq, dk, dv, dkv = la.la_backward(q, k, v, do, torch.from_numpy(slopes).to(device))
+    torch.cuda.synchronize()
+    del q, k, v, do
+
+    def inputs_of(h, t0, nt):
+        x = exact(w, 0, h, t0, nt)
+        g = synth.bf16_bits_to_f32(synth.generate(synth.V, seed_do, w.d, h0=h, nh=1, t0=t0, nt=nt, dtype="bf16"))
+        return x + [g]
+
+    length = 128
+    sl = lambda h: np.array([slopes[h]])
+    for h in (0, 31, 63):
+        for end in (length, 70000, w.n):
+            start = max(0, end - length - WINDOW)
+            ref = oracle.backward_recurrent(*inputs_of(h, start, end - start), sl(h))
+            got = to_host(dq[0:1, h:h + 1, end - length:end])
+            assert_close(got, ref[0][:, :, -length:], "bf16", f"full dq head {h} tokens ..{end}", stored="bf16")
+        for begin in (0, 70000, w.n - length):
+            stop = min(w.n, begin + length + WINDOW)
+            ref = oracle.backward_recurrent(*inputs_of(h, begin, stop - begin), sl(h))
+            for name, t, r in (("dk", dk, ref[1]), ("dv", dv, ref[2])):
+                got = to_host(t[0:1, h:h + 1, begin:begin + length])
+                assert_close(got, r[:, :, :length], "bf16", f"full {name} head {h} tokens {begin}..", stored="bf16")
+            if begin == 0:
+                assert_close(dkv[0:1, h:h + 1].cpu().numpy(), ref[3], "bf16", f"full dKV_in head {h}")
