@@ -67,7 +67,7 @@ Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk
     } else {
         p.chunk = chunk;
         p.n_chunks = (n + chunk - 1) / chunk;
-        const int64_t local_groups = units * (p.n_chunks - 1);
+        const int64_t local_groups = batch * heads * (p.n_chunks - 1);  // full-width summary workgroups
         while (local_groups * p.sub < kLocalTargetGroups && p.chunk % (2 * p.sub * kBlock) == 0 &&
                p.chunk / (2 * p.sub) >= kMinSubChunk)
             p.sub *= 2;
@@ -184,8 +184,15 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
         return dt == LA_BF16 ? launch_fwd_bf16(b, mode, st) : launch_fwd_f32(b, (int)d, mode, st);
     };
 
+    // chunk summaries: full width (one workgroup per chunk-head) for plain bf16, else the sliced
+    // tile kernel in its summary mode
+    const bool full_width = dt == LA_BF16 && a.act == 0;
     if (p.n_chunks > 1 && p.sub == 1) {
-        s = launch_status(run(kModeLocal, p.n_chunks - 1), "chunk-summary launch");
+        FwdArgs b = a;
+        b.chunks_launched = p.n_chunks - 1;
+        b.groups = bh * (p.n_chunks - 1);
+        s = launch_status(full_width ? launch_summary_bf16(b, st) : run(kModeLocal, p.n_chunks - 1),
+                          "chunk-summary launch");
         if (s != LA_OK) return s;
         s = launch_status(launch_scan(a.ws, kv, slopes, bh, heads, p.n_chunks, p.chunk, (int)d, st),
                           "prefix-combine launch");
@@ -200,7 +207,9 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
         b.n_chunks = n_sub + 1;  // the summary pass skips a sequence's last (sub-)chunk
         b.chunks_launched = n_sub;
         b.groups = bh * n_sub;
-        s = launch_status(dt == LA_BF16 ? launch_fwd_bf16(b, kModeLocal, st) : launch_fwd_f32(b, (int)d, kModeLocal, st),
+        s = launch_status(full_width ? launch_summary_bf16(b, st)
+                                     : dt == LA_BF16 ? launch_fwd_bf16(b, kModeLocal, st)
+                                                     : launch_fwd_f32(b, (int)d, kModeLocal, st),
                           "chunk-summary launch");
         if (s != LA_OK) return s;
         s = launch_status(launch_scan_sub(a.ws, b.ws, kv, slopes, bh, heads, p.n_chunks, p.sub, b.chunk, (int)d, st),

@@ -16,12 +16,12 @@ constexpr int kTargetGroups = 256;  // workgroups that fill one MI355X (256 CUs,
 constexpr int kMinChunk = 1024;  // shortest chunk worth a 64 KiB state exchange
 constexpr int kShortTokens = 8;  // packed sequences this short run token by token (no 64-token tile)
 #ifndef LA_LOCAL_TARGET_GROUPS
-#define LA_LOCAL_TARGET_GROUPS 256
+#define LA_LOCAL_TARGET_GROUPS 128
 #endif
 // Chunk summaries are computed per sub-chunk (halving) until the summary pass has at least this
-// many workgroups.  The summary kernel runs four waves, so with one workgroup per CU each SIMD
-// holds a single latency-bound wave; two sub-chunks per chunk let most CUs hold two.  (Measured on
-// 8 heads: 1M tokens 4.82 -> 4.33 ms; more sub-chunks gain <= 2% there and cost up to 25% at 32K.)
+// many full-width workgroups (one per chunk-head; the sliced summaries of the fused path get four
+// times as many).  Measured on 8 heads: 128 and 256 tie at 1M tokens, and 128 is 7% faster at 32K
+// (fewer summary slots to fold); 512 and above are slower at both.
 constexpr int kLocalTargetGroups = LA_LOCAL_TARGET_GROUPS;
 constexpr int kMinSubChunk = 256;  // shortest sub-chunk worth a 64 KiB summary
 
@@ -134,6 +134,9 @@ __device__ inline Work decode_work(const FwdArgs& a, int64_t group)
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream);
+// Chunk summaries (kModeLocal semantics) at full width, one workgroup per group of `a` (no value
+// slices); bf16 without the SiLU prologue.
+hipError_t launch_summary_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
                        int64_t n_chunks, int64_t chunk, int d, hipStream_t stream);
 // Prefixes from sub-chunk summaries: pref[u][0] = kv[u]; pref[u][j] = the state after chunks

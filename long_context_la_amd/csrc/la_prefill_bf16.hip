@@ -565,6 +565,154 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     }
 }
 
+// ------------------------------------------------------------------ chunk summaries at full width
+// Page "MiniMax-01: Scaling Foundation Models with Lightning Attention | Summary", section 3.2
+// (LASP+): each partition's local summary S = sum_t lambda^(C-1-t) k_t^T v_t, from a zero state.
+// The tile kernel above slices the value columns over four workgroups, which suits the outputs,
+// but for a summary alone it makes each slice re-read all of K.  Here one workgroup owns a whole
+// (sequence, head, sub-chunk) and its full d x d state: K and V are read once.  Per 64-token tile
+// the state is decayed by lambda^L and K^T (W V) is added, with W V staged as bf16 hi + lo as in
+// the tile kernel.  Eight waves split the 8 x 8 state tiles of 16 x 16 as 2 key-row halves x 4
+// value-column quarters.  No SiLU prologue (the fused path keeps the sliced summaries).
+struct SumRegs { uint4 k[2]; uint4 v[2]; };  // 16-byte chunks tid and tid + 512 of the K and V tiles
+
+template <bool REV>
+__global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
+    __shared__ __attribute__((aligned(16))) u16 sWh[2][BK * KS];
+    __shared__ __attribute__((aligned(16))) u16 sWl[2][BK * KS];
+
+    const int64_t group = blockIdx.x;
+    if (group >= a.groups) return;
+    const Work wk = decode_work(a, group);
+    if (wk.j == wk.nck - 1) return;  // a sequence's last (sub-)chunk needs no summary
+    const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
+    const int n_tiles = (int)((t_end - t_begin + BK - 1) / BK);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, lr = l & 15, g = l >> 4;
+    const int it0 = 4 * (w >> 2), jt0 = 2 * (w & 3);  // this wave's state tiles: key rows 16(it0..it0+3), value cols 16(jt0..jt0+1)
+    const int tr_row = lr >> 2, tr_col = 4 * (lr & 3);
+    const float nsl = neg_slope_log2e(a.slopes, wk.h);
+    const u16* Kg = static_cast<const u16*>(a.k) + wk.base;
+    const u16* Vg = static_cast<const u16*>(a.v) + wk.base;
+    const int64_t sn = a.sn;
+    const uint32_t row_bytes = (uint32_t)(sn * 2);
+
+    auto tile_len = [&](int tile) __attribute__((always_inline)) {
+        const int64_t t0 = t_begin + (int64_t)tile * BK;
+        return (int)((t_end - t0 < BK) ? t_end - t0 : BK);
+    };
+    auto tile_bytes = [&](int tile) __attribute__((always_inline)) {
+        const int L = tile_len(tile);
+        return (int64_t)(L > 0 ? L : 0) * row_bytes;
+    };
+    // memory row of the tile's first byte and byte offset of its row r (reverse walk: row r is
+    // memory row L-1-r of the span; rows past the span fall outside the buffer and read zero)
+    auto tile_row0 = [&](int tile) __attribute__((always_inline)) {
+        const int64_t t0 = t_begin + (int64_t)tile * BK;
+        if constexpr (!REV) return t0;
+        const int L = tile_len(tile);
+        const int64_t r0 = a.n - t0 - (L > 0 ? L : 0);
+        return r0 > 0 ? r0 : (int64_t)0;
+    };
+    auto row_off = [&](int tile, int r) __attribute__((always_inline)) {
+        if constexpr (!REV) return (uint32_t)r * row_bytes;
+        return (uint32_t)(tile_len(tile) - 1 - r) * row_bytes;
+    };
+    auto load = [&](SumRegs& R, int tile) __attribute__((always_inline)) {
+        const int64_t t0 = tile_row0(tile);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, tile_bytes(tile));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, tile_bytes(tile));
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tid + 512 * m;
+            R.k[m] = buf_load16(rk, row_off(tile, c >> 4) + 16u * (c & 15));
+            R.v[m] = buf_load16(rv, row_off(tile, c >> 4) + 16u * (c & 15));
+        }
+    };
+    auto stage = [&](const SumRegs& R, int buf, int tile) __attribute__((always_inline)) {
+        const int L = tile_len(tile);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tid + 512 * m, r = c >> 4, off = r * KS + 8 * (c & 15);
+            *reinterpret_cast<uint4*>(&sK[buf][off]) = R.k[m];
+            const float wt = (r < L) ? decay_pow(nsl, (float)(L - 1 - r)) : 0.f;
+            const uint32_t in[4] = {R.v[m].x, R.v[m].y, R.v[m].z, R.v[m].w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
+            *reinterpret_cast<uint4*>(&sWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4*>(&sWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+    };
+    f32x4 st[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // S <- lambda^L S + K^T (W V) on this wave's 4 x 2 state tiles (k = token within the tile)
+    auto update = [&](int buf, int tile) __attribute__((always_inline)) {
+        const float dl = decay_pow(nsl, (float)tile_len(tile));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) st[k] *= dl;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int k0 = 32 * ks + 8 * g;
+            bf16x8 ka[4], vh[2], vl[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (k0 + tr_row) * KS + 16 * (it0 + i) + tr_col;
+                ka[i] = join(lds_tr(&sK[buf][o]), lds_tr(&sK[buf][o + 4 * KS]));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int o = (k0 + tr_row) * KS + 16 * (jt0 + j) + tr_col;
+                vh[j] = join(lds_tr(&sWh[buf][o]), lds_tr(&sWh[buf][o + 4 * KS]));
+                vl[j] = join(lds_tr(&sWl[buf][o]), lds_tr(&sWl[buf][o + 4 * KS]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    st[2 * i + j] = mfma(ka[i], vh[j], st[2 * i + j]);
+                    st[2 * i + j] = mfma(ka[i], vl[j], st[2 * i + j]);
+                }
+        }
+    };
+    SumRegs RA, RB;
+    load(RA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(RB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(RA, 0, 0);
+    __syncthreads();
+    auto step = [&](SumRegs& R, SumRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(R, tile + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        update(buf, tile);
+        if (tile + 1 < n_tiles) stage(Rn, buf ^ 1, tile + 1);
+    };
+    int tile = 0;
+    for (; tile + 2 <= n_tiles; tile += 2) {
+        step(RA, RB, 0, tile);
+        __syncthreads();
+        step(RB, RA, 1, tile + 1);
+        __syncthreads();
+    }
+    if (tile < n_tiles) step(RA, RB, 0, tile);
+    // C layout: lane (g, lr) holds rows 4g..4g+3 (key) of column lr (value) of each tile
+    float* dst = a.ws + wk.slot_out * (int64_t)(D * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                dst[(16 * (it0 + i) + 4 * g + t) * D + 16 * (jt0 + j) + lr] = st[2 * i + j][t];
+}
+
 template <bool GATE, bool REV, bool ACT>
 void launch_mode(const FwdArgs& a, int mode, dim3 grid, hipStream_t stream)
 {
@@ -584,6 +732,14 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream)
     else if (gate) launch_mode<true, false, false>(a, mode, grid, stream);
     else if (act) launch_mode<false, false, true>(a, mode, grid, stream);
     else launch_mode<false, false, false>(a, mode, grid, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_summary_bf16(const FwdArgs& a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)a.groups), block(512);
+    if (a.rev) hipLaunchKernelGGL((k_summary_bf16<true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_summary_bf16<false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

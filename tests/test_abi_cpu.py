@@ -93,12 +93,12 @@ def test_plan_and_workspace_sizes():
     # 8 heads: 8 chunks per sequence
     c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 32768, 128)
     assert c == 4096
-    # prefix slots (8 per head) + summary slots: 7 chunks x 2 sub-chunks + 1, so that the summary
-    # pass has 32 x 14 = 448 >= 256 workgroups
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * (8 + 1 + 7 * 2) * 128 * 128 * 4
+    # prefix slots (8 per head) + summary slots: 7 chunks x 4 sub-chunks + 1, so that the summary
+    # pass has 8 x 28 = 224 >= 128 full-width workgroups
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * (8 + 1 + 7 * 4) * 128 * 128 * 4
     c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 1048576, 128)
     assert c == 131072
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (8 + 1 + 7 * 2) * 128 * 128 * 4
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (8 + 1 + 7 * 4) * 128 * 128 * 4
     # sub-chunks stay >= 256 tokens and multiples of 64: a 1024-token chunk splits at most 4 ways
     assert la.la_prefill_workspace_size(la.LA_BF16, 1, 1, 4096, 128, chunk_tokens=1024) == (4 + 1 + 3 * 4) * 128 * 128 * 4
     # short sequences are not chunked
