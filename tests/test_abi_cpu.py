@@ -168,3 +168,57 @@ def test_varlen_validation_codes():
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
 def test_varlen_no_device_is_reported_not_fatal():
     assert _varlen([10, 20]) == la.LA_ERR_DEVICE
+
+
+def _fusion(flags, gate=None, weight=None, eps=0.0):
+    return la.la_fusion(flags, None if gate is None else gate.value, None if weight is None else weight.value, eps)
+
+
+def test_fused_validation_codes():
+    L = la.lib()
+
+    def prefill(fu, o=FAKE):
+        return L.la_prefill_fused(la.LA_BF16, FAKE, FAKE, FAKE, o, 1, 8, 4096, 128, 8 * 4096 * 128, 4096 * 128, 128,
+                                  FAKE, FAKE, ctypes.byref(fu), FAKE, 1 << 30, None)
+
+    def decode(fu, o=FAKE):
+        return L.la_decode_fused(la.LA_BF16, FAKE, FAKE, FAKE, o, 2, 2, 128, FAKE, FAKE, ctypes.byref(fu), None)
+
+    for call in (prefill, decode):
+        assert call(_fusion(1 << 10)) == la.LA_ERR_INVALID_ARGUMENT                      # unknown flag
+        assert call(_fusion(la.LA_GATE)) == la.LA_ERR_INVALID_ARGUMENT                   # gate tensor missing
+        assert call(_fusion(la.LA_GATE, gate=ctypes.c_void_p((1 << 20) + 4))) == la.LA_ERR_INVALID_ARGUMENT
+        assert call(_fusion(la.LA_NORM, eps=0.0)) == la.LA_ERR_INVALID_ARGUMENT          # eps must be > 0
+        assert call(_fusion(la.LA_NORM, weight=ctypes.c_void_p((1 << 20) + 4), eps=1e-5)) == la.LA_ERR_INVALID_ARGUMENT
+        assert call(_fusion(la.LA_NORM, eps=1e-5), o=None) == la.LA_ERR_INVALID_ARGUMENT  # the epilogue needs o
+    # SiLU alone without an output is a state-only prefill: valid
+    if not gpu_available():
+        assert prefill(_fusion(la.LA_SILU_K | la.LA_SILU_V), o=None) == la.LA_ERR_DEVICE
+
+
+def _backward(**kw):
+    a = dict(dt=la.LA_BF16, q=FAKE, k=FAKE, v=FAKE, do=FAKE, B=1, H=8, N=4096, d=128, sb=8 * 4096 * 128,
+             sh=4096 * 128, sn=128, slopes=FAKE, kv_in=None, dkv_out=None, dq=FAKE, dk=FAKE, dv=FAKE, dkv_in=None,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return la.lib().la_backward(a["dt"], a["q"], a["k"], a["v"], a["do"], a["B"], a["H"], a["N"], a["d"], a["sb"],
+                                a["sh"], a["sn"], a["slopes"], a["kv_in"], a["dkv_out"], a["dq"], a["dk"], a["dv"],
+                                a["dkv_in"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_validation_codes():
+    # the workspace holds one state per (batch, head) plus the prefill's chunk workspace
+    need = la.la_backward_workspace_size(la.LA_BF16, 1, 8, 4096, 128)
+    assert need == 8 * 128 * 128 * 4 + la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 4096, 128)
+    assert la.la_backward_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 64 * 128 * 128 * 4
+    assert la.la_backward_workspace_size(la.LA_BF16, 1, 8, 100, 96) == 0                 # invalid shape
+    assert _backward(do=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _backward(dk=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _backward(slopes=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert _backward(d=64, sn=64) == la.LA_ERR_UNSUPPORTED                                 # bf16 needs d = 128
+    assert _backward(dkv_out=ctypes.c_void_p((1 << 20) + 4)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned state
+    assert _backward(ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
+    assert _backward(ws_bytes=need - 16) == la.LA_ERR_WORKSPACE
+    if not gpu_available():
+        assert _backward(ws_bytes=need) == la.LA_ERR_DEVICE
+        assert _backward(N=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) == la.LA_ERR_DEVICE
