@@ -299,6 +299,45 @@ def time_mixed(device, heads=64, d=128, iters=200):
     return res
 
 
+def time_decode_small(device, heads=64, d=128, steps=64, reps=20):
+    """One sequence x 64 heads: a launch-bound decode.  Eager calls versus the same 64 steps
+    captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed."""
+    import torch
+
+    import long_context_la_amd as la
+
+    gen = torch.Generator(device="cpu").manual_seed(61)
+    q, k, v = (torch.randn(steps, 1, heads, d, generator=gen).to(torch.bfloat16).to(device) for _ in range(3))
+    slopes = torch.from_numpy(np.exp2(-(np.arange(heads) + 1) / 8.0).astype(np.float32)).to(device)
+    kv = torch.zeros(1, heads, d, d, dtype=torch.float32, device=device)
+    o = torch.empty(steps, 1, heads, d, dtype=torch.bfloat16, device=device)
+
+    def run():
+        for t in range(steps):
+            la.la_decode(q[t], k[t], v[t], slopes, kv, o[t])
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / (reps * steps) * 1e6
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / (reps * steps) * 1e6
+    log(f"small decode (1 x {heads} heads): eager {eager:.1f} us/step, graph {graph:.1f} us/step")
+    return {"workload": f"1 seq x {heads} heads, d={d}, bf16; {steps} steps per graph", "us_per_step_eager": eager,
+            "us_per_step_graph": graph}
+
+
 def time_decode(w, steps, device, prefix_slab=16):
     import torch
 
@@ -432,6 +471,7 @@ def main():
         result["backward"] = backward
     if not args.no_decode:
         result["mixed_batch"] = time_mixed(device)
+        result["decode_small_batch"] = time_decode_small(device)
         wd = synth.WORKLOADS["decode"]
         us = time_decode(wd, args.decode_steps, device)
         gbs = wd.batch * wd.heads * DECODE_BYTES_PER_UNIT / (us * 1e-6) / 1e9
