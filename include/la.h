@@ -31,6 +31,12 @@
  *   - The KV state is always float32, [batch][heads][d][d], row i = key dim.
  *   - Results are deterministic: the same inputs on the same device give the
  *     same bits (no floating-point atomics).
+ *   - HIP graphs: la_state_init, la_prefill(_ex, _fused), la_decode(_fused)
+ *     and la_backward enqueue kernels only (no allocation, memset or host
+ *     copy), so a sequence of them can be captured into a graph and replayed;
+ *     the replay reads the tensors at the captured addresses.
+ *     la_prefill_varlen enqueues a host-to-device copy of its chunk tables
+ *     from a temporary host buffer and must not be captured.
  */
 #ifndef LIGHTNING_LA_H
 #define LIGHTNING_LA_H
