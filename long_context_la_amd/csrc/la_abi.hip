@@ -19,11 +19,6 @@ la_status fail(la_status s, const std::string& msg)
     return s;
 }
 
-la_status ok()
-{
-    return LA_OK;
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 la_status device_check()

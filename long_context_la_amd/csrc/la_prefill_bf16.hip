@@ -87,7 +87,6 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9-family raw buffer descript
 
 __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 __device__ __forceinline__ float hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t f32_to_bits(float f) { return (uint32_t)__builtin_bit_cast(u16, (__bf16)f); }
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Element offset of (row, col) in a state copy: unpadded 256-byte rows whose 16-byte chunks are
