@@ -88,3 +88,22 @@ def test_backward_empty_sequence(device):
     dq, dk, dv, dkv = la.la_backward(q, q, q, q, torch.full((H,), 0.1, device=device), dkv_out=g)
     torch.cuda.synchronize()
     assert dq.shape == q.shape and torch.equal(dkv, g)
+
+
+def test_backward_chunked_batch(device):
+    # batch of two, chunked: the reverse walks' summaries run per (sequence, head, sub-chunk)
+    run_backward(2, 2, 3000, 128, "bf16", device, states=True, seed=94)
+
+
+def test_backward_is_deterministic(device):
+    torch = _torch()
+    exact, raw = inputs(95, 1, 2, 2000, 128, "bf16")
+    q, k, v = (to_device(x, "bf16", device) for x in raw)
+    do = torch.randn_like(q.float()).to(torch.bfloat16)
+    slopes = torch.tensor([0.25, 0.01], device=device)
+    g = torch.randn(1, 2, 128, 128, device=device)
+    a = la.la_backward(q, k, v, do, slopes, dkv_out=g)
+    b = la.la_backward(q, k, v, do, slopes, dkv_out=g)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -221,3 +221,11 @@ def test_n_zero_is_noop(device):
     la.la_prefill(q, q, q, torch.zeros(2, device=device), kv, o=torch.empty_like(q))
     torch.cuda.synchronize()
     assert torch.equal(kv, before)
+
+
+def test_bf16_chunked_batch_with_states(device):
+    # two sequences of the batch, both cut into chunks and sub-chunk summaries (full-width
+    # summary kernel), each from its own incoming state
+    kv0 = np.random.default_rng(9).standard_normal((2, 2, 128, 128)).astype(np.float32)
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 2, 2, 5000, 128) < 5000
+    check_prefill(28, 2, 2, 5000, 128, "bf16", SL2, device, kv_in=kv0)
