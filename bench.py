@@ -130,10 +130,13 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True)
     ws_bytes = la.la_prefill_workspace_size(la.LA_BF16, w.batch, w.heads, w.n, w.d)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream(device)
+    # the long-context workload keeps a state checkpoint every ckpt_every tokens
+    ck = (torch.empty(w.batch, w.heads, w.n // w.ckpt_every, w.d, w.d, dtype=torch.float32, device=device)
+          if w.ckpt_every else None)
 
     def step():
         la.la_state_init(kv)
-        la.la_prefill(q, k, v, slopes, kv, o=o, workspace=ws)
+        la.la_prefill(q, k, v, slopes, kv, o=o, ckpt=ck, ckpt_every=w.ckpt_every, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -150,7 +153,7 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True)
     for a, b in ev:
         la.la_state_init(kv)
         a.record(stream)
-        la.la_prefill(q, k, v, slopes, kv, o=o, workspace=ws)
+        la.la_prefill(q, k, v, slopes, kv, o=o, ckpt=ck, ckpt_every=w.ckpt_every, workspace=ws)
         b.record(stream)
     torch.cuda.synchronize()
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -416,6 +419,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the informational share (8 x 32K) and long (8 x 1M) prefill legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
@@ -469,6 +474,19 @@ def main():
         result["varlen"] = varlen
     if backward is not None:
         result["backward"] = backward
+    if args.workload == "full" and not args.no_other_workloads:
+        others = {}
+        for name, steps in (("share", 20), ("long", 3)):
+            wo = synth.WORKLOADS[name]
+            ms_o, kms_o, nch_o, _, _ = time_prefill(wo, steps, 1, device, with_backward=False, with_varlen=False)
+            th = wo.batch * wo.heads * wo.n
+            log(f"prefill {name}: {ms_o:.3f} ms/step, kernel(s) {kms_o:.3f} ms, {nch_o} chunk(s)")
+            others[name] = {"workload": f"batch {wo.batch}, {wo.heads} heads, d={wo.d}, N={wo.n}, bf16, "
+                                        f"{nch_o} chunks (LASP+ summaries + prefix combine)",
+                            "ms_per_step": ms_o, "kernel_ms": kms_o, "tokens_per_s": wo.batch * wo.n / (ms_o * 1e-3),
+                            "hbm_frac": BYTES_PER_TOKEN_HEAD * th / (kms_o * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "mfma_frac": model_flops_per_token_head(wo.d) * th / (ms_o * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        result["other_workloads"] = others
     if not args.no_decode:
         result["mixed_batch"] = time_mixed(device)
         result["decode_small_batch"] = time_decode_small(device)

@@ -509,6 +509,12 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         __builtin_amdgcn_sched_barrier(0);
         stage_tile(RA, 0, 0);
         if (OUT) write_state_copy(swc, st, 0);
+        // Checkpoints fall on tile ends (ckpt_every is a multiple of the tile and chunks start on
+        // tile boundaries), so a per-tile counter replaces a 64-bit division per tile: ck_phase
+        // counts the tiles since the last checkpoint, ck_slot is the next checkpoint's slot.
+        const int ck_tiles = a.ckpt ? (int)(a.ckpt_every / BK) : 1;
+        int ck_phase = a.ckpt ? (int)((t_begin / BK) % ck_tiles) : 0;
+        int64_t ck_slot = a.ckpt ? t_begin / a.ckpt_every : 0;
         __syncthreads();
         auto step = [&](KVRegs& R, KVRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
@@ -517,9 +523,12 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             update_state(swc, st, buf, tile);
             if (OUT && tile + 1 < n_tiles) write_state_copy(swc, st, buf ^ 1);
             if (MODE != kModeLocal && a.ckpt) {
-                const int64_t end = tile_start(tile) + tile_len(tile);
-                if (end % a.ckpt_every == 0)
-                    store_state(swc, st, a.ckpt + (u * a.n_ckpt + (end / a.ckpt_every - 1)) * d2);
+                if (++ck_phase == ck_tiles) {
+                    ck_phase = 0;
+                    // a short last tile never ends on a checkpoint (its end is not a tile multiple)
+                    if (tile_len(tile) == BK) store_state(swc, st, a.ckpt + (u * a.n_ckpt + ck_slot) * d2);
+                    ++ck_slot;
+                }
             }
             if (tile + 1 < n_tiles) stage_tile(Rn, buf ^ 1, tile + 1);
         };
