@@ -260,6 +260,22 @@ la_status la_backward(la_dtype dt, const void* q, const void* k, const void* v, 
                       const float* kv_in, const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * la_backward for packed variable-length sequences (layout, cu_seqlens and
+ * short-sequence handling as la_prefill_varlen): kv_in, dkv_out and dkv_in
+ * are [n_seq][heads][d][d] float32 (NULL as for la_backward).  Each sequence's
+ * gradients use only its own tokens and states; an empty sequence gives
+ * dkv_in = dkv_out.  Like la_prefill_varlen it uploads chunk tables (three
+ * times: one per run) and must not be captured into a graph.
+ */
+size_t la_backward_varlen_workspace_size(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                         int64_t d);
+la_status la_backward_varlen(la_dtype dt, const void* q, const void* k, const void* v, const void* dout,
+                             int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
+                             int64_t stride_h, int64_t stride_n, const float* slopes, const float* kv_in,
+                             const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 

@@ -34,6 +34,7 @@ EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_si
             "la_prefill_varlen_workspace_size", "la_prefill_varlen_workspace_size_ex",
             "la_prefill_varlen_chunk_tokens", "la_prefill_varlen", "la_prefill_varlen_ex", "la_decode",
             "la_prefill_fused", "la_decode_fused", "la_backward_workspace_size", "la_backward",
+            "la_backward_varlen_workspace_size", "la_backward_varlen",
             "la_status_string", "la_last_error"]
 
 LA_SILU_Q = 1
@@ -98,6 +99,10 @@ def lib():
     L.la_backward_workspace_size.argtypes = [i32, i64, i64, i64, i64]
     L.la_backward.restype = i32
     L.la_backward.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
+    L.la_backward_varlen_workspace_size.restype = sz
+    L.la_backward_varlen_workspace_size.argtypes = [i32, i64, p, i64, i64]
+    L.la_backward_varlen.restype = i32
+    L.la_backward_varlen.argtypes = [i32, p, p, p, p, i64, p, i64, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
     L.la_decode.restype = i32
     L.la_decode.argtypes = [i32, p, p, p, p, i64, i64, i64, p, p, p]
     L.la_status_string.restype = ctypes.c_char_p
@@ -383,4 +388,51 @@ def la_backward(q, k, v, dout, slopes, kv_in=None, dkv_out=None, dq=None, dk=Non
                            _ptr(kv_in), _ptr(dkv_out), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(dkv_in),
                            _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
     _check(st, "la_backward")
+    return outs[0], outs[1], outs[2], dkv_in
+
+
+def la_backward_varlen_workspace_size(dtype: int, cu_seqlens, heads: int, d: int) -> int:
+    cu, n_seq = _cu_array(cu_seqlens)
+    return int(lib().la_backward_varlen_workspace_size(dtype, n_seq, cu, heads, d))
+
+
+def la_backward_varlen(q, k, v, dout, slopes, cu_seqlens, kv_in=None, dkv_out=None, dq=None, dk=None, dv=None,
+                       dkv_in=None, workspace=None, stream=None):
+    """la_backward for packed sequences: q, k, v, dout are [T, H, d] (or any [T, H, d] view with a
+    contiguous last dimension and shared strides) and cu_seqlens holds n_seq + 1 offsets (host);
+    states are [n_seq, H, d, d] float32.  Returns (dq, dk, dv, dkv_in)."""
+    import torch
+
+    _require_cuda(q, k, v, dout, slopes, kv_in, dkv_out, dq, dk, dv, dkv_in, workspace)
+    dt = _dtype_code(q)
+    T, H, d = q.shape
+    for t in (k, v, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or t.stride() != q.stride():
+            raise ValueError("q, k, v, dout must share shape, strides and dtype")
+    if q.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    cu, n_seq = _cu_array(cu_seqlens)
+    if cu[n_seq] != T:
+        raise ValueError("cu_seqlens[-1] must equal the number of packed tokens")
+    outs = []
+    for t in (dq, dk, dv):
+        if t is None:
+            t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        elif t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+            raise ValueError("dq, dk, dv must match q in shape, strides and dtype")
+        outs.append(t)
+    for t in (kv_in, dkv_out, dkv_in):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (n_seq, H, d, d) or not t.is_contiguous()):
+            raise ValueError("states must be contiguous float32 [n_seq, H, d, d]")
+    if dkv_in is None:
+        dkv_in = torch.empty(n_seq, H, d, d, dtype=torch.float32, device=q.device)
+    need = int(lib().la_backward_varlen_workspace_size(dt, n_seq, cu, H, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    sn, sh, _ = q.stride()
+    st = lib().la_backward_varlen(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), n_seq, cu, H, d, sh, sn, _ptr(slopes),
+                                  _ptr(kv_in), _ptr(dkv_out), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                  _ptr(dkv_in), _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
+    _check(st, "la_backward_varlen")
     return outs[0], outs[1], outs[2], dkv_in

@@ -363,7 +363,7 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
 la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
                               int64_t sh, int64_t sn, const float* slopes, float* kv, int64_t chunk_tokens,
-                              void* workspace, size_t workspace_bytes, void* stream)
+                              void* workspace, size_t workspace_bytes, void* stream, bool rev = false)
 {
     VarPlan p;
     la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, chunk_tokens, p);
@@ -406,12 +406,13 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     a.ctab = ctab;
     a.stab = ctab + 5 * p.total_chunks;
     a.groups = p.total_chunks * heads;
+    a.rev = rev ? 1 : 0;
     auto run = [&](int mode) -> hipError_t {
         return dt == LA_BF16 ? launch_fwd_bf16(a, mode, st) : launch_fwd_f32(a, (int)d, mode, st);
     };
     if (p.n_short > 0) {
         const int64_t* rtab = a.stab + 2 * n_seq;
-        s = launch_status(launch_recur_short(dt, q, k, v, o, p.n_short, heads, (int)d, sn, sh, slopes, kv, rtab, st),
+        s = launch_status(launch_recur_short(dt, q, k, v, o, p.n_short, heads, (int)d, sn, sh, slopes, kv, rtab, rev, st),
                           "short-sequence launch");
         if (s != LA_OK) return s;
     }
@@ -424,6 +425,52 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
         if (s != LA_OK) return s;
     }
     return launch_status(run(o ? kModeOut : kModeState), "prefill launch");
+}
+
+// The backward pass for packed sequences: the three runs of backward_impl, each over the packed
+// layout (the reverse runs walk every sequence from its last token to its first).
+size_t backward_varlen_bytes(const VarPlan& p, int64_t n_seq, int64_t heads, int64_t d)
+{
+    return state_bytes(n_seq, heads, d) + varlen_workspace_bytes(p, heads, d);
+}
+
+la_status backward_varlen_impl(la_dtype dt, const void* q, const void* k, const void* v, const void* dout,
+                               int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d, int64_t sh, int64_t sn,
+                               const float* slopes, const float* kv_in, const float* dkv_out, void* dq, void* dk,
+                               void* dv, float* dkv_in, void* workspace, size_t workspace_bytes, void* stream)
+{
+    VarPlan p;
+    la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, 0, p);
+    if (s != LA_OK) return s;
+    if (!slopes) return fail(LA_ERR_INVALID_ARGUMENT, "slopes must not be NULL");
+    if (cu[n_seq] > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
+        return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk, dv must not be NULL");
+    if ((kv_in && !aligned16(kv_in)) || (dkv_out && !aligned16(dkv_out)) || (dkv_in && !aligned16(dkv_in)))
+        return fail(LA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
+    const size_t sbytes = state_bytes(n_seq, heads, d);
+    if (!workspace || workspace_bytes < backward_varlen_bytes(p, n_seq, heads, d) || !aligned16(workspace))
+        return fail(LA_ERR_WORKSPACE, "workspace missing, misaligned or smaller than la_backward_varlen_workspace_size");
+    s = device_check();
+    if (s != LA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* S = static_cast<float*>(workspace);
+    void* vws = static_cast<char*>(workspace) + sbytes;
+    const size_t vbytes = workspace_bytes - sbytes;
+    const int64_t bh = n_seq * heads;
+    auto prep = [&](float* dst, const float* src, bool tr, int power) {
+        return launch_status(launch_state_prep(dst, src, slopes, bh, heads, (int)d, tr, power, st), "state set-up launch");
+    };
+    s = prep(S, kv_in, true, 0);
+    if (s == LA_OK)
+        s = prefill_varlen_impl(dt, dout, v, k, dq, n_seq, cu, heads, d, sh, sn, slopes, S, 0, vws, vbytes, stream);
+    if (s == LA_OK) s = prep(S, dkv_out, true, dkv_out ? 1 : 0);
+    if (s == LA_OK)
+        s = prefill_varlen_impl(dt, v, dout, q, dk, n_seq, cu, heads, d, sh, sn, slopes, S, 0, vws, vbytes, stream, true);
+    if (s == LA_OK) s = prep(S, dkv_out, false, dkv_out ? 1 : 0);
+    if (s == LA_OK)
+        s = prefill_varlen_impl(dt, k, q, dout, dv, n_seq, cu, heads, d, sh, sn, slopes, S, 0, vws, vbytes, stream, true);
+    if (s == LA_OK && dkv_in) s = prep(dkv_in, S, false, -1);
+    return s;
 }
 
 }  // namespace
@@ -613,6 +660,34 @@ la_status la_backward(la_dtype dt, const void* q, const void* k, const void* v, 
     try {
         return backward_impl(dt, q, k, v, dout, batch, heads, n, d, stride_b, stride_h, stride_n, slopes, kv_in,
                              dkv_out, dq, dk, dv, dkv_in, workspace, workspace_bytes, stream);
+    } catch (const std::exception& e) {
+        return fail(LA_ERR_INTERNAL, e.what());
+    } catch (...) {
+        return fail(LA_ERR_INTERNAL, "unknown error");
+    }
+}
+
+size_t la_backward_varlen_workspace_size(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
+                                         int64_t d)
+{
+    try {
+        VarPlan p;
+        if (make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, 0, p) != LA_OK) return 0;
+        return backward_varlen_bytes(p, n_seq, heads, d);
+    } catch (...) {
+        return 0;
+    }
+}
+
+la_status la_backward_varlen(la_dtype dt, const void* q, const void* k, const void* v, const void* dout,
+                             int64_t n_seq, const int64_t* cu_seqlens, int64_t heads, int64_t d,
+                             int64_t stride_h, int64_t stride_n, const float* slopes, const float* kv_in,
+                             const float* dkv_out, void* dq, void* dk, void* dv, float* dkv_in,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    try {
+        return backward_varlen_impl(dt, q, k, v, dout, n_seq, cu_seqlens, heads, d, stride_h, stride_n, slopes, kv_in,
+                                    dkv_out, dq, dk, dv, dkv_in, workspace, workspace_bytes, stream);
     } catch (const std::exception& e) {
         return fail(LA_ERR_INTERNAL, e.what());
     } catch (...) {

@@ -72,8 +72,8 @@ struct FwdArgs {
     // sigmoid(gate) before it is stored.
     uint32_t act;
     const void* gate;
-    // Reverse walk (fixed-length batches only): token t of the recurrence is memory row n-1-t
-    // of its sequence; outputs are written to the same rows.  Used by the backward pass.
+    // Reverse walk: token t of the recurrence is memory row rev_end-1-t of its sequence (see
+    // Work); outputs are written to the same rows.  Used by the backward pass.
     int rev;
 };
 
@@ -98,6 +98,8 @@ struct Work {
     int64_t t_end;
     int64_t slot_in;   // workspace slot with the chunk's incoming prefix (chunked sequences)
     int64_t slot_out;  // workspace slot that receives the chunk's local state (kModeLocal)
+    int64_t rev_end;   // reverse walk: token u of the recurrence is memory row rev_end - 1 - u
+                       // (n for a fixed-length batch, s0 + s1 for packed sequence [s0, s1))
 };
 
 __device__ inline Work decode_work(const FwdArgs& a, int64_t group)
@@ -116,6 +118,9 @@ __device__ inline Work decode_work(const FwdArgs& a, int64_t group)
         w.base = w.h * a.sh;
         w.slot_in = c * a.heads + w.h;
         w.slot_out = (c + 1) * a.heads + w.h;
+        // the sequence's first chunk begins at s0 and its last chunk ends at s1
+        const int64_t c0 = e[4];
+        w.rev_end = a.rev ? a.ctab[5 * c0] + a.ctab[5 * (c0 + w.nck - 1) + 1] : 0;
     } else {
         w.u = group / a.chunks_launched;
         w.j = group % a.chunks_launched;
@@ -127,6 +132,7 @@ __device__ inline Work decode_work(const FwdArgs& a, int64_t group)
         w.base = bb * a.sb + w.h * a.sh;
         w.slot_in = w.u * a.n_chunks + w.j;
         w.slot_out = w.slot_in + 1;
+        w.rev_end = a.n;
     }
     return w;
 }
@@ -152,9 +158,10 @@ hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStre
 // only without the transpose.
 hipError_t launch_state_prep(float* dst, const float* src, const float* slopes, int64_t bh, int64_t heads,
                              int d, bool transpose, int power, hipStream_t stream);
+// Sequences of <= kShortTokens tokens, token by token (rev: from the last token to the first).
 hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_short, int64_t heads, int d, int64_t sn, int64_t sh,
-                              const float* slopes, float* kv, const int64_t* tab, hipStream_t stream);
+                              const float* slopes, float* kv, const int64_t* tab, bool rev, hipStream_t stream);
 // Decode step; `fu` (optional) adds the SiLU prologue, RMS normalisation and gate epilogue.
 hipError_t launch_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                          int64_t bh, int64_t heads, int d, const float* slopes, float* kv,

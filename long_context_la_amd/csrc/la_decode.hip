@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void k_recur_short(const T* __restrict__ q, co
                                                      const T* __restrict__ v, T* __restrict__ o,
                                                      const float* __restrict__ slopes, float* __restrict__ kv,
                                                      int64_t heads, int64_t sn, int64_t sh,
-                                                     const int64_t* __restrict__ tab)
+                                                     const int64_t* __restrict__ tab, int rev)
 {
     constexpr int CG = D / 4;
     constexpr int RG = 256 / CG;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_recur_short(const T* __restrict__ q, co
     for (int m = 0; m < RPT; ++m) st[m] = reinterpret_cast<const f32x4*>(S + (rg + RG * m) * D)[cg];
     const float lam = (float)exp(-(double)slopes[h]);
     for (int64_t i = 0; i < n; ++i) {
-        const int64_t row = (tok0 + i) * sn + h * sh;
+        const int64_t row = (rev ? tok0 + n - 1 - i : tok0 + i) * sn + h * sh;
         if (tid < D) {
             sq[tid] = to_f32(q[row + tid]);
             sk[tid] = to_f32(k[row + tid]);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void k_recur_short(const T* __restrict__ q, co
 
 hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_short, int64_t heads, int d, int64_t sn, int64_t sh,
-                              const float* slopes, float* kv, const int64_t* tab, hipStream_t stream)
+                              const float* slopes, float* kv, const int64_t* tab, bool rev, hipStream_t stream)
 {
     const dim3 grid((unsigned)(n_short * heads)), block(256);
     if (dt == LA_BF16) {
@@ -223,17 +223,17 @@ hipError_t launch_recur_short(la_dtype dt, const void* q, const void* k, const v
              vv = static_cast<const __bf16*>(v);
         auto oo = static_cast<__bf16*>(o);
         if (d == 128)
-            hipLaunchKernelGGL((k_recur_short<__bf16, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+            hipLaunchKernelGGL((k_recur_short<__bf16, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab, rev ? 1 : 0);
         else
-            hipLaunchKernelGGL((k_recur_short<__bf16, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+            hipLaunchKernelGGL((k_recur_short<__bf16, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab, rev ? 1 : 0);
     } else {
         auto qq = static_cast<const float*>(q), kk = static_cast<const float*>(k),
              vv = static_cast<const float*>(v);
         auto oo = static_cast<float*>(o);
         if (d == 128)
-            hipLaunchKernelGGL((k_recur_short<float, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+            hipLaunchKernelGGL((k_recur_short<float, 128>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab, rev ? 1 : 0);
         else
-            hipLaunchKernelGGL((k_recur_short<float, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab);
+            hipLaunchKernelGGL((k_recur_short<float, 64>), grid, block, 0, stream, qq, kk, vv, oo, slopes, kv, heads, sn, sh, tab, rev ? 1 : 0);
     }
     return hipGetLastError();
 }

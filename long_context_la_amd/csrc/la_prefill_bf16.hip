@@ -243,7 +243,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int64_t t0 = tile_start(tile);
         if constexpr (!REV) return t0;
         const int L = tile_len(tile);
-        const int64_t r0 = a.n - t0 - (L > 0 ? L : 0);
+        const int64_t r0 = wk.rev_end - t0 - (L > 0 ? L : 0);
         return r0 > 0 ? r0 : (int64_t)0;
     };
     auto row_off = [&](int tile, int r) __attribute__((always_inline)) {
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
         const int64_t t0 = t_begin + (int64_t)tile * BK;
         if constexpr (!REV) return t0;
         const int L = tile_len(tile);
-        const int64_t r0 = a.n - t0 - (L > 0 ? L : 0);
+        const int64_t r0 = wk.rev_end - t0 - (L > 0 ? L : 0);
         return r0 > 0 ? r0 : (int64_t)0;
     };
     auto row_off = [&](int tile, int r) __attribute__((always_inline)) {

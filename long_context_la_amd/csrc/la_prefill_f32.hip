@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     const int64_t d2 = (int64_t)D * D;
     // memory row of token t of the recurrence: t, or n-1-t when the sequence is walked backwards
     // (the reverse state recurrence of the backward pass)
-    auto mrow = [&](int64_t t) { return a.rev ? a.n - 1 - t : t; };
+    auto mrow = [&](int64_t t) { return a.rev ? wk.rev_end - 1 - t : t; };
 
     // incoming state slice
     float st[RPT];

@@ -222,3 +222,27 @@ def test_backward_validation_codes():
     if not gpu_available():
         assert _backward(ws_bytes=need) == la.LA_ERR_DEVICE
         assert _backward(N=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) == la.LA_ERR_DEVICE
+
+
+def test_backward_varlen_workspace_and_validation():
+    lengths = [300, 0, 5, 1, 2000]
+    cu = _cu(lengths)
+    ws = la.la_backward_varlen_workspace_size(la.LA_BF16, cu, 2, 128)
+    assert ws == len(lengths) * 2 * 128 * 128 * 4 + la.la_prefill_varlen_workspace_size(la.LA_BF16, cu, 2, 128)
+    assert la.la_backward_varlen_workspace_size(la.LA_BF16, [1, 5], 2, 128) == 0     # cu[0] != 0
+    c, n_seq = la._cu_array(cu)
+    L = la.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, do=FAKE, dk=FAKE, slopes=FAKE, dkv_out=None, ws=FAKE, ws_bytes=ws)
+        a.update(kw)
+        return L.la_backward_varlen(la.LA_BF16, a["q"], FAKE, FAKE, a["do"], n_seq, c, 2, 128, 128, 256,
+                                    a["slopes"], None, a["dkv_out"], FAKE, a["dk"], FAKE, None, a["ws"],
+                                    a["ws_bytes"], None)
+    assert call(do=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert call(dk=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert call(slopes=None) == la.LA_ERR_INVALID_ARGUMENT
+    assert call(dkv_out=ctypes.c_void_p((1 << 20) + 4)) == la.LA_ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=ws - 16) == la.LA_ERR_WORKSPACE
+    if not gpu_available():
+        assert call() == la.LA_ERR_DEVICE
