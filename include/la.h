@@ -130,8 +130,9 @@ size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int6
  *                ckpt_every must be a positive multiple of 64.
  *   workspace  : device scratch of at least la_prefill_workspace_size() bytes
  *                (may be NULL when that size is 0); contents are clobbered.
- * Supported: LA_F32 with d in {64, 128}; LA_BF16 with d = 128.  n == 0 is a
- * no-op that leaves kv unchanged.
+ * Supported: d in {64, 128} for both dtypes (bfloat16 at d = 128 runs on the
+ * MFMA kernels, every other case on the float32-arithmetic tile kernel).
+ * n == 0 is a no-op that leaves kv unchanged.
  */
 la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                      int64_t batch, int64_t heads, int64_t n, int64_t d,

@@ -53,7 +53,8 @@ def test_prefill_validation_codes():
     assert _prefill(B=0) == la.LA_ERR_INVALID_ARGUMENT
     assert _prefill(N=-1) == la.LA_ERR_INVALID_ARGUMENT
     assert _prefill(d=96, sn=96) == la.LA_ERR_UNSUPPORTED
-    assert _prefill(d=64, sn=64) == la.LA_ERR_UNSUPPORTED          # bf16 needs d = 128
+    # bf16 at d = 64 is a supported shape: it gets as far as the workspace check
+    assert _prefill(d=64, sn=64, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
     assert _prefill(sn=100) == la.LA_ERR_INVALID_ARGUMENT           # not a 16-byte multiple
     assert _prefill(sn=64) == la.LA_ERR_INVALID_ARGUMENT            # stride_n < d
     assert _prefill(q=ctypes.c_void_p((1 << 20) + 2)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned
@@ -156,7 +157,8 @@ def test_varlen_validation_codes():
     assert _varlen([10, 20], kv=None) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], cu=[3, 10, 20]) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], cu=[0, 10, 5]) == la.LA_ERR_INVALID_ARGUMENT
-    assert _varlen([10, 20], d=64, sh=64, sn=512) == la.LA_ERR_UNSUPPORTED
+    assert _varlen([10, 20], d=96, sh=96, sn=768) == la.LA_ERR_UNSUPPORTED
+    assert _varlen([10, 20], d=64, sh=64, sn=512, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE  # bf16 d = 64: valid
     assert _varlen([10, 20], sn=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], chunk=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
@@ -215,7 +217,7 @@ def test_backward_validation_codes():
     assert _backward(do=None) == la.LA_ERR_INVALID_ARGUMENT
     assert _backward(dk=None) == la.LA_ERR_INVALID_ARGUMENT
     assert _backward(slopes=None) == la.LA_ERR_INVALID_ARGUMENT
-    assert _backward(d=64, sn=64) == la.LA_ERR_UNSUPPORTED                                 # bf16 needs d = 128
+    assert _backward(d=64, sn=64, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE              # bf16 d = 64 is valid
     assert _backward(dkv_out=ctypes.c_void_p((1 << 20) + 4)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned state
     assert _backward(ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
     assert _backward(ws_bytes=need - 16) == la.LA_ERR_WORKSPACE

@@ -49,7 +49,7 @@ def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, l
     assert_close(dkv.cpu().numpy(), want[3], dtype, f"dkv_in {what}")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)])
 @pytest.mark.parametrize("states", [False, True])
 def test_backward_small(device, dtype, d, states):
     run_backward(1, 2, 200, d, dtype, device, states=states)
@@ -69,6 +69,12 @@ def test_backward_chunked_bf16(device):
 
 def test_backward_chunked_f32(device):
     run_backward(1, 1, 3000, 64, "f32", device, states=True, seed=91)
+
+
+def test_backward_chunked_bf16_d64(device):
+    # bfloat16 at d = 64 runs on the VALU tile kernel, chunked like the others
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 2, 3000, 64) < 3000
+    run_backward(1, 2, 3000, 64, "bf16", device, states=True, seed=94)
 
 
 def test_backward_strided_layout(device):

@@ -107,7 +107,7 @@ def assert_close_epilogue(got, want, o_pre, dtype, what, norm, eps, weight, gate
     return worst
 
 
-CASES = [("bf16", 128), ("f32", 128), ("f32", 64)]
+CASES = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)]
 
 
 @pytest.mark.parametrize("dtype,d", CASES)

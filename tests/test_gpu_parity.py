@@ -76,6 +76,12 @@ def test_bf16_ragged(device, N):
     check_prefill(23, 1, 2, N, 128, "bf16", SL2, device)
 
 
+@pytest.mark.parametrize("N", [1, 63, 65, 1000])
+def test_bf16_d64_ragged(device, N):
+    # bfloat16 at d = 64: the VALU tile kernel with bfloat16 loads and stores
+    check_prefill(35, 2, 3, N, 64, "bf16", np.array([0.5, 2.0 ** -3, 2.0 ** -7], np.float32), device)
+
+
 @pytest.mark.parametrize("chunk", [64, 1024, 0])
 def test_bf16_chunked(device, chunk):
     check_prefill(24, 1, 2, 8192, 128, "bf16", np.array([2.0 ** -4, 2.0 ** -10], np.float32), device,
@@ -159,7 +165,7 @@ def test_impulse(device, dtype):
     assert_close(kv, kv_ref, dtype, "impulse KV")
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])
 def test_checkpoints(device, dtype, d):
     check_prefill(30, 1, 2, 1024, d, dtype, SL2, device, ckpt_every=256, chunk_tokens=320 if dtype == "f32" else 0)
     check_prefill(31, 1, 2, 2048, d, dtype, SL2, device, ckpt_every=512, chunk_tokens=1024)
@@ -221,6 +227,13 @@ def test_n_zero_is_noop(device):
     la.la_prefill(q, q, q, torch.zeros(2, device=device), kv, o=torch.empty_like(q))
     torch.cuda.synchronize()
     assert torch.equal(kv, before)
+
+
+def test_bf16_d64_chunked_with_states(device):
+    # chunks and sub-chunk summaries through the VALU tile kernel's summary mode
+    kv0 = np.random.default_rng(10).standard_normal((1, 2, 64, 64)).astype(np.float32)
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 2, 9000, 64) < 9000
+    check_prefill(36, 1, 2, 9000, 64, "bf16", SL2, device, kv_in=kv0)
 
 
 def test_bf16_chunked_batch_with_states(device):

@@ -20,7 +20,7 @@ def _torch():
 
 def _case(i):
     rng = np.random.default_rng(1000 + i)
-    dtype, d = [("bf16", 128), ("f32", 128), ("f32", 64)][rng.integers(3)]
+    dtype, d = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)][rng.integers(4)]
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
     N = int(rng.integers(1, 2600))
     chunk = int(rng.choice([0, 64, 128, 256, 512, 1024, 1088]))

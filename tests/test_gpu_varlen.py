@@ -92,7 +92,7 @@ def run_varlen(lengths, H, d, dtype, device, chunk_tokens=0, head_major=False, w
 LENGTHS = [0, 1, 5, 64, 65, 200, 1000, 1500]
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)])
 def test_varlen_mixed_lengths(device, dtype, d):
     run_varlen(LENGTHS, 4, d, dtype, device)
 
