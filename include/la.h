@@ -120,7 +120,9 @@ size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int6
  *                the last dimension is contiguous).  q, k, v are read-only and
  *                may alias each other; o must not overlap q, k, v or kv.
  *                Pointers 16-byte aligned; strides multiples of 8 elements
- *                (bf16) or 4 (f32); stride_n >= d.
+ *                (bf16) or 4 (f32); d <= stride_n <= 2^22 (a 64-row tile
+ *                then spans under 2 GiB, the reach of a 32-bit buffer
+ *                offset), else LA_ERR_UNSUPPORTED.
  *   slopes     : [heads] float32 device array, s_h >= 0 and finite
  *                (documented, not checked: reading it would need a sync);
  *                lambda_h = exp(-s_h).

@@ -76,6 +76,10 @@ using namespace la;
 
 namespace {
 
+// Tile kernels address a 64-row tile with 32-bit buffer offsets (rows past a ragged tail wrap to
+// offsets above the tile's range): a row stride of at most 2^22 elements keeps that within reach.
+constexpr int64_t kMaxRowStride = int64_t(1) << 22;
+
 la_status check_shape(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)
 {
     if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_INVALID_ARGUMENT, "dtype must be LA_F32 or LA_BF16");
@@ -132,6 +136,7 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     const int64_t align = (dt == LA_BF16) ? 8 : 4;
     if (sn < d || sb < 0 || sh < 0 || sb % align || sh % align || sn % align)
         return fail(LA_ERR_INVALID_ARGUMENT, "strides must be >= 0, multiples of 16 bytes, stride_n >= d");
+    if (sn > kMaxRowStride) return fail(LA_ERR_UNSUPPORTED, "stride_n above 2^22 elements");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) || !aligned16(kv) ||
         (ckpt && !aligned16(ckpt)))
         return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
@@ -374,6 +379,7 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     const int64_t align = (dt == LA_BF16) ? 8 : 4;
     if (sn < d || sh < 0 || sh % align || sn % align)
         return fail(LA_ERR_INVALID_ARGUMENT, "strides must be >= 0, multiples of 16 bytes, stride_n >= d");
+    if (sn > kMaxRowStride) return fail(LA_ERR_UNSUPPORTED, "stride_n above 2^22 elements");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) || !aligned16(kv))
         return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
     const size_t need = varlen_workspace_bytes(p, heads, d);

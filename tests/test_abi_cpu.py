@@ -57,6 +57,7 @@ def test_prefill_validation_codes():
     assert _prefill(d=64, sn=64, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
     assert _prefill(sn=100) == la.LA_ERR_INVALID_ARGUMENT           # not a 16-byte multiple
     assert _prefill(sn=64) == la.LA_ERR_INVALID_ARGUMENT            # stride_n < d
+    assert _prefill(sn=(1 << 22) + 8) == la.LA_ERR_UNSUPPORTED      # 32-bit tile offsets
     assert _prefill(q=ctypes.c_void_p((1 << 20) + 2)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned
     assert _prefill(ckpt=FAKE, ckpt_every=100) == la.LA_ERR_UNSUPPORTED
     assert _prefill(ckpt=FAKE, ckpt_every=0) == la.LA_ERR_UNSUPPORTED
@@ -160,6 +161,7 @@ def test_varlen_validation_codes():
     assert _varlen([10, 20], d=96, sh=96, sn=768) == la.LA_ERR_UNSUPPORTED
     assert _varlen([10, 20], d=64, sh=64, sn=512, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE  # bf16 d = 64: valid
     assert _varlen([10, 20], sn=100) == la.LA_ERR_INVALID_ARGUMENT
+    assert _varlen([10, 20], sn=(1 << 22) + 8) == la.LA_ERR_UNSUPPORTED
     assert _varlen([10, 20], chunk=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
     assert _varlen([10, 20], ws_bytes=8) == la.LA_ERR_WORKSPACE
