@@ -88,6 +88,32 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+SETTLE_S = 0.2  # seconds of untimed steps before each leg's warm-up (--settle-s)
+
+
+def set_settle(seconds):
+    global SETTLE_S
+    SETTLE_S = max(0.0, float(seconds))
+
+
+def settle(fn, seconds=None, batch=4):
+    """Runs `fn` (one untimed step) for about `seconds` of wall time before a leg's warm-up.
+    After the GPU idles (input generation on the host), its clock climbs over the first ~15
+    launches of the full-layer prefill (~5.6 ms for the first step, ~2.6 ms from about the 15th);
+    the timed steps should see the clock that a continuous workload runs at."""
+    import torch
+
+    seconds = SETTLE_S if seconds is None else seconds
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        n += batch
+    return n
+
+
 def model_flops_per_token_head(d=128, B=MODEL_TILE):
     return 4 * B * d + 4 * d * d
 
@@ -138,6 +164,7 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True)
         la.la_state_init(kv)
         la.la_prefill(q, k, v, slopes, kv, o=o, ckpt=ck, ckpt_every=w.ckpt_every, workspace=ws)
 
+    settle(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -183,6 +210,7 @@ def time_backward(q, k, v, dout, slopes, w, steps, warmup, device):
     def call():
         la.la_backward(q, k, v, dout, slopes, dkv_out=g, dq=dq, dk=dk, dv=dv, dkv_in=dkv, workspace=ws)
 
+    settle(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -219,6 +247,7 @@ def time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device):
     ws = torch.empty(la.la_prefill_varlen_workspace_size(la.LA_BF16, cu, w.heads, w.d), dtype=torch.uint8,
                      device=device)
     stream = torch.cuda.current_stream(device)
+    settle(lambda: la.la_prefill_varlen(qv, kv_, vv, slopes, kv, cu, o=ov, workspace=ws))
     for _ in range(warmup):
         la.la_prefill_varlen(qv, kv_, vv, slopes, kv, cu, o=ov, workspace=ws)
     torch.cuda.synchronize()
@@ -369,6 +398,7 @@ def time_decode(w, steps, device, prefix_slab=16):
     stream = torch.cuda.current_stream(device)
     # warm-up on a scratch copy of the state so the timed run starts from the preloaded one
     scratch = kv.clone()
+    settle(lambda: la.la_decode(toks[0][0], toks[1][0], toks[2][0], slopes, scratch, o))
     for s in range(3):
         la.la_decode(toks[0][s], toks[1][s], toks[2][s], slopes, scratch, o)
     del scratch
@@ -413,6 +443,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before each leg's warm-up (lets the clock settle)")
     ap.add_argument("--workload", default="full", choices=["full", "share", "long"])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
@@ -424,9 +456,10 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
+    set_settle(args.settle_s)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences would "
-              "shard across GPUs with no or one small exchange; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU; runs on several GPUs are not supported (heads and sequences "
+              "would shard across GPUs with no exchange or one small all-gather).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -455,6 +488,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_s,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
