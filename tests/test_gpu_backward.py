@@ -115,7 +115,7 @@ def test_backward_is_deterministic(device):
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
 def test_backward_varlen_packed(device, dtype, d):
     """la_backward_varlen on packed sequences of mixed lengths: empty, short (token by token),
     tiled, and long enough to be cut into chunks, each with its own states; every sequence is

@@ -158,7 +158,7 @@ def test_mixed_step_two_streams(device):
         assert_close(kvp.cpu().numpy()[s:s + 1], kv_r, dtype, f"mixed step prefill KV {s}")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
 def test_varlen_short_sequences(device, dtype, d):
     # 1..8 tokens run token by token, 9 and more in 64-token tiles; the boundary on both sides
     run_varlen([1, 8, 9, 2, 0, 7, 3], 3, d, dtype, device)
