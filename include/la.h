@@ -133,7 +133,9 @@ size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int6
  *   workspace  : device scratch of at least la_prefill_workspace_size() bytes
  *                (may be NULL when that size is 0); contents are clobbered.
  * Supported: d in {64, 128} for both dtypes (bfloat16 at d = 128 runs on the
- * MFMA kernels, every other case on the float32-arithmetic tile kernel).
+ * MFMA kernels, every other case on the float32-arithmetic tile kernel);
+ * batch*heads <= 2^20, and batch*heads*chunks <= 2^20 for the chunk count the
+ * plan (or chunk_tokens) gives, else LA_ERR_UNSUPPORTED.
  * n == 0 is a no-op that leaves kv unchanged.
  */
 la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, void* o,
@@ -226,7 +228,8 @@ la_status la_decode_fused(la_dtype dt, const void* q, const void* k, const void*
  * generation as its own kernel): kv <- lambda_h * kv + k^T v, then o = q . kv.
  *   q, k, v, o : contiguous [batch][heads][d] of dtype dt (o must not overlap
  *                q, k, v or kv); slopes [heads] float32; kv [batch][heads][d][d]
- *                float32 updated in place.  d in {64, 128}; both dtypes.
+ *                float32 updated in place.  d in {64, 128}; both dtypes;
+ *                batch*heads <= 2^20 (else LA_ERR_UNSUPPORTED).
  */
 la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                     int64_t batch, int64_t heads, int64_t d,

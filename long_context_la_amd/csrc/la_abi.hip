@@ -79,6 +79,9 @@ namespace {
 // Tile kernels address a 64-row tile with 32-bit buffer offsets (rows past a ragged tail wrap to
 // offsets above the tile's range): a row stride of at most 2^22 elements keeps that within reach.
 constexpr int64_t kMaxRowStride = int64_t(1) << 22;
+// Work items of one launch: (batch, head) pairs, or (sequence or batch, head, chunk) triples.  At
+// most 2^20 keeps every grid (4 value slices x 512 threads per item) under 2^31 work-items.
+constexpr int64_t kMaxUnits = int64_t(1) << 20;
 
 la_status check_shape(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)
 {
@@ -88,6 +91,7 @@ la_status check_shape(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int6
     if (d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d must be 64 or 128");
     if (batch > (int64_t(1) << 24) || heads > (int64_t(1) << 24) || n > (int64_t(1) << 40))
         return fail(LA_ERR_INVALID_ARGUMENT, "size out of range");
+    if (batch * heads > kMaxUnits) return fail(LA_ERR_UNSUPPORTED, "more than 2^20 (batch, head) pairs in one call");
     return LA_OK;
 }
 
@@ -142,6 +146,9 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
         return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
 
     const Plan p = make_plan(batch, heads, n, d, chunk_tokens);
+    const int64_t n_sub = p.n_chunks > 1 ? (p.n_chunks - 1) * p.sub : 0;
+    if (batch * heads * (p.n_chunks > n_sub ? p.n_chunks : n_sub) > kMaxUnits)
+        return fail(LA_ERR_UNSUPPORTED, "more than 2^20 (batch, head, chunk) work items: use a larger chunk_tokens");
     const size_t need = workspace_bytes_for(p, batch, heads, d);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return fail(LA_ERR_WORKSPACE, "workspace missing, misaligned or smaller than la_prefill_workspace_size");
@@ -338,6 +345,13 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
         chunk = c;
     }
     p.chunk = chunk > 0 ? chunk : kBlock;
+    int64_t n_tiled_chunks = 0;
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t n = cu[s + 1] - cu[s];
+        if (n > kShortTokens) n_tiled_chunks += (n + p.chunk - 1) / p.chunk;
+    }
+    if (n_tiled_chunks * heads > kMaxUnits)
+        return fail(LA_ERR_UNSUPPORTED, "more than 2^20 (chunk, head) work items: use a larger chunk_tokens");
     p.tab.clear();
     std::vector<int64_t> stab((size_t)(2 * n_seq)), rtab;
     for (int64_t s = 0; s < n_seq; ++s) {
@@ -615,7 +629,7 @@ la_status la_decode_fused(la_dtype dt, const void* q, const void* k, const void*
             return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, o, slopes and kv must not be NULL");
         if (batch < 1 || heads < 1) return fail(LA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
         if (d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d must be 64 or 128");
-        if (batch * heads > (int64_t(1) << 31) - 1) return fail(LA_ERR_INVALID_ARGUMENT, "too many (batch, head) pairs");
+        if (batch * heads > kMaxUnits) return fail(LA_ERR_UNSUPPORTED, "more than 2^20 (batch, head) pairs in one call");
         if (!aligned16(kv)) return fail(LA_ERR_INVALID_ARGUMENT, "kv must be 16-byte aligned");
         s = device_check();
         if (s != LA_OK) return s;

@@ -21,22 +21,22 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ ws, const floa
                                               int64_t heads, int64_t n_chunks, int64_t chunk, int d2)
 {
     const int64_t per = d2 / 4;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= bh * per) return;
-    const int64_t u = idx / per;
-    const int64_t e = idx % per;
-    const float nsl = neg_slope_log2e(slopes, u % heads);
-    const float lc = decay_pow(nsl, (float)chunk);
-    float4* base = reinterpret_cast<float4*>(ws + u * n_chunks * (int64_t)d2) + e;
-    float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
-    base[0] = p;
-    for (int64_t j = 1; j < n_chunks; ++j) {
-        const float4 s = base[j * per];
-        p.x = lc * p.x + s.x;
-        p.y = lc * p.y + s.y;
-        p.z = lc * p.z + s.z;
-        p.w = lc * p.w + s.w;
-        base[j * per] = p;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < bh * per; idx += (int64_t)gridDim.x * 256) {
+        const int64_t u = idx / per;
+        const int64_t e = idx % per;
+        const float nsl = neg_slope_log2e(slopes, u % heads);
+        const float lc = decay_pow(nsl, (float)chunk);
+        float4* base = reinterpret_cast<float4*>(ws + u * n_chunks * (int64_t)d2) + e;
+        float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
+        base[0] = p;
+        for (int64_t j = 1; j < n_chunks; ++j) {
+            const float4 s = base[j * per];
+            p.x = lc * p.x + s.x;
+            p.y = lc * p.y + s.y;
+            p.z = lc * p.z + s.z;
+            p.w = lc * p.w + s.w;
+            base[j * per] = p;
+        }
     }
 }
 
@@ -49,26 +49,26 @@ __global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, cons
                                                   int64_t sub_len, int d2)
 {
     const int64_t per = d2 / 4;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= bh * per) return;
-    const int64_t u = idx / per;
-    const int64_t e = idx % per;
-    const float nsl = neg_slope_log2e(slopes, u % heads);
-    const float ls = decay_pow(nsl, (float)sub_len);
     const int64_t n_sub = (n_chunks - 1) * n_sub_per;
-    const float4* S = reinterpret_cast<const float4*>(sub + u * (n_sub + 1) * (int64_t)d2) + e;
-    float4* P = reinterpret_cast<float4*>(pref + u * n_chunks * (int64_t)d2) + e;
-    float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
-    P[0] = p;
-    for (int64_t j = 1; j < n_chunks; ++j) {
-        for (int64_t f = 0; f < n_sub_per; ++f) {
-            const float4 s = S[((j - 1) * n_sub_per + f + 1) * per];
-            p.x = ls * p.x + s.x;
-            p.y = ls * p.y + s.y;
-            p.z = ls * p.z + s.z;
-            p.w = ls * p.w + s.w;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < bh * per; idx += (int64_t)gridDim.x * 256) {
+        const int64_t u = idx / per;
+        const int64_t e = idx % per;
+        const float nsl = neg_slope_log2e(slopes, u % heads);
+        const float ls = decay_pow(nsl, (float)sub_len);
+        const float4* S = reinterpret_cast<const float4*>(sub + u * (n_sub + 1) * (int64_t)d2) + e;
+        float4* P = reinterpret_cast<float4*>(pref + u * n_chunks * (int64_t)d2) + e;
+        float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
+        P[0] = p;
+        for (int64_t j = 1; j < n_chunks; ++j) {
+            for (int64_t f = 0; f < n_sub_per; ++f) {
+                const float4 s = S[((j - 1) * n_sub_per + f + 1) * per];
+                p.x = ls * p.x + s.x;
+                p.y = ls * p.y + s.y;
+                p.z = ls * p.z + s.z;
+                p.w = ls * p.w + s.w;
+            }
+            P[j * per] = p;
         }
-        P[j * per] = p;
     }
 }
 
@@ -80,36 +80,36 @@ __global__ __launch_bounds__(256) void k_scan_varlen(float* __restrict__ ws, con
                                                      int64_t heads, int64_t chunk, int d2)
 {
     const int64_t per = d2 / 4;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= n_seq * heads * per) return;
-    const int64_t u = idx / per;
-    const int64_t e = idx % per;
-    const int64_t sq = u / heads, h = u % heads;
-    const int64_t c0 = stab[2 * sq], nc = stab[2 * sq + 1];
-    if (nc <= 1) return;
-    const float nsl = neg_slope_log2e(slopes, h);
-    const float lc = decay_pow(nsl, (float)chunk);
     const int64_t step = heads * per;  // float4s between slots (c, h) and (c+1, h)
-    float4* base = reinterpret_cast<float4*>(ws + (c0 * heads + h) * (int64_t)d2) + e;
-    float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
-    base[0] = p;
-    for (int64_t j = 1; j < nc; ++j) {
-        const float4 s = base[j * step];
-        p.x = lc * p.x + s.x;
-        p.y = lc * p.y + s.y;
-        p.z = lc * p.z + s.z;
-        p.w = lc * p.w + s.w;
-        base[j * step] = p;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n_seq * heads * per;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t u = idx / per;
+        const int64_t e = idx % per;
+        const int64_t sq = u / heads, h = u % heads;
+        const int64_t c0 = stab[2 * sq], nc = stab[2 * sq + 1];
+        if (nc <= 1) continue;
+        const float nsl = neg_slope_log2e(slopes, h);
+        const float lc = decay_pow(nsl, (float)chunk);
+        float4* base = reinterpret_cast<float4*>(ws + (c0 * heads + h) * (int64_t)d2) + e;
+        float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
+        base[0] = p;
+        for (int64_t j = 1; j < nc; ++j) {
+            const float4 s = base[j * step];
+            p.x = lc * p.x + s.x;
+            p.y = lc * p.y + s.y;
+            p.z = lc * p.z + s.z;
+            p.w = lc * p.w + s.w;
+            base[j * step] = p;
+        }
     }
 }
 
 __global__ __launch_bounds__(256) void k_state_init(float* __restrict__ kv, const float* __restrict__ kv0,
                                                     int64_t count4)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count4) return;
-    reinterpret_cast<float4*>(kv)[i] =
-        kv0 ? reinterpret_cast<const float4*>(kv0)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count4; i += (int64_t)gridDim.x * 256)
+        reinterpret_cast<float4*>(kv)[i] =
+            kv0 ? reinterpret_cast<const float4*>(kv0)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // Backward-pass state set-up: a state (or its transpose) scaled by exp(power * s_h).
@@ -118,16 +118,24 @@ __global__ __launch_bounds__(256) void k_state_prep(float* __restrict__ dst, con
                                                     int d, int transpose, int power)
 {
     const int64_t d2 = (int64_t)d * d;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= bh * d2) return;
-    const int64_t u = idx / d2, e = idx % d2;
-    float x = 0.f;
-    if (src) {
-        const int64_t r = e / d, c = e % d;
-        x = src[u * d2 + (transpose ? c * d + r : e)];
-        if (power != 0) x *= exp2f(-(float)power * neg_slope_log2e(slopes, u % heads));
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < bh * d2; idx += (int64_t)gridDim.x * 256) {
+        const int64_t u = idx / d2, e = idx % d2;
+        float x = 0.f;
+        if (src) {
+            const int64_t r = e / d, c = e % d;
+            x = src[u * d2 + (transpose ? c * d + r : e)];
+            if (power != 0) x *= exp2f(-(float)power * neg_slope_log2e(slopes, u % heads));
+        }
+        dst[idx] = x;
     }
-    dst[idx] = x;
+}
+
+// Grid of a grid-stride kernel over `items` threads' worth of work (256 per block), capped so the
+// launch stays far inside the 32-bit work-item count of a dispatch.
+dim3 stride_grid(int64_t items)
+{
+    const int64_t blocks = (items + 255) / 256;
+    return dim3((unsigned)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536));
 }
 
 }  // namespace
@@ -136,7 +144,7 @@ hipError_t launch_state_prep(float* dst, const float* src, const float* slopes, 
                              int d, bool transpose, int power, hipStream_t stream)
 {
     const int64_t count = bh * (int64_t)d * d;
-    const dim3 grid((unsigned)((count + 255) / 256)), block(256);
+    const dim3 grid = stride_grid(count), block(256);
     hipLaunchKernelGGL(k_state_prep, grid, block, 0, stream, dst, src, slopes, bh, heads, d, transpose ? 1 : 0,
                        power);
     return hipGetLastError();
@@ -147,7 +155,7 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
 {
     const int d2 = d * d;
     const int64_t threads = bh * (d2 / 4);
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    const dim3 grid = stride_grid(threads), block(256);
     hipLaunchKernelGGL(k_scan, grid, block, 0, stream, ws, kv, slopes, bh, heads, n_chunks, chunk, d2);
     return hipGetLastError();
 }
@@ -158,7 +166,7 @@ hipError_t launch_scan_sub(float* pref, const float* sub, const float* kv, const
 {
     const int d2 = d * d;
     const int64_t threads = bh * (d2 / 4);
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    const dim3 grid = stride_grid(threads), block(256);
     hipLaunchKernelGGL(k_scan_sub, grid, block, 0, stream, pref, sub, kv, slopes, bh, heads, n_chunks, n_sub_per,
                        sub_len, d2);
     return hipGetLastError();
@@ -169,7 +177,7 @@ hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, c
 {
     const int d2 = d * d;
     const int64_t threads = n_seq * heads * (d2 / 4);
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    const dim3 grid = stride_grid(threads), block(256);
     hipLaunchKernelGGL(k_scan_varlen, grid, block, 0, stream, ws, kv, slopes, stab, n_seq, heads, chunk, d2);
     return hipGetLastError();
 }
@@ -177,7 +185,7 @@ hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, c
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream)
 {
     const int64_t count4 = count / 4;  // count = B*H*d*d, a multiple of 4096
-    const dim3 grid((unsigned)((count4 + 255) / 256)), block(256);
+    const dim3 grid = stride_grid(count4), block(256);
     hipLaunchKernelGGL(k_state_init, grid, block, 0, stream, kv, kv0, count4);
     return hipGetLastError();
 }

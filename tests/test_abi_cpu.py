@@ -58,6 +58,8 @@ def test_prefill_validation_codes():
     assert _prefill(sn=100) == la.LA_ERR_INVALID_ARGUMENT           # not a 16-byte multiple
     assert _prefill(sn=64) == la.LA_ERR_INVALID_ARGUMENT            # stride_n < d
     assert _prefill(sn=(1 << 22) + 8) == la.LA_ERR_UNSUPPORTED      # 32-bit tile offsets
+    assert _prefill(B=1 << 10, H=(1 << 10) + 1) == la.LA_ERR_UNSUPPORTED   # > 2^20 (batch, head) pairs
+    assert _prefill(N=1 << 30, chunk=64) == la.LA_ERR_UNSUPPORTED          # > 2^20 (head, chunk) items
     assert _prefill(q=ctypes.c_void_p((1 << 20) + 2)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned
     assert _prefill(ckpt=FAKE, ckpt_every=100) == la.LA_ERR_UNSUPPORTED
     assert _prefill(ckpt=FAKE, ckpt_every=0) == la.LA_ERR_UNSUPPORTED
@@ -84,6 +86,8 @@ def test_decode_and_state_init_validation():
     assert L.la_decode(la.LA_BF16, None, FAKE, FAKE, FAKE, 2, 2, 128, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARGUMENT
     assert L.la_decode(la.LA_BF16, FAKE, FAKE, FAKE, FAKE, 2, 2, 96, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
     assert L.la_decode(la.LA_F32, FAKE, FAKE, FAKE, FAKE, 0, 2, 64, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARGUMENT
+    # one launch covers at most 2^20 (batch, head) pairs
+    assert L.la_decode(la.LA_F32, FAKE, FAKE, FAKE, FAKE, (1 << 19) + 1, 2, 64, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
     assert L.la_state_init(None, None, 1, 1, 128, None) == la.LA_ERR_INVALID_ARGUMENT
     assert L.la_state_init(FAKE, None, 1, 1, 32, None) == la.LA_ERR_UNSUPPORTED
 
@@ -162,6 +166,7 @@ def test_varlen_validation_codes():
     assert _varlen([10, 20], d=64, sh=64, sn=512, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE  # bf16 d = 64: valid
     assert _varlen([10, 20], sn=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], sn=(1 << 22) + 8) == la.LA_ERR_UNSUPPORTED
+    assert _varlen([1 << 30, 20], chunk=64) == la.LA_ERR_UNSUPPORTED        # > 2^20 (chunk, head) items
     assert _varlen([10, 20], chunk=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
     assert _varlen([10, 20], ws_bytes=8) == la.LA_ERR_WORKSPACE
