@@ -272,10 +272,14 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         }
         R.v = buf_load16(rv, row_off(tile, st_id >> 2) + 16u * (st_id & 3));
     };
-    // Decay weights of a full tile, computed once: lambda^(BK-1-r) for the V row r this lane
-    // stages and lambda^BK for the state; only a ragged last tile computes its own.
+    // Decay weights, computed once: lambda^(L-1-r) for the V row r this lane stages (0 past the
+    // tile's end) and lambda^L for the state, for a full tile and for the last tile, the only one
+    // that can be shorter.
+    const int L_last = tile_len(n_tiles - 1);
     const float wt_full = decay_pow(nsl, (float)(BK - 1 - (st_id >> 2)));
     const float dl_full = decay_pow(nsl, (float)BK);
+    const float wt_last = ((st_id >> 2) < L_last) ? decay_pow(nsl, (float)(L_last - 1 - (st_id >> 2))) : 0.f;
+    const float dl_last = decay_pow(nsl, (float)L_last);
     // K and V rows into LDS buffer `buf`, with the decay-weighted V as bf16 hi + lo.
     auto stage_tile = [&](const KVRegs& R, int buf, int tile) __attribute__((always_inline)) {
         const int L = tile_len(tile);
@@ -287,8 +291,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
         const uint4 vx = silu_v ? silu8(R.v) : R.v;
         *reinterpret_cast<uint4*>(&sV[buf][off]) = vx;
-        float wt = wt_full;
-        if (L != BK) wt = (r < L) ? decay_pow(nsl, (float)(L - 1 - r)) : 0.f;
+        const float wt = (L == BK) ? wt_full : wt_last;
         const uint32_t in[4] = {vx.x, vx.y, vx.z, vx.w};
         uint32_t hi[4], lo[4];
 #pragma unroll
@@ -333,8 +336,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     // KV <- lambda^L KV + K^T (W V) on this wave's state tiles
     auto update_state = [&](auto swc, f32x4* st, int buf, int tile) __attribute__((always_inline)) {
         constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
-        const int L = tile_len(tile);
-        const float dl = (L == BK) ? dl_full : decay_pow(nsl, (float)L);
+        const float dl = (tile_len(tile) == BK) ? dl_full : dl_last;
 #pragma unroll
         for (int k = 0; k < C; ++k) st[k] *= dl;
         // key-row tiles it0..it1 cover this wave's state tiles; the two value-column tiles of one
@@ -651,17 +653,25 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
             R.v[m] = buf_load16(rv, row_off(tile, c >> 4) + 16u * (c & 15));
         }
     };
-    // full-tile decay weights, computed once (rows tid/16 and 32 + tid/16; lambda^BK)
-    const float wt_full[2] = {decay_pow(nsl, (float)(BK - 1 - (tid >> 4))), decay_pow(nsl, (float)(BK - 33 - (tid >> 4)))};
+    // decay weights of a full tile and of the last tile (the only one that can be shorter),
+    // computed once: rows tid/16 and 32 + tid/16 of W, and lambda^L
+    const int L_last = tile_len(n_tiles - 1);
+    float wt_full[2], wt_last[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int r = (tid >> 4) + 32 * m;
+        wt_full[m] = decay_pow(nsl, (float)(BK - 1 - r));
+        wt_last[m] = (r < L_last) ? decay_pow(nsl, (float)(L_last - 1 - r)) : 0.f;
+    }
     const float dl_full = decay_pow(nsl, (float)BK);
+    const float dl_last = decay_pow(nsl, (float)L_last);
     auto stage = [&](const SumRegs& R, int buf, int tile) __attribute__((always_inline)) {
         const int L = tile_len(tile);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int c = tid + 512 * m, r = c >> 4, off = r * KS + 8 * (c & 15);
             *reinterpret_cast<uint4*>(&sK[buf][off]) = R.k[m];
-            float wt = wt_full[m];
-            if (L != BK) wt = (r < L) ? decay_pow(nsl, (float)(L - 1 - r)) : 0.f;
+            const float wt = (L == BK) ? wt_full[m] : wt_last[m];
             const uint32_t in[4] = {R.v[m].x, R.v[m].y, R.v[m].z, R.v[m].w};
             uint32_t hi[4], lo[4];
 #pragma unroll
@@ -675,8 +685,7 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     for (int k = 0; k < 8; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     // S <- lambda^L S + K^T (W V) on this wave's 4 x 2 state tiles (k = token within the tile)
     auto update = [&](int buf, int tile) __attribute__((always_inline)) {
-        const int L = tile_len(tile);
-        const float dl = (L == BK) ? dl_full : decay_pow(nsl, (float)L);
+        const float dl = (tile_len(tile) == BK) ? dl_full : dl_last;
 #pragma unroll
         for (int k = 0; k < 8; ++k) st[k] *= dl;
 #pragma unroll
