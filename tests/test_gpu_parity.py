@@ -171,6 +171,23 @@ def test_checkpoints(device, dtype, d):
     check_prefill(31, 1, 2, 2048, d, dtype, SL2, device, ckpt_every=512, chunk_tokens=1024)
 
 
+@pytest.mark.parametrize("ckpt_every,chunk", [(64, 320), (192, 1088), (320, 0)])
+@pytest.mark.parametrize("slopes", [(2.0 ** -2, 2.0 ** -8), (0.9, 0.3)])
+def test_bf16_checkpoints_tile_parities(device, ckpt_every, chunk, slopes):
+    # checkpoints after even and odd tiles of chunks that start on odd tiles, ragged last chunk;
+    # slow decays (the state waves' paired scaling) and fast ones (per-tile scaling)
+    check_prefill(37, 1, 2, 2000, 128, "bf16", np.array(slopes, np.float32), device, ckpt_every=ckpt_every,
+                  chunk_tokens=chunk)
+
+
+@pytest.mark.parametrize("N", [64, 128, 130, 192, 200])
+@pytest.mark.parametrize("slopes", [(2.0 ** -2, 2.0 ** -8), (0.9, 0.3)])
+def test_bf16_tile_count_parities(device, N, slopes):
+    # one to four tiles: the final state after an even or an odd last tile, full or short
+    kv0 = np.random.default_rng(N).standard_normal((1, 2, 128, 128)).astype(np.float32)
+    check_prefill(38, 1, 2, N, 128, "bf16", np.array(slopes, np.float32), device, kv_in=kv0)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_state_only(device, dtype):
     exact, raw = inputs(32, 1, 2, 3000, 128, dtype)
