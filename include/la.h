@@ -132,8 +132,8 @@ size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int6
  *                ckpt_every must be a positive multiple of 64.
  *   workspace  : device scratch of at least la_prefill_workspace_size() bytes
  *                (may be NULL when that size is 0); contents are clobbered.
- * Supported: d in {64, 128} for both dtypes (bfloat16 at d = 128 runs on the
- * MFMA kernels, every other case on the float32-arithmetic tile kernel);
+ * Supported: d in {64, 128} for both dtypes (bfloat16 runs on the MFMA
+ * kernels, float32 on the float32-arithmetic tile kernel);
  * batch*heads <= 2^20, and batch*heads*chunks <= 2^20 for the chunk count the
  * plan (or chunk_tokens) gives, else LA_ERR_UNSUPPORTED.
  * n == 0 is a no-op that leaves kv unchanged.

@@ -182,18 +182,18 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     a.rev = rev ? 1 : 0;
     const int64_t bh = batch * heads;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool mfma = dt == LA_BF16 && d == 128;  // the bf16 MFMA kernels; else the VALU tile kernel
+    const bool mfma = dt == LA_BF16;  // the bf16 MFMA kernels; float32 runs on the VALU tile kernel
 
     auto run = [&](int mode, int64_t chunks) -> hipError_t {
         FwdArgs b = a;
         b.chunks_launched = chunks;
         b.groups = bh * chunks;
-        return mfma ? launch_fwd_bf16(b, mode, st) : launch_fwd_vec(dt, b, (int)d, mode, st);
+        return mfma ? launch_fwd_bf16(b, (int)d, mode, st) : launch_fwd_f32(b, (int)d, mode, st);
     };
 
-    // chunk summaries: full width (one workgroup per chunk-head) for plain bf16, else the sliced
-    // tile kernel in its summary mode
-    const bool full_width = mfma && a.act == 0;
+    // chunk summaries: full width (one workgroup per chunk-head) for plain bf16 at d = 128, else the
+    // sliced tile kernel in its summary mode
+    const bool full_width = mfma && d == 128 && a.act == 0;
     if (p.n_chunks > 1 && p.sub == 1) {
         FwdArgs b = a;
         b.chunks_launched = p.n_chunks - 1;
@@ -215,8 +215,8 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
         b.chunks_launched = n_sub;
         b.groups = bh * n_sub;
         s = launch_status(full_width ? launch_summary_bf16(b, st)
-                                     : mfma ? launch_fwd_bf16(b, kModeLocal, st)
-                                                     : launch_fwd_vec(dt, b, (int)d, kModeLocal, st),
+                                     : mfma ? launch_fwd_bf16(b, (int)d, kModeLocal, st)
+                                            : launch_fwd_f32(b, (int)d, kModeLocal, st),
                           "chunk-summary launch");
         if (s != LA_OK) return s;
         s = launch_status(launch_scan_sub(a.ws, b.ws, kv, slopes, bh, heads, p.n_chunks, p.sub, b.chunk, (int)d, st),
@@ -428,7 +428,7 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     a.groups = p.total_chunks * heads;
     a.rev = rev ? 1 : 0;
     auto run = [&](int mode) -> hipError_t {
-        return (dt == LA_BF16 && d == 128) ? launch_fwd_bf16(a, mode, st) : launch_fwd_vec(dt, a, (int)d, mode, st);
+        return dt == LA_BF16 ? launch_fwd_bf16(a, (int)d, mode, st) : launch_fwd_f32(a, (int)d, mode, st);
     };
     if (p.n_short > 0) {
         const int64_t* rtab = a.stab + 2 * n_seq;

@@ -138,9 +138,9 @@ __device__ inline Work decode_work(const FwdArgs& a, int64_t group)
 }
 
 // Launchers (each returns the hipError_t of its launch).
-// The VALU tile kernel: float32 at d = 64 / 128, bfloat16 at d = 64.
-hipError_t launch_fwd_vec(la_dtype dt, const FwdArgs& a, int d, int mode, hipStream_t stream);
-hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream);
+// The float32 tile kernel (VALU arithmetic, d = 64 or 128).
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mode, hipStream_t stream);
 // Chunk summaries (kModeLocal semantics) at full width, one workgroup per group of `a` (no value
 // slices); bf16 without the SiLU prologue.
 hipError_t launch_summary_bf16(const FwdArgs& a, hipStream_t stream);

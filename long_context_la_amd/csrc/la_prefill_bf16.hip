@@ -1,4 +1,4 @@
-// bfloat16 prefill on gfx950 matrix cores (d = 128).
+// bfloat16 prefill on gfx950 matrix cores (d = 128 and d = 64).
 //
 // Page "MiniMax-01: Scaling Foundation Models with Lightning Attention |
 // Summary", section 2.2: tiles of the sequence get an intra-tile masked term
@@ -74,12 +74,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int D = 128, BK = kBlock, SW = kSliceW;
-constexpr int KS = D + 16;  // row stride (elements) of the row-major K tile: 288 B, so the 4 rows of a
-                            // transposing read fall in disjoint banks
+constexpr int BK = kBlock, SW = kSliceW;
+// Row stride (elements) of the row-major K tile of head dimension D: 288 B at d = 128 and 160 B at
+// d = 64, so the 4 rows of a transposing read fall in disjoint banks.
+template <int D> constexpr int kKS = D + 16;
 constexpr int VS = SW + 16;  // row stride of the V, W V tiles: 96 B (same reason)
-constexpr int SS = D;       // row stride of the state copies (stored KV^T: [value col][key row]); the
-                            // 16-byte chunk index is XORed with row % 16 (see ss_off)
 constexpr int OS = SW + 16;  // row stride of the output staging tile: 96 B, so that 16 rows x 32 B of
                              // 8-byte writes and 16 rows x 64 B of 16-byte reads spread evenly over
                              // the banks
@@ -89,12 +88,14 @@ __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_fl
 __device__ __forceinline__ float hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// Element offset of (row, col) in a state copy: unpadded 256-byte rows whose 16-byte chunks are
-// permuted by row % 16, so that 16 lanes reading one chunk position of 16 rows (operand reads) or
-// writing 8-byte halves of 16 rows (state publication) touch 16 different chunks of the bank space.
+// Element offset of (row, col) in a state copy (stored KV^T: [value col][key row]): unpadded rows of
+// D elements whose 16-byte chunks are permuted by the row index (modulo the D/8 chunks of a row), so
+// that 16 lanes reading one chunk position of 16 rows (operand reads) or writing 8-byte halves of
+// 16 rows (state publication) spread over the bank space.
+template <int D>
 __device__ __forceinline__ int ss_off(int row, int col)
 {
-    return row * SS + ((((col >> 3) ^ row) & 15) << 3) + (col & 7);
+    return row * D + ((((col >> 3) ^ row) & (D / 8 - 1)) << 3) + (col & 7);
 }
 
 // Two floats -> packed bf16 pair (round to nearest even).
@@ -175,25 +176,33 @@ template <int N> struct IntC { static constexpr int value = N; };
 // The four value slices of a head read the same Q and K rows at nearly the same time; each slice
 // walks the 64-byte column blocks (Q) and 16-row blocks (K) starting at its own index, so that the
 // simultaneous requests of sibling slices fall on different cache lines.
-struct QRegs { uint4 q[4]; };            // Q fragments: row 16w + lane%16, features 32((ks+slice)%4) + 8g .. +7
-struct KVRegs { uint4 k[4]; uint4 v; };  // K chunks st_id + 256m of the 64x128 tile; V slice row st_id/4
+// Q fragments: row 16w + lane%16, features 32((ks+slice)%(D/32)) + 8g .. +7
+template <int D> struct QRegs { uint4 q[D / 32]; };
+// K chunks st_id + 256m of the 64 x D tile; V slice row st_id/4
+template <int D> struct KVRegs { uint4 k[D / 32]; uint4 v; };
 
 // REV walks each sequence from its last token to its first (token index t of the recurrence is
 // memory row n-1-t), the order of the reverse state recurrence of the backward pass.  ACT enables
 // the SiLU prologue (which of q, k, v is chosen at run time); without it no activation code is
 // compiled in, since untaken branches inside the tile loops still cost about 10% here.
-template <int MODE, bool GATE, bool REV, bool ACT>
+template <int MODE, bool GATE, bool REV, bool ACT, int D>
 __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
     static_assert(!(GATE && REV), "the reverse walk has no epilogue");
+    static_assert(D == 64 || D == 128, "head dimension 64 or 128");
     constexpr bool OUT = MODE == kModeOut;
+    constexpr int KS = kKS<D>;
+    constexpr int NQ = D / 32;   // 32-feature steps of a score or inter product; also Q, K loads per lane
+    constexpr int CPR = D / 8, CPR_LOG = D == 128 ? 4 : 3;  // 16-byte chunks per row of Q or K
+    using QR = QRegs<D>;
+    using KR = KVRegs<D>;
     constexpr int SW0 = OUT ? 4 : 0;  // first state wave
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sV[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sVWh[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sVWl[2][BK * VS];
-    __shared__ __attribute__((aligned(16))) u16 sSh[2][SW * SS];
-    __shared__ __attribute__((aligned(16))) u16 sSl[2][SW * SS];
+    __shared__ __attribute__((aligned(16))) u16 sSh[2][SW * D];
+    __shared__ __attribute__((aligned(16))) u16 sSl[2][SW * D];
     __shared__ __attribute__((aligned(16))) u16 sO[BK * OS];
 
     int64_t group;
@@ -256,19 +265,26 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 
     // ------------------------------------------------------------------ state waves
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
-    // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..) of state wave sw:
-    // [first, first + count), split 6/5/3/2 with outputs (to balance the SIMDs), 4 each without.
-    auto st_first = [](int sw) constexpr { return OUT ? (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14) : 4 * sw; };
-    auto st_count = [](int sw) constexpr { return OUT ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : 4; };
+    // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), D/8 of them, of state
+    // wave sw: [first, first + count).  With outputs the split evens out the MFMAs per SIMD (output
+    // wave w + state wave w): 6/5/3/2 of 16 at d = 128, 3/3/1/1 of 8 at d = 64; equal shares without.
+    auto st_first = [](int sw) constexpr {
+        if (!OUT) return (D / 32) * sw;
+        return D == 128 ? (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14) : (sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7);
+    };
+    auto st_count = [](int sw) constexpr {
+        if (!OUT) return D / 32;
+        return D == 128 ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : (sw <= 1 ? 3 : 1);
+    };
 
-    auto load_kv = [&](KVRegs& R, int tile) __attribute__((always_inline)) {
+    auto load_kv = [&](KR& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_row0(tile);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, tile_bytes(tile));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, tile_bytes(tile));
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int c = st_id + 256 * ((m + slice) & 3);
-            R.k[m] = buf_load16(rk, row_off(tile, c >> 4) + 16u * (c & 15));
+        for (int m = 0; m < NQ; ++m) {
+            const int c = st_id + 256 * ((m + slice) & (NQ - 1));
+            R.k[m] = buf_load16(rk, row_off(tile, c >> CPR_LOG) + 16u * (c & (CPR - 1)));
         }
         R.v = buf_load16(rv, row_off(tile, st_id >> 2) + 16u * (st_id & 3));
     };
@@ -281,12 +297,12 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const float wt_last = ((st_id >> 2) < L_last) ? decay_pow(nsl, (float)(L_last - 1 - (st_id >> 2))) : 0.f;
     const float dl_last = decay_pow(nsl, (float)L_last);
     // K and V rows into LDS buffer `buf`, with the decay-weighted V as bf16 hi + lo.
-    auto stage_tile = [&](const KVRegs& R, int buf, int tile) __attribute__((always_inline)) {
+    auto stage_tile = [&](const KR& R, int buf, int tile) __attribute__((always_inline)) {
         const int L = tile_len(tile);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int c = st_id + 256 * ((m + slice) & 3);
-            *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + 8 * (c & 15)]) = silu_k ? silu8(R.k[m]) : R.k[m];
+        for (int m = 0; m < NQ; ++m) {
+            const int c = st_id + 256 * ((m + slice) & (NQ - 1));
+            *reinterpret_cast<uint4*>(&sK[buf][(c >> CPR_LOG) * KS + 8 * (c & (CPR - 1))]) = silu_k ? silu8(R.k[m]) : R.k[m];
         }
         const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
         const uint4 vx = silu_v ? silu8(R.v) : R.v;
@@ -308,7 +324,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             uint32_t h01, l01, h23, l23;
             split2(st[k][0], st[k][1], h01, l01);
             split2(st[k][2], st[k][3], h23, l23);
-            const int off = ss_off(16 * (q & 1) + lr, 16 * (q >> 1) + 4 * g);
+            const int off = ss_off<D>(16 * (q & 1) + lr, 16 * (q >> 1) + 4 * g);
             *reinterpret_cast<uint2*>(&sSh[buf][off]) = make_uint2(h01, h23);
             *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(l01, l23);
         }
@@ -383,20 +399,20 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
         drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
-    auto load_q = [&](QRegs& R, int tile) __attribute__((always_inline)) {
+    auto load_q = [&](QR& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_row0(tile);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, tile_bytes(tile));
         const uint32_t off = row_off(tile, 16 * w + lr) + 16u * g;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ((ks + slice) & 3));
+        for (int ks = 0; ks < NQ; ++ks) R.q[ks] = buf_load16(rq, off + 64u * ((ks + slice) & (NQ - 1)));
     };
     // Outputs of tile `tile` from LDS buffer `buf`; R.q is refilled with tile next_q once consumed.
-    auto compute_out = [&](auto wc, QRegs& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
+    auto compute_out = [&](auto wc, QR& R, int buf, int tile, int next_q) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
         const int64_t t0 = tile_row0(tile);
-        bf16x8 qf[4];
+        bf16x8 qf[NQ];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, silu_q ? silu8(R.q[ks]) : R.q[ks]);
+        for (int ks = 0; ks < NQ; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, silu_q ? silu8(R.q[ks]) : R.q[ks]);
         // the gate values of this lane's outputs (row 16W + lr, columns 16jt + 4g..+3), read early
         // so the loads are long done when the products are
         uint2 gx[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
@@ -409,20 +425,20 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // Issue every LDS operand read of the inter and score products up front (the fence keeps
         // the scheduler from sinking them next to their MFMAs, which would expose each read's
         // latency in turn).
-        bf16x8 sh[2][4], sl[2][4], kop[W + 1][4];
+        bf16x8 sh[2][NQ], sl[2][NQ], kop[W + 1][NQ];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int off = ss_off(16 * jt + lr, 32 * ((ks + slice) & 3) + 8 * g);
+            for (int ks = 0; ks < NQ; ++ks) {
+                const int off = ss_off<D>(16 * jt + lr, 32 * ((ks + slice) & (NQ - 1)) + 8 * g);
                 sh[jt][ks] = lds8(&sSh[buf][off]);
                 sl[jt][ks] = lds8(&sSl[buf][off]);
             }
 #pragma unroll
         for (int ct = 0; ct <= W; ++ct)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                kop[ct][ks] = lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ((ks + slice) & 3) + 8 * g]);
+            for (int ks = 0; ks < NQ; ++ks)
+                kop[ct][ks] = lds8(&sK[buf][(16 * ct + lr) * KS + 32 * ((ks + slice) & (NQ - 1)) + 8 * g]);
         __builtin_amdgcn_sched_barrier(0);
         // inter-tile term, transposed: (Q KV)^T = KV^T Q^T, so a lane's accumulators hold one output
         // row (query lr) and four consecutive value columns 16jt + 4g..+3; rows scaled by lambda^(r+1)
@@ -431,7 +447,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int jt = 0; jt < 2; ++jt) {
             acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < NQ; ++ks) {
                 acc[jt] = mfma(sh[jt][ks], qf[ks], acc[jt]);
                 acc[jt] = mfma(sl[jt][ks], qf[ks], acc[jt]);
             }
@@ -443,7 +459,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             if (ct <= W) {
                 f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) s = mfma(kop[ct][ks], qf[ks], s);
+                for (int ks = 0; ks < NQ; ++ks) s = mfma(kop[ct][ks], qf[ks], s);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) p[ct][t] = s[t] * dmask[ct][t];
             } else {
@@ -512,7 +528,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const float* src = nullptr;
         if (MODE != kModeLocal) src = (wk.nck > 1) ? a.ws + wk.slot_in * d2 : a.kv + u * d2;
         load_state(swc, st, src);
-        KVRegs RA, RB;
+        KR RA, RB;
         load_kv(RA, 0);
         __builtin_amdgcn_sched_barrier(0);
         load_kv(RB, 1);
@@ -529,7 +545,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         int ck_phase = a.ckpt ? (int)((t_begin / BK) % ck_tiles) : 0;
         int64_t ck_slot = a.ckpt ? t_begin / a.ckpt_every : 0;
         __syncthreads();
-        auto step = [&](KVRegs& R, KVRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
+        auto step = [&](KR& R, KR& Rn, int buf, int tile) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
             load_kv(R, tile + 2);
             __builtin_amdgcn_sched_barrier(0);
@@ -557,7 +573,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         else if (j == wk.nck - 1) store_state(swc, st, a.kv + u * d2);
     };
     auto out_loop = [&](auto wc) __attribute__((always_inline)) {
-        QRegs QA, QB;
+        QR QA, QB;
         load_q(QA, 0);
         __builtin_amdgcn_sched_barrier(0);
         load_q(QB, 1);
@@ -600,6 +616,7 @@ struct SumRegs { uint4 k[2]; uint4 v[2]; };  // 16-byte chunks tid and tid + 512
 template <bool REV>
 __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
 {
+    constexpr int D = 128, KS = kKS<D>;  // (d = 128 only: at d = 64 the sliced summaries serve)
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sWh[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sWl[2][BK * KS];
@@ -746,25 +763,32 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
                 dst[(16 * (it0 + i) + 4 * g + t) * D + 16 * (jt0 + j) + lr] = st[2 * i + j][t];
 }
 
-template <bool GATE, bool REV, bool ACT>
+template <bool GATE, bool REV, bool ACT, int D>
 void launch_mode(const FwdArgs& a, int mode, dim3 grid, hipStream_t stream)
 {
-    if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT>), grid, dim3(512), 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT>), grid, dim3(256), 0, stream, a);
+    if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT, D>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT, D>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT, D>), grid, dim3(256), 0, stream, a);
+}
+
+template <int D>
+void launch_d(const FwdArgs& a, int mode, hipStream_t stream)
+{
+    const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
+    const bool gate = a.gate && mode == kModeOut, act = a.act != 0;
+    if (a.rev) launch_mode<false, true, false, D>(a, mode, grid, stream);  // the backward pass: plain inputs
+    else if (gate && act) launch_mode<true, false, true, D>(a, mode, grid, stream);
+    else if (gate) launch_mode<true, false, false, D>(a, mode, grid, stream);
+    else if (act) launch_mode<false, false, true, D>(a, mode, grid, stream);
+    else launch_mode<false, false, false, D>(a, mode, grid, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int mode, hipStream_t stream)
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mode, hipStream_t stream)
 {
-    const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
-    const bool gate = a.gate && mode == kModeOut, act = a.act != 0;
-    if (a.rev) launch_mode<false, true, false>(a, mode, grid, stream);  // the backward pass: plain inputs
-    else if (gate && act) launch_mode<true, false, true>(a, mode, grid, stream);
-    else if (gate) launch_mode<true, false, false>(a, mode, grid, stream);
-    else if (act) launch_mode<false, false, true>(a, mode, grid, stream);
-    else launch_mode<false, false, false>(a, mode, grid, stream);
+    if (d == 128) launch_d<128>(a, mode, stream);
+    else launch_d<64>(a, mode, stream);
     return hipGetLastError();
 }
 

@@ -11,30 +11,14 @@
 // slice): the state's columns and the outputs' columns split cleanly by value
 // column, so slices need no communication.  Everything is float32 FMAs on
 // LDS tiles; this path favours plain, checkable arithmetic over speed (the
-// bfloat16 MFMA kernel is the fast one).  T is the element type of q, k, v, o:
-// float, or bfloat16 for d = 64 (the MFMA kernel covers bfloat16 at d = 128).
+// bfloat16 path is the fast one).
 #include "la_common.h"
 
 namespace la {
 namespace {
 
-__device__ inline float ld1(const float* p) { return *p; }
-__device__ inline float ld1(const __bf16* p) { return (float)*p; }
-__device__ inline float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ inline float4 ld4(const __bf16* p)
-{
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                       __uint_as_float(u.y & 0xffff0000u));
-}
-__device__ inline void st1(float* p, float x) { *p = x; }
-__device__ inline void st1(__bf16* p, float x) { *p = (__bf16)x; }
-// SiLU of an input; a bfloat16 activation is stored as bfloat16, so the value is rounded to it
-__device__ inline float act(float x, float) { return silu_f32(x); }
-__device__ inline float act(float x, __bf16) { return (float)(__bf16)silu_f32(x); }
-
-template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void k_fwd_vec(FwdArgs a)
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
 {
     constexpr int BK = kBlock, SW = kSliceW;
     constexpr int RPT = D / 8;  // state rows per thread (thread owns column tid%32, rows tid/32 + 8m)
@@ -58,10 +42,10 @@ __global__ __launch_bounds__(256) void k_fwd_vec(FwdArgs a)
     const int row0 = tid / SW;
     const float nsl = neg_slope_log2e(a.slopes, h);
     const int64_t base = wk.base;
-    const T* Q = static_cast<const T*>(a.q) + base;
-    const T* K = static_cast<const T*>(a.k) + base;
-    const T* V = static_cast<const T*>(a.v) + base;
-    T* O = static_cast<T*>(a.o) + base;
+    const float* Q = static_cast<const float*>(a.q) + base;
+    const float* K = static_cast<const float*>(a.k) + base;
+    const float* V = static_cast<const float*>(a.v) + base;
+    float* O = static_cast<float*>(a.o) + base;
     const int64_t d2 = (int64_t)D * D;
     // memory row of token t of the recurrence: t, or n-1-t when the sequence is walked backwards
     // (the reverse state recurrence of the backward pass)
@@ -83,19 +67,18 @@ __global__ __launch_bounds__(256) void k_fwd_vec(FwdArgs a)
             const int r = e / (D / 4), c4 = e % (D / 4);
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), qx = kx;
             if (r < L) {
-                kx = ld4(K + mrow(t0 + r) * a.sn + 4 * c4);
-                if (MODE == kModeOut) qx = ld4(Q + mrow(t0 + r) * a.sn + 4 * c4);
-                const T tag{};
-                if (a.act & LA_SILU_K) kx = make_float4(act(kx.x, tag), act(kx.y, tag), act(kx.z, tag), act(kx.w, tag));
-                if (a.act & LA_SILU_Q) qx = make_float4(act(qx.x, tag), act(qx.y, tag), act(qx.z, tag), act(qx.w, tag));
+                kx = *reinterpret_cast<const float4*>(K + mrow(t0 + r) * a.sn + 4 * c4);
+                if (MODE == kModeOut) qx = *reinterpret_cast<const float4*>(Q + mrow(t0 + r) * a.sn + 4 * c4);
+                if (a.act & LA_SILU_K) kx = make_float4(silu_f32(kx.x), silu_f32(kx.y), silu_f32(kx.z), silu_f32(kx.w));
+                if (a.act & LA_SILU_Q) qx = make_float4(silu_f32(qx.x), silu_f32(qx.y), silu_f32(qx.z), silu_f32(qx.w));
             }
             sK[r][4 * c4] = kx.x; sK[r][4 * c4 + 1] = kx.y; sK[r][4 * c4 + 2] = kx.z; sK[r][4 * c4 + 3] = kx.w;
             sQ[r][4 * c4] = qx.x; sQ[r][4 * c4 + 1] = qx.y; sQ[r][4 * c4 + 2] = qx.z; sQ[r][4 * c4 + 3] = qx.w;
         }
         for (int e = tid; e < BK * SW; e += 256) {
             const int r = e / SW, c = e % SW;
-            const float x = (r < L) ? ld1(V + mrow(t0 + r) * a.sn + slice * SW + c) : 0.f;
-            sV[r][c] = (a.act & LA_SILU_V) ? act(x, T{}) : x;
+            const float x = (r < L) ? V[mrow(t0 + r) * a.sn + slice * SW + c] : 0.f;
+            sV[r][c] = (a.act & LA_SILU_V) ? silu_f32(x) : x;
         }
         if (tid < BK) sW[tid] = (tid < L) ? decay_pow(nsl, (float)(L - 1 - tid)) : 0.f;
         __syncthreads();
@@ -120,8 +103,8 @@ __global__ __launch_bounds__(256) void k_fwd_vec(FwdArgs a)
                 for (int i = 0; i < D; ++i) inter += sQ[r][i] * sKV[i][col];
                 float acc = decay_pow(nsl, (float)(r + 1)) * inter;
                 for (int c = 0; c <= r; ++c) acc += sP[r][c] * sV[c][col];
-                if (a.gate) acc *= sigmoid_f32(ld1(static_cast<const T*>(a.gate) + base + mrow(t0 + r) * a.sn + slice * SW + col));
-                st1(O + mrow(t0 + r) * a.sn + slice * SW + col, acc);
+                if (a.gate) acc *= sigmoid_f32(static_cast<const float*>(a.gate)[base + mrow(t0 + r) * a.sn + slice * SW + col]);
+                O[mrow(t0 + r) * a.sn + slice * SW + col] = acc;
             }
         }
 
@@ -157,22 +140,21 @@ __global__ __launch_bounds__(256) void k_fwd_vec(FwdArgs a)
     }
 }
 
-template <typename T, int D>
+template <int D>
 hipError_t launch_d(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices)), block(256);
-    if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_vec<T, D, kModeOut>), grid, block, 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_vec<T, D, kModeState>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_fwd_vec<T, D, kModeLocal>), grid, block, 0, stream, a);
+    if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_f32<D, kModeOut>), grid, block, 0, stream, a);
+    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_f32<D, kModeState>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_f32<D, kModeLocal>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_vec(la_dtype dt, const FwdArgs& a, int d, int mode, hipStream_t stream)
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream)
 {
-    if (dt == LA_BF16) return launch_d<__bf16, 64>(a, mode, stream);  // d = 128 has the MFMA kernel
-    return d == 128 ? launch_d<float, 128>(a, mode, stream) : launch_d<float, 64>(a, mode, stream);
+    return d == 128 ? launch_d<128>(a, mode, stream) : launch_d<64>(a, mode, stream);
 }
 
 }  // namespace la
