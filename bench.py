@@ -452,7 +452,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the informational share (8 x 32K) and long (8 x 1M) prefill legs")
+                    help="skip the informational share (8 x 32K), long (8 x 1M) and d = 64 full-layer prefill legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
@@ -510,7 +510,7 @@ def main():
         result["backward"] = backward
     if args.workload == "full" and not args.no_other_workloads:
         others = {}
-        for name, steps in (("share", 20), ("long", 3)):
+        for name, steps in (("share", 20), ("long", 3), ("full_d64", 20)):
             wo = synth.WORKLOADS[name]
             ms_o, kms_o, nch_o, _, _ = time_prefill(wo, steps, 1, device, with_backward=False, with_varlen=False)
             th = wo.batch * wo.heads * wo.n
@@ -518,7 +518,7 @@ def main():
             others[name] = {"workload": f"batch {wo.batch}, {wo.heads} heads, d={wo.d}, N={wo.n}, bf16, "
                                         f"{nch_o} chunks (LASP+ summaries + prefix combine)",
                             "ms_per_step": ms_o, "kernel_ms": kms_o, "tokens_per_s": wo.batch * wo.n / (ms_o * 1e-3),
-                            "hbm_frac": BYTES_PER_TOKEN_HEAD * th / (kms_o * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "hbm_frac": 4 * wo.d * 2 * th / (kms_o * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             "mfma_frac": model_flops_per_token_head(wo.d) * th / (ms_o * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         result["other_workloads"] = others
     if not args.no_decode:

@@ -134,6 +134,7 @@ WORKLOADS = {
     "tiny": Workload("tiny", 1, 2, 512, 64, "f32", 1, "alibi_heads", extra={"block": 64}),
     "share": Workload("share", 1, 8, 32768, 128, "bf16", 2, "alibi_heads", extra={"block": 256}),
     "full": Workload("full", 1, 64, 131072, 128, "bf16", 3, "alibi_64"),
+    "full_d64": Workload("full_d64", 1, 64, 131072, 64, "bf16", 3, "alibi_64"),  # the same at d = 64
     "long": Workload("long", 1, 8, 1048576, 128, "bf16", 4, "alibi_heads", ckpt_every=65536),
     "decode": Workload("decode", 128, 64, 4096, 128, "bf16", 5, "alibi_64", decode_steps=1000),
 }

@@ -1,7 +1,8 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times.
 
 * share  (1 x 8 heads x 32768 tokens, bf16): every output and final state against the oracle.
-* full   (1 x 64 heads x 131072 tokens, bf16): sampled windows and every final state.
+* full   (1 x 64 heads x 131072 tokens, bf16): sampled windows and every final state; the same
+  shape at head dimension 64 too.
 * long   (1 x 8 heads x 1,048,576 tokens, bf16, checkpoints every 65536): checkpoints, final
   states and output windows (including the chunk boundaries of the LASP+-style split).
 * decode (128 sequences x 64 heads, 4096-token prefix then decode steps): sampled (seq, head).
@@ -118,6 +119,27 @@ def test_full_layer_windows_and_states(device):
     items = [(0, h, w.n) for h in range(w.heads)]
     for (b, h, end), (_, kv_ref) in zip(items, windows_reference(w, items, 1, slopes)):
         assert_close(kv_h[0:1, h:h + 1], kv_ref[None, None], "bf16", f"full KV head {h}")
+
+
+def test_full_layer_d64_windows_and_states(device):
+    # the full layer's shape at head dimension 64 (2 value slices per head, so the sequences are
+    # cut into chunks to fill the GPU): sampled windows across the chunk boundary, every state
+    w = synth.WORKLOADS["full_d64"]
+    slopes = w.slopes()
+    chunk = la.la_prefill_chunk_tokens(la.LA_BF16, w.batch, w.heads, w.n, w.d)
+    assert chunk < w.n
+    q, k, v = upload(w, device)
+    o, kv, _ = run_prefill(w, q, k, v, device)
+    del q, k, v
+    kv_h = kv.cpu().numpy()
+    length = 256
+    items = [(0, h, end) for h in (0, 37, 63) for end in (256, chunk, chunk + 256, w.n)]
+    for (b, h, end), (o_ref, _) in zip(items, windows_reference(w, items, length, slopes)):
+        got = to_host(o[0:1, h:h + 1, end - length:end])
+        assert_close(got, o_ref[None, None], "bf16", f"d=64 O head {h} tokens ..{end}", stored="bf16")
+    items = [(0, h, w.n) for h in range(w.heads)]
+    for (b, h, end), (_, kv_ref) in zip(items, windows_reference(w, items, 1, slopes)):
+        assert_close(kv_h[0:1, h:h + 1], kv_ref[None, None], "bf16", f"d=64 KV head {h}")
 
 
 def test_long_context_checkpoints_and_boundaries(device):
