@@ -10,24 +10,48 @@
 // One 256-thread workgroup owns one (batch, head, chunk, 32-column value
 // slice): the state's columns and the outputs' columns split cleanly by value
 // column, so slices need no communication.  Everything is float32 FMAs on
-// LDS tiles; this path favours plain, checkable arithmetic over speed (the
-// bfloat16 path is the fast one).
+// LDS tiles (the bfloat16 path is the matrix-core one).  Each thread keeps a
+// block of results in registers and reads its operands as 8- or 16-byte runs,
+// so one LDS read feeds 4 to 16 FMAs:
+//   scores  P[r][c]     rows 4(t/16)..+3, keys t%16 + 16b for the key blocks b
+//                       at or below the wave's 16 rows (the rest are masked)
+//   outputs O[r][col]   rows 4(t/16)..+3, columns 2(t%16), 2(t%16)+1
+//   state   KV[i][col]  key rows R(t/8)..+R-1 (R = d/32), columns 4(t%8)..+3
+// Row paddings of 4 floats put 16 consecutive rows (or 4 rows 4 apart) on
+// distinct banks for these reads.
 #include "la_common.h"
 
 namespace la {
 namespace {
 
+template <int N> struct IntC { static constexpr int value = N; };
+
+__device__ inline float dot4(float4 x, float4 y, float acc)
+{
+    acc = fmaf(x.x, y.x, acc);
+    acc = fmaf(x.y, y.y, acc);
+    acc = fmaf(x.z, y.z, acc);
+    return fmaf(x.w, y.w, acc);
+}
+__device__ inline float4 silu4(float4 x)
+{
+    return make_float4(silu_f32(x.x), silu_f32(x.y), silu_f32(x.z), silu_f32(x.w));
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
 {
     constexpr int BK = kBlock, SW = kSliceW;
-    constexpr int RPT = D / 8;  // state rows per thread (thread owns column tid%32, rows tid/32 + 8m)
-    __shared__ float sQ[BK][D + 1];
-    __shared__ float sK[BK][D + 1];
-    __shared__ float sV[BK][SW];
-    __shared__ float sP[BK][BK + 1];
-    __shared__ float sKV[D][SW];
-    __shared__ float sW[BK];
+    constexpr int DP = D + 4, SP = SW + 4, PP = BK + 4;  // padded rows (floats)
+    constexpr int RI = D / 32;                           // state rows per thread
+    constexpr bool OUT = MODE == kModeOut;
+    __shared__ __attribute__((aligned(16))) float sQ[OUT ? BK : 1][DP];
+    __shared__ __attribute__((aligned(16))) float sK[BK][DP];
+    __shared__ __attribute__((aligned(16))) float sV[OUT ? BK : 1][SP];
+    __shared__ __attribute__((aligned(16))) float sVW[BK][SP];
+    __shared__ __attribute__((aligned(16))) float sP[OUT ? BK : 1][PP];
+    __shared__ __attribute__((aligned(16))) float sKV[OUT ? D : 1][SP];
+    __shared__ float sDec[BK + 1];  // lambda^k, k = 0..BK
 
     int64_t group;
     int slice;
@@ -38,95 +62,201 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     const int64_t u = wk.u, j = wk.j, h = wk.h;
     const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int tid = threadIdx.x;
-    const int col = tid % SW;
-    const int row0 = tid / SW;
+    const int wv = tid >> 6;                 // wave: output rows 16wv..16wv+15
+    const int rb = tid >> 4, cb = tid & 15;  // score and output blocks
+    const int ib = tid >> 3, jb = tid & 7;   // state block
     const float nsl = neg_slope_log2e(a.slopes, h);
     const int64_t base = wk.base;
     const float* Q = static_cast<const float*>(a.q) + base;
     const float* K = static_cast<const float*>(a.k) + base;
-    const float* V = static_cast<const float*>(a.v) + base;
-    float* O = static_cast<float*>(a.o) + base;
+    const float* V = static_cast<const float*>(a.v) + base + slice * SW;
+    float* O = static_cast<float*>(a.o) + base + slice * SW;
+    const float* G = a.gate ? static_cast<const float*>(a.gate) + base + slice * SW : nullptr;
     const int64_t d2 = (int64_t)D * D;
-    // memory row of token t of the recurrence: t, or n-1-t when the sequence is walked backwards
-    // (the reverse state recurrence of the backward pass)
+    // memory row of token t of the recurrence: t, or rev_end-1-t when the sequence is walked
+    // backwards (the reverse state recurrence of the backward pass)
     auto mrow = [&](int64_t t) { return a.rev ? wk.rev_end - 1 - t : t; };
+    if (tid <= BK) sDec[tid] = decay_pow(nsl, (float)tid);
 
-    // incoming state slice
-    float st[RPT];
+    // this thread's block of the incoming state slice, also published to LDS for the inter term
+    float st[RI][4];
     const float* src = nullptr;
     if (MODE != kModeLocal) src = (wk.nck > 1) ? a.ws + wk.slot_in * d2 : a.kv + u * d2;
+    auto state_at = [&](int r, int e) { return (RI * ib + r) * D + slice * SW + 4 * jb + e; };
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) st[m] = src ? src[(row0 + 8 * m) * D + slice * SW + col] : 0.f;
+    for (int r = 0; r < RI; ++r)
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) sKV[row0 + 8 * m][col] = st[m];
+        for (int e = 0; e < 4; ++e) st[r][e] = src ? src[state_at(r, e)] : 0.f;
+    auto publish = [&]() {
+        if constexpr (OUT)
+#pragma unroll
+            for (int r = 0; r < RI; ++r)
+                *reinterpret_cast<float4*>(&sKV[RI * ib + r][4 * jb]) =
+                    make_float4(st[r][0], st[r][1], st[r][2], st[r][3]);
+    };
+    publish();
+
+    // masked, decayed scores of this wave's rows against key blocks 0..NB-1 (the later ones lie
+    // wholly above the diagonal)
+    auto scores = [&](auto nbc) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nbc)::value;
+        float s[4][NB];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) s[x][b] = 0.f;
+#pragma unroll 2
+        for (int i = 0; i < D; i += 4) {
+            float4 q[4], k[NB];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) q[x] = *reinterpret_cast<const float4*>(&sQ[4 * rb + x][i]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) k[b] = *reinterpret_cast<const float4*>(&sK[cb + 16 * b][i]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) s[x][b] = dot4(q[x], k[b], s[x][b]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int r = 4 * rb + x, c = cb + 16 * b;
+                sP[r][c] = (b < NB && c <= r) ? s[x][b < NB ? b : 0] * sDec[r - c] : 0.f;
+            }
+    };
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += BK) {
         const int L = (int)((t_end - t0 < BK) ? t_end - t0 : BK);
-        __syncthreads();  // previous tile's readers are done
+        __syncthreads();  // the previous tile's readers are done; the published state is visible
         for (int e = tid; e < BK * (D / 4); e += 256) {
             const int r = e / (D / 4), c4 = e % (D / 4);
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), qx = kx;
             if (r < L) {
                 kx = *reinterpret_cast<const float4*>(K + mrow(t0 + r) * a.sn + 4 * c4);
-                if (MODE == kModeOut) qx = *reinterpret_cast<const float4*>(Q + mrow(t0 + r) * a.sn + 4 * c4);
-                if (a.act & LA_SILU_K) kx = make_float4(silu_f32(kx.x), silu_f32(kx.y), silu_f32(kx.z), silu_f32(kx.w));
-                if (a.act & LA_SILU_Q) qx = make_float4(silu_f32(qx.x), silu_f32(qx.y), silu_f32(qx.z), silu_f32(qx.w));
+                if (a.act & LA_SILU_K) kx = silu4(kx);
+                if (OUT) {
+                    qx = *reinterpret_cast<const float4*>(Q + mrow(t0 + r) * a.sn + 4 * c4);
+                    if (a.act & LA_SILU_Q) qx = silu4(qx);
+                }
             }
-            sK[r][4 * c4] = kx.x; sK[r][4 * c4 + 1] = kx.y; sK[r][4 * c4 + 2] = kx.z; sK[r][4 * c4 + 3] = kx.w;
-            sQ[r][4 * c4] = qx.x; sQ[r][4 * c4 + 1] = qx.y; sQ[r][4 * c4 + 2] = qx.z; sQ[r][4 * c4 + 3] = qx.w;
+            *reinterpret_cast<float4*>(&sK[r][4 * c4]) = kx;
+            if constexpr (OUT) *reinterpret_cast<float4*>(&sQ[r][4 * c4]) = qx;
         }
-        for (int e = tid; e < BK * SW; e += 256) {
-            const int r = e / SW, c = e % SW;
-            const float x = (r < L) ? V[mrow(t0 + r) * a.sn + slice * SW + c] : 0.f;
-            sV[r][c] = (a.act & LA_SILU_V) ? silu_f32(x) : x;
+        for (int e = tid; e < BK * (SW / 4); e += 256) {
+            const int r = e / (SW / 4), c4 = e % (SW / 4);
+            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < L) {
+                vx = *reinterpret_cast<const float4*>(V + mrow(t0 + r) * a.sn + 4 * c4);
+                if (a.act & LA_SILU_V) vx = silu4(vx);
+            }
+            if constexpr (OUT) *reinterpret_cast<float4*>(&sV[r][4 * c4]) = vx;
+            const float w = (r < L) ? sDec[L - 1 - r] : 0.f;  // W = lambda^(L-1-r)
+            *reinterpret_cast<float4*>(&sVW[r][4 * c4]) = make_float4(w * vx.x, w * vx.y, w * vx.z, w * vx.w);
         }
-        if (tid < BK) sW[tid] = (tid < L) ? decay_pow(nsl, (float)(L - 1 - tid)) : 0.f;
         __syncthreads();
 
-        if (MODE == kModeOut) {
-            // masked, decayed scores P[r][c] = lambda^(r-c) q_r . k_c  (c <= r)
-            for (int e = tid; e < BK * BK; e += 256) {
-                const int r = e / BK, c = e % BK;
-                float p = 0.f;
-                if (c <= r) {
-                    float dot = 0.f;
-#pragma unroll 8
-                    for (int i = 0; i < D; ++i) dot += sQ[r][i] * sK[c][i];
-                    p = dot * decay_pow(nsl, (float)(r - c));
-                }
-                sP[r][c] = p;
+        if constexpr (OUT) {
+            switch (wv) {
+            case 0: scores(IntC<1>{}); break;
+            case 1: scores(IntC<2>{}); break;
+            case 2: scores(IntC<3>{}); break;
+            default: scores(IntC<4>{}); break;
             }
             __syncthreads();
-            for (int r = row0; r < L; r += 8) {
-                float inter = 0.f;
-#pragma unroll 8
-                for (int i = 0; i < D; ++i) inter += sQ[r][i] * sKV[i][col];
-                float acc = decay_pow(nsl, (float)(r + 1)) * inter;
-                for (int c = 0; c <= r; ++c) acc += sP[r][c] * sV[c][col];
-                if (a.gate) acc *= sigmoid_f32(static_cast<const float*>(a.gate)[base + mrow(t0 + r) * a.sn + slice * SW + col]);
-                O[mrow(t0 + r) * a.sn + slice * SW + col] = acc;
+            // o = lambda^(r+1) q_r KV + sum_{c <= r} P[r][c] v_c  (P is zero above the diagonal)
+            float o[4][2];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) o[x][0] = o[x][1] = 0.f;
+#pragma unroll 2
+            for (int i = 0; i < D; i += 4) {
+                float4 q[4];
+                float2 kv[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) q[x] = *reinterpret_cast<const float4*>(&sQ[4 * rb + x][i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kv[e] = *reinterpret_cast<const float2*>(&sKV[i + e][2 * cb]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    o[x][0] = dot4(q[x], make_float4(kv[0].x, kv[1].x, kv[2].x, kv[3].x), o[x][0]);
+                    o[x][1] = dot4(q[x], make_float4(kv[0].y, kv[1].y, kv[2].y, kv[3].y), o[x][1]);
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float dr = sDec[4 * rb + x + 1];
+                o[x][0] *= dr;
+                o[x][1] *= dr;
+            }
+            const int c_end = 16 * wv + 16;  // keys at or before this wave's last row
+            for (int c = 0; c < c_end; c += 4) {
+                float4 p[4];
+                float2 v[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) p[x] = *reinterpret_cast<const float4*>(&sP[4 * rb + x][c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const float2*>(&sV[c + e][2 * cb]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    o[x][0] = dot4(p[x], make_float4(v[0].x, v[1].x, v[2].x, v[3].x), o[x][0]);
+                    o[x][1] = dot4(p[x], make_float4(v[0].y, v[1].y, v[2].y, v[3].y), o[x][1]);
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 4 * rb + x;
+                if (r >= L) continue;
+                const int64_t at = mrow(t0 + r) * a.sn + 2 * cb;
+                float2 y = make_float2(o[x][0], o[x][1]);
+                if (G) {
+                    const float2 g = *reinterpret_cast<const float2*>(G + at);
+                    y.x *= sigmoid_f32(g.x);
+                    y.y *= sigmoid_f32(g.y);
+                }
+                *reinterpret_cast<float2*>(O + at) = y;
             }
         }
 
-        // state update
-        const float dl = decay_pow(nsl, (float)L);
+        // state update on this thread's block: KV <- lambda^L KV + K^T (W V)
+        const float dl = sDec[L];
+        float acc[RI][4];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int i = row0 + 8 * m;
-            float acc = 0.f;
-            for (int c = 0; c < L; ++c) acc += sW[c] * sK[c][i] * sV[c][col];
-            st[m] = dl * st[m] + acc;
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[r][e] = 0.f;
+        for (int c = 0; c < L; ++c) {
+            const float4 w4 = *reinterpret_cast<const float4*>(&sVW[c][4 * jb]);
+            float kk[RI];
+            if constexpr (RI == 4) {
+                const float4 k4 = *reinterpret_cast<const float4*>(&sK[c][4 * ib]);
+                kk[0] = k4.x; kk[1] = k4.y; kk[2] = k4.z; kk[3] = k4.w;
+            } else {
+                const float2 k2 = *reinterpret_cast<const float2*>(&sK[c][2 * ib]);
+                kk[0] = k2.x; kk[1] = k2.y;
+            }
+#pragma unroll
+            for (int r = 0; r < RI; ++r) {
+                acc[r][0] = fmaf(kk[r], w4.x, acc[r][0]);
+                acc[r][1] = fmaf(kk[r], w4.y, acc[r][1]);
+                acc[r][2] = fmaf(kk[r], w4.z, acc[r][2]);
+                acc[r][3] = fmaf(kk[r], w4.w, acc[r][3]);
+            }
         }
-        __syncthreads();  // all inter-term reads of sKV are done
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) sKV[row0 + 8 * m][col] = st[m];
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[r][e] = fmaf(dl, st[r][e], acc[r][e]);
+        __syncthreads();  // all inter-term reads of the published state are done
+        publish();
 
         if (MODE != kModeLocal && a.ckpt) {
             const int64_t end = t0 + L;
             if (end % a.ckpt_every == 0) {
                 float* dst = a.ckpt + (u * a.n_ckpt + (end / a.ckpt_every - 1)) * d2;
 #pragma unroll
-                for (int m = 0; m < RPT; ++m) dst[(row0 + 8 * m) * D + slice * SW + col] = st[m];
+                for (int r = 0; r < RI; ++r)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[state_at(r, e)] = st[r][e];
             }
         }
     }
@@ -136,7 +266,9 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     else if (j == wk.nck - 1) dst = a.kv + u * d2;
     if (dst) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) dst[(row0 + 8 * m) * D + slice * SW + col] = st[m];
+        for (int r = 0; r < RI; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[state_at(r, e)] = st[r][e];
     }
 }
 
