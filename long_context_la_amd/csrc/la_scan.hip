@@ -29,6 +29,7 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ ws, const floa
         float4* base = reinterpret_cast<float4*>(ws + u * n_chunks * (int64_t)d2) + e;
         float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
         base[0] = p;
+#pragma unroll 4
         for (int64_t j = 1; j < n_chunks; ++j) {
             const float4 s = base[j * per];
             p.x = lc * p.x + s.x;
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, cons
         float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
         P[0] = p;
         for (int64_t j = 1; j < n_chunks; ++j) {
+#pragma unroll 4
             for (int64_t f = 0; f < n_sub_per; ++f) {
                 const float4 s = S[((j - 1) * n_sub_per + f + 1) * per];
                 p.x = ls * p.x + s.x;
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(256) void k_scan_varlen(float* __restrict__ ws, con
         float4* base = reinterpret_cast<float4*>(ws + (c0 * heads + h) * (int64_t)d2) + e;
         float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
         base[0] = p;
+#pragma unroll 4
         for (int64_t j = 1; j < nc; ++j) {
             const float4 s = base[j * step];
             p.x = lc * p.x + s.x;
