@@ -7,18 +7,18 @@
 // and then KV <- lambda^L KV + sum_c lambda^(L-1-c) k_c^T v_c.
 // Work is O(n d^2 + n B d) with B the tile length.
 //
-// One 256-thread workgroup owns one (batch, head, chunk, 32-column value
-// slice): the state's columns and the outputs' columns split cleanly by value
-// column, so slices need no communication.  Everything is float32 FMAs on
-// LDS tiles (the bfloat16 path is the matrix-core one).  Each thread keeps a
-// block of results in registers and reads its operands as 8- or 16-byte runs,
-// so one LDS read feeds 4 to 16 FMAs:
-//   scores  P[r][c]     rows 4(t/16)..+3, keys t%16 + 16b for the key blocks b
-//                       at or below the wave's 16 rows (the rest are masked)
-//   outputs O[r][col]   rows 4(t/16)..+3, columns 2(t%16), 2(t%16)+1
-//   state   KV[i][col]  key rows R(t/8)..+R-1 (R = d/32), columns 4(t%8)..+3
-// Row paddings of 4 floats put 16 consecutive rows (or 4 rows 4 apart) on
-// distinct banks for these reads.
+// One 512-thread workgroup (two waves per SIMD) owns one (batch, head, chunk,
+// 32-column value slice): the state's columns and the outputs' columns split
+// cleanly by value column, so slices need no communication.  Everything is
+// float32 FMAs on LDS tiles (the bfloat16 path is the matrix-core one).  Each
+// thread keeps a block of results in registers and reads its operands as 8- or
+// 16-byte runs, so one LDS read feeds 2 to 8 FMAs:
+//   scores  P[r][c]     rows 8w + 4x (x = (t%64)/32, wave w), keys t%32 + 32b
+//                       for the key blocks b that reach the wave's 8 rows
+//   outputs O[r][col]   rows 2(t/16)..+1, columns 2(t%16), 2(t%16)+1
+//   state   KV[i][col]  key rows R(t/8)..+R-1 (R = d/64), columns 4(t%8)..+3
+// Row paddings of 4 floats put consecutive rows on distinct banks for these
+// reads.
 #include "la_common.h"
 
 namespace la {
@@ -38,12 +38,14 @@ __device__ inline float4 silu4(float4 x)
     return make_float4(silu_f32(x.x), silu_f32(x.y), silu_f32(x.z), silu_f32(x.w));
 }
 
+constexpr int kThreads = 512;
+
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
+__global__ __launch_bounds__(kThreads) void k_fwd_f32(FwdArgs a)
 {
     constexpr int BK = kBlock, SW = kSliceW;
     constexpr int DP = D + 4, SP = SW + 4, PP = BK + 4;  // padded rows (floats)
-    constexpr int RI = D / 32;                           // state rows per thread
+    constexpr int RI = D / 64;                           // state rows per thread
     constexpr bool OUT = MODE == kModeOut;
     __shared__ __attribute__((aligned(16))) float sQ[OUT ? BK : 1][DP];
     __shared__ __attribute__((aligned(16))) float sK[BK][DP];
@@ -62,9 +64,10 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     const int64_t u = wk.u, j = wk.j, h = wk.h;
     const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;                 // wave: output rows 16wv..16wv+15
-    const int rb = tid >> 4, cb = tid & 15;  // score and output blocks
-    const int ib = tid >> 3, jb = tid & 7;   // state block
+    const int wv = tid >> 6;                                  // wave: score rows 8wv..8wv+7
+    const int sr = 8 * wv + 4 * ((tid & 63) >> 5), sc = tid & 31;  // score block: rows sr..+3, keys sc + 32b
+    const int rb = tid >> 4, cb = tid & 15;                   // output block: rows 2rb..+1, columns 2cb..+1
+    const int ib = tid >> 3, jb = tid & 7;                    // state block
     const float nsl = neg_slope_log2e(a.slopes, h);
     const int64_t base = wk.base;
     const float* Q = static_cast<const float*>(a.q) + base;
@@ -96,8 +99,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     };
     publish();
 
-    // masked, decayed scores of this wave's rows against key blocks 0..NB-1 (the later ones lie
-    // wholly above the diagonal)
+    // masked, decayed scores of this thread's 4 rows against key blocks 0..NB-1 (a later block
+    // lies wholly above the wave's rows)
     auto scores = [&](auto nbc) __attribute__((always_inline)) {
         constexpr int NB = decltype(nbc)::value;
         float s[4][NB];
@@ -109,9 +112,9 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
         for (int i = 0; i < D; i += 4) {
             float4 q[4], k[NB];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) q[x] = *reinterpret_cast<const float4*>(&sQ[4 * rb + x][i]);
+            for (int x = 0; x < 4; ++x) q[x] = *reinterpret_cast<const float4*>(&sQ[sr + x][i]);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) k[b] = *reinterpret_cast<const float4*>(&sK[cb + 16 * b][i]);
+            for (int b = 0; b < NB; ++b) k[b] = *reinterpret_cast<const float4*>(&sK[sc + 32 * b][i]);
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -120,8 +123,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int r = 4 * rb + x, c = cb + 16 * b;
+            for (int b = 0; b < 2; ++b) {
+                const int r = sr + x, c = sc + 32 * b;
                 sP[r][c] = (b < NB && c <= r) ? s[x][b < NB ? b : 0] * sDec[r - c] : 0.f;
             }
     };
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
     for (int64_t t0 = t_begin; t0 < t_end; t0 += BK) {
         const int L = (int)((t_end - t0 < BK) ? t_end - t0 : BK);
         __syncthreads();  // the previous tile's readers are done; the published state is visible
-        for (int e = tid; e < BK * (D / 4); e += 256) {
+        for (int e = tid; e < BK * (D / 4); e += kThreads) {
             const int r = e / (D / 4), c4 = e % (D / 4);
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), qx = kx;
             if (r < L) {
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
             *reinterpret_cast<float4*>(&sK[r][4 * c4]) = kx;
             if constexpr (OUT) *reinterpret_cast<float4*>(&sQ[r][4 * c4]) = qx;
         }
-        for (int e = tid; e < BK * (SW / 4); e += 256) {
+        for (int e = tid; e < BK * (SW / 4); e += kThreads) {
             const int r = e / (SW / 4), c4 = e % (SW / 4);
             float4 vx = make_float4(0.f, 0.f, 0.f, 0.f);
             if (r < L) {
@@ -157,54 +160,50 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
         __syncthreads();
 
         if constexpr (OUT) {
-            switch (wv) {
-            case 0: scores(IntC<1>{}); break;
-            case 1: scores(IntC<2>{}); break;
-            case 2: scores(IntC<3>{}); break;
-            default: scores(IntC<4>{}); break;
-            }
+            if (wv < 4) scores(IntC<1>{});  // rows below 32 meet keys 0..31 only
+            else scores(IntC<2>{});
             __syncthreads();
             // o = lambda^(r+1) q_r KV + sum_{c <= r} P[r][c] v_c  (P is zero above the diagonal)
-            float o[4][2];
+            float o[2][2];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) o[x][0] = o[x][1] = 0.f;
+            for (int x = 0; x < 2; ++x) o[x][0] = o[x][1] = 0.f;
 #pragma unroll 2
             for (int i = 0; i < D; i += 4) {
-                float4 q[4];
+                float4 q[2];
                 float2 kv[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) q[x] = *reinterpret_cast<const float4*>(&sQ[4 * rb + x][i]);
+                for (int x = 0; x < 2; ++x) q[x] = *reinterpret_cast<const float4*>(&sQ[2 * rb + x][i]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) kv[e] = *reinterpret_cast<const float2*>(&sKV[i + e][2 * cb]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
+                for (int x = 0; x < 2; ++x) {
                     o[x][0] = dot4(q[x], make_float4(kv[0].x, kv[1].x, kv[2].x, kv[3].x), o[x][0]);
                     o[x][1] = dot4(q[x], make_float4(kv[0].y, kv[1].y, kv[2].y, kv[3].y), o[x][1]);
                 }
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float dr = sDec[4 * rb + x + 1];
+            for (int x = 0; x < 2; ++x) {
+                const float dr = sDec[2 * rb + x + 1];
                 o[x][0] *= dr;
                 o[x][1] *= dr;
             }
-            const int c_end = 16 * wv + 16;  // keys at or before this wave's last row
+            const int c_end = 8 * wv + 8;  // keys at or before this wave's last row (rows 8wv..8wv+7)
             for (int c = 0; c < c_end; c += 4) {
-                float4 p[4];
+                float4 p[2];
                 float2 v[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) p[x] = *reinterpret_cast<const float4*>(&sP[4 * rb + x][c]);
+                for (int x = 0; x < 2; ++x) p[x] = *reinterpret_cast<const float4*>(&sP[2 * rb + x][c]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const float2*>(&sV[c + e][2 * cb]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
+                for (int x = 0; x < 2; ++x) {
                     o[x][0] = dot4(p[x], make_float4(v[0].x, v[1].x, v[2].x, v[3].x), o[x][0]);
                     o[x][1] = dot4(p[x], make_float4(v[0].y, v[1].y, v[2].y, v[3].y), o[x][1]);
                 }
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 4 * rb + x;
+            for (int x = 0; x < 2; ++x) {
+                const int r = 2 * rb + x;
                 if (r >= L) continue;
                 const int64_t at = mrow(t0 + r) * a.sn + 2 * cb;
                 float2 y = make_float2(o[x][0], o[x][1]);
@@ -227,12 +226,11 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
         for (int c = 0; c < L; ++c) {
             const float4 w4 = *reinterpret_cast<const float4*>(&sVW[c][4 * jb]);
             float kk[RI];
-            if constexpr (RI == 4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&sK[c][4 * ib]);
-                kk[0] = k4.x; kk[1] = k4.y; kk[2] = k4.z; kk[3] = k4.w;
-            } else {
+            if constexpr (RI == 2) {
                 const float2 k2 = *reinterpret_cast<const float2*>(&sK[c][2 * ib]);
                 kk[0] = k2.x; kk[1] = k2.y;
+            } else {
+                kk[0] = sK[c][ib];
             }
 #pragma unroll
             for (int r = 0; r < RI; ++r) {
@@ -275,7 +273,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdArgs a)
 template <int D>
 hipError_t launch_d(const FwdArgs& a, int mode, hipStream_t stream)
 {
-    const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices)), block(256);
+    const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices)), block(kThreads);
     if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_f32<D, kModeOut>), grid, block, 0, stream, a);
     else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_f32<D, kModeState>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_fwd_f32<D, kModeLocal>), grid, block, 0, stream, a);
