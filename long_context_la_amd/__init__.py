@@ -113,6 +113,12 @@ def lib():
     return L
 
 
+def _same_strides(t, ref) -> bool:
+    """Same element strides as ref on every dimension longer than 1 (a dimension of size 1 is
+    never stepped over, so its stride does not matter; the library takes ref's)."""
+    return all(a == b for a, b, n in zip(t.stride(), ref.stride(), ref.shape) if n > 1)
+
+
 def la_status_string(status: int) -> str:
     return lib().la_status_string(status).decode()
 
@@ -181,9 +187,9 @@ def la_prefill(q, k, v, slopes, kv, o=None, ckpt=None, ckpt_every: int = 0, work
     B, H, N, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
-    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(-1) != 1:
+    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
         raise ValueError("q, k, v must share strides with a contiguous last dimension")
-    if o is not None and (o.shape != q.shape or o.stride() != q.stride() or o.dtype != q.dtype):
+    if o is not None and (o.shape != q.shape or not _same_strides(o, q) or o.dtype != q.dtype):
         raise ValueError("o must match q in shape, strides and dtype")
     if slopes.dtype != torch.float32 or kv.dtype != torch.float32:
         raise ValueError("slopes and kv must be float32")
@@ -240,9 +246,9 @@ def la_prefill_varlen(q, k, v, slopes, kv, cu_seqlens, o=None, workspace=None, c
     T, H, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
-    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(-1) != 1:
+    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
         raise ValueError("q, k, v must share strides with a contiguous last dimension")
-    if o is not None and (o.shape != q.shape or o.stride() != q.stride() or o.dtype != q.dtype):
+    if o is not None and (o.shape != q.shape or not _same_strides(o, q) or o.dtype != q.dtype):
         raise ValueError("o must match q in shape, strides and dtype")
     if slopes.dtype != torch.float32 or kv.dtype != torch.float32:
         raise ValueError("slopes and kv must be float32")
@@ -309,10 +315,10 @@ def la_prefill_fused(q, k, v, slopes, kv, o, silu_q=False, silu_k=False, silu_v=
     B, H, N, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
-    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(-1) != 1:
+    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
         raise ValueError("q, k, v must share strides with a contiguous last dimension")
     for t in (o, gate):
-        if t is not None and (t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype):
+        if t is not None and (t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype):
             raise ValueError("o and gate must match q in shape, strides and dtype")
     if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d):
         raise ValueError("norm_weight must be a float32 tensor of d elements")
@@ -363,7 +369,7 @@ def la_backward(q, k, v, dout, slopes, kv_in=None, dkv_out=None, dq=None, dk=Non
     dt = _dtype_code(q)
     B, H, N, d = q.shape
     for t in (k, v, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or t.stride() != q.stride():
+        if t.shape != q.shape or t.dtype != q.dtype or not _same_strides(t, q):
             raise ValueError("q, k, v, dout must share shape, strides and dtype")
     if q.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
@@ -371,7 +377,7 @@ def la_backward(q, k, v, dout, slopes, kv_in=None, dkv_out=None, dq=None, dk=Non
     for t in (dq, dk, dv):
         if t is None:
             t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-        elif t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+        elif t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype:
             raise ValueError("dq, dk, dv must match q in shape, strides and dtype")
         outs.append(t)
     for t in (kv_in, dkv_out, dkv_in):
@@ -407,7 +413,7 @@ def la_backward_varlen(q, k, v, dout, slopes, cu_seqlens, kv_in=None, dkv_out=No
     dt = _dtype_code(q)
     T, H, d = q.shape
     for t in (k, v, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or t.stride() != q.stride():
+        if t.shape != q.shape or t.dtype != q.dtype or not _same_strides(t, q):
             raise ValueError("q, k, v, dout must share shape, strides and dtype")
     if q.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
@@ -418,7 +424,7 @@ def la_backward_varlen(q, k, v, dout, slopes, cu_seqlens, kv_in=None, dkv_out=No
     for t in (dq, dk, dv):
         if t is None:
             t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-        elif t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+        elif t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype:
             raise ValueError("dq, dk, dv must match q in shape, strides and dtype")
         outs.append(t)
     for t in (kv_in, dkv_out, dkv_in):

@@ -255,3 +255,14 @@ def test_backward_varlen_workspace_and_validation():
     assert call(ws_bytes=ws - 16) == la.LA_ERR_WORKSPACE
     if not gpu_available():
         assert call() == la.LA_ERR_DEVICE
+
+
+def test_binding_stride_match_ignores_size_one_dims():
+    import torch
+
+    # numpy gives a size-1 leading dimension the stride of the next one
+    q = torch.from_numpy(np.ascontiguousarray(np.zeros((3, 1, 128), np.float32).transpose(1, 0, 2))).permute(1, 0, 2)
+    o = torch.empty((1, 3, 128)).permute(1, 0, 2)                           # [3, 1, 128], stride_h 384
+    assert q.stride() != o.stride()
+    assert la._same_strides(o, q) and la._same_strides(q, o)
+    assert not la._same_strides(torch.empty(3, 2, 128).permute(1, 0, 2), torch.empty(2, 3, 128))

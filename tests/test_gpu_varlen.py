@@ -92,6 +92,23 @@ def run_varlen(lengths, H, d, dtype, device, chunk_tokens=0, head_major=False, w
 LENGTHS = [0, 1, 5, 64, 65, 200, 1000, 1500]
 
 
+@pytest.mark.parametrize("i", range(10))
+def test_varlen_sweep(device, i):
+    # seeded random packed batches: sequence count and lengths (empty, token by token, tiled, cut
+    # into chunks), heads, dtype and d, explicit chunk lengths, layout, with and without outputs
+    rng = np.random.default_rng(5000 + i)
+    dtype, d = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)][rng.integers(4)]
+    n_seq = int(rng.integers(1, 9))
+    lengths = [int([0, rng.integers(1, 9), rng.integers(9, 300), rng.integers(300, 3000)][k])
+               for k in rng.integers(0, 4, n_seq)]
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    H = int(rng.integers(1, 4))
+    chunk = int(rng.choice([0, 64, 256, 1024]))
+    run_varlen(lengths, H, d, dtype, device, chunk_tokens=chunk, head_major=bool(rng.random() < 0.5),
+               want_o=bool(rng.random() < 0.8), seed=6000 + i)
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)])
 def test_varlen_mixed_lengths(device, dtype, d):
     run_varlen(LENGTHS, 4, d, dtype, device)
