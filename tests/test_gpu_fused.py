@@ -137,6 +137,23 @@ def test_fused_chunked_with_incoming_state(device):
                       kv_in=kv_in)
 
 
+@pytest.mark.parametrize("i", range(10))
+def test_prefill_fused_sweep(device, i):
+    # seeded random fused prefills: SiLU on any subset of q, k, v, norm with or without a weight,
+    # gate, dtype and d, batch/heads/length (chunked when long), incoming states
+    rng = np.random.default_rng(7000 + i)
+    dtype, d = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)][rng.integers(4)]
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    N = int(rng.integers(1, 3000))
+    silu = tuple(bool(x) for x in rng.random(3) < 0.5)
+    norm = bool(rng.random() < 0.5)
+    weight = norm and bool(rng.random() < 0.5)
+    gate = bool(rng.random() < 0.5)
+    kv_in = rng.standard_normal((B, H, d, d)).astype(np.float32) if rng.random() < 0.5 else None
+    run_prefill_fused(B, H, N, d, dtype, device, silu=silu, norm=norm, weight=weight, gate=gate, kv_in=kv_in,
+                      seed=7100 + i)
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
 def test_decode_fused(device, dtype, d):
     torch = _torch()
