@@ -180,3 +180,51 @@ def test_decode_fused(device, dtype, d):
         assert_close_epilogue(to_host(o), o_ref, o_pre, dtype, f"decode fused O step {s}", True, 1e-6, w, g,
                               intermediate=False)
     assert_close(kv.cpu().numpy(), kv_ref, dtype, "decode fused KV")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_decode_sweep(device, i):
+    # seeded random decode runs: batch, heads, dtype and d, steps, and per step a random choice of
+    # the plain step or the fused one (SiLU subset, norm with or without a weight, gate)
+    torch = _torch()
+    rng = np.random.default_rng(8000 + i)
+    dtype, d = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)][rng.integers(4)]
+    B, H, steps = int(rng.integers(1, 5)), int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    slopes = np.exp2(-rng.uniform(0.5, 9, H)).astype(np.float32)
+    ts = torch.from_numpy(slopes).to(device)
+    kv0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    kv = torch.from_numpy(kv0.copy()).to(device)
+    kv_ref = kv0.astype(np.float64)
+    w = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    for s in range(steps):
+        exact, raw = inputs(8100 + 10 * i + s, B, H, 1, d, dtype)
+        q, k, v = (to_device(np.ascontiguousarray(x[:, :, 0]), dtype, device) for x in raw)
+        o = torch.empty_like(q)
+        what = f"case {i} step {s} ({dtype}, d={d}, B={B}, H={H})"
+        if rng.random() < 0.3:
+            la.la_decode(q, k, v, ts, kv, o)
+            torch.cuda.synchronize()
+            o_ref = oracle.decode_step(*(e[:, :, 0] for e in exact), slopes, kv_ref)
+            assert_close(to_host(o)[:, :, None], o_ref[:, :, None], dtype, "decode O " + what, stored=dtype)
+            continue
+        silu = tuple(bool(x) for x in rng.random(3) < 0.5)
+        norm = bool(rng.random() < 0.5)
+        weight = norm and bool(rng.random() < 0.5)
+        gate = bool(rng.random() < 0.5)
+        g, _ = gate_and_weight(8200 + 10 * i + s, (B, H, d), d, dtype)
+        la.la_decode_fused(q, k, v, ts, kv, o, silu_q=silu[0], silu_k=silu[1], silu_v=silu[2],
+                           norm_eps=1e-6 if norm else None,
+                           norm_weight=torch.from_numpy(w).to(device) if weight else None,
+                           gate=dev(g, dtype, device) if gate else None)
+        torch.cuda.synchronize()
+        x, act = activated([e[:, :, 0] for e in exact], silu, dtype)
+        qa, ka, va = (oracle.silu(e) if f else e for e, f in zip(x, act))
+        o_pre = oracle.decode_step(qa, ka, va, slopes, kv_ref)
+        o_ref = o_pre
+        if norm:
+            o_ref = oracle.rms_norm(o_ref, 1e-6, w if weight else None)
+        if gate:
+            o_ref = o_ref * oracle.sigmoid(g)
+        assert_close_epilogue(to_host(o), o_ref, o_pre, dtype, "decode fused O " + what, norm, 1e-6,
+                              w if weight else None, g if gate else None, intermediate=False)
+    assert_close(kv.cpu().numpy(), kv_ref, dtype, f"decode KV case {i}")
