@@ -120,39 +120,65 @@ def test_backward_varlen_packed(device, dtype, d):
     """la_backward_varlen on packed sequences of mixed lengths: empty, short (token by token),
     tiled, and long enough to be cut into chunks, each with its own states; every sequence is
     checked against the oracle on its own tokens."""
+    lengths = [300, 0, 5, 1, 2000, 64, 9, 4100]
+    cu = [0] + list(np.cumsum(lengths))
+    assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16 if dtype == "bf16" else la.LA_F32, cu, 2, d) < 4100
+    run_backward_varlen(lengths, 2, d, dtype, device, np.array([2.0 ** -2, 2.0 ** -7], np.float32), seed=96)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_backward_varlen_sweep(device, i):
+    # seeded random packed batches through the backward: lengths (empty, token by token, tiled,
+    # chunked), heads, dtype and d, slopes, with or without states
+    rng = np.random.default_rng(9000 + i)
+    dtype, d = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)][rng.integers(4)]
+    n_seq = int(rng.integers(1, 7))
+    lengths = [int([0, rng.integers(1, 9), rng.integers(9, 300), rng.integers(300, 3000)][k])
+               for k in rng.integers(0, 4, n_seq)]
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    H = int(rng.integers(1, 4))
+    slopes = np.exp2(-rng.uniform(1, 9, H)).astype(np.float32)
+    run_backward_varlen(lengths, H, d, dtype, device, slopes, seed=9100 + 10 * i, states=bool(rng.random() < 0.6))
+
+
+def run_backward_varlen(lengths, H, d, dtype, device, slopes, seed, states=True):
+    """la_backward_varlen on one packed batch; every sequence against the oracle on its own tokens
+    (an empty sequence passes dL/dKV_final through unchanged)."""
     torch = _torch()
     import synth
 
-    lengths = [300, 0, 5, 1, 2000, 64, 9, 4100]
-    H = 2
     cu = [0] + list(np.cumsum(lengths))
     T = cu[-1]
-    exact, raw = inputs(96, 1, H, T, d, dtype)
-    graw = synth.generate(synth.V, 97, d, nh=H, nt=T, dtype=dtype)
+    exact, raw = inputs(seed, 1, H, T, d, dtype)
+    graw = synth.generate(synth.V, seed + 1, d, nh=H, nt=T, dtype=dtype)
     gex = synth.bf16_bits_to_f32(graw) if dtype == "bf16" else graw
-    slopes = np.array([2.0 ** -2, 2.0 ** -7], np.float32)
-    rng = np.random.default_rng(98)
-    kv_in = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32)
-    dkv_out = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32)
+    rng = np.random.default_rng(seed + 2)
+    kv_in = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32) if states else None
+    dkv_out = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32) if states else None
 
     def packed(x):  # [1, H, T, d] -> device [T, H, d]
         return to_device(np.ascontiguousarray(x[0].transpose(1, 0, 2)), dtype, device)
 
+    def dev_or_none(x):
+        return None if x is None else torch.from_numpy(x).to(device)
+
     q, k, v, do = (packed(x) for x in (*raw, graw))
-    assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16 if dtype == "bf16" else la.LA_F32, cu, H, d) < 4100
     dq, dk, dv, dkv = la.la_backward_varlen(q, k, v, do, torch.from_numpy(slopes).to(device), cu,
-                                            kv_in=torch.from_numpy(kv_in).to(device),
-                                            dkv_out=torch.from_numpy(dkv_out).to(device))
+                                            kv_in=dev_or_none(kv_in), dkv_out=dev_or_none(dkv_out))
     torch.cuda.synchronize()
     got = [to_host(t).transpose(1, 0, 2)[None] for t in (dq, dk, dv)]  # [1, H, T, d]
     dkv_h = dkv.cpu().numpy()
     for s, n in enumerate(lengths):
         a, b = cu[s], cu[s + 1]
         if n == 0:
-            np.testing.assert_allclose(dkv_h[s], dkv_out[s], rtol=1e-6, atol=1e-6)
+            passed = dkv_out[s] if states else np.zeros((H, d, d), np.float32)
+            np.testing.assert_allclose(dkv_h[s], passed, rtol=1e-6, atol=1e-6)
             continue
         want = oracle.backward_recurrent(*(x[:, :, a:b] for x in exact), gex[:, :, a:b], slopes,
-                                         kv_in=kv_in[s:s + 1], dkv_out=dkv_out[s:s + 1])
+                                         kv_in=kv_in[s:s + 1] if states else None,
+                                         dkv_out=dkv_out[s:s + 1] if states else None)
+        what = f"sequence {s} ({n} tokens, {dtype}, d={d}, H={H}, states={states})"
         for name, g_, r in zip(("dq", "dk", "dv"), got, want[:3]):
-            assert_close(g_[:, :, a:b], r, dtype, f"{name} sequence {s} ({n} tokens)", stored=dtype)
-        assert_close(dkv_h[s:s + 1], want[3], dtype, f"dKV_in sequence {s}")
+            assert_close(g_[:, :, a:b], r, dtype, f"{name} {what}", stored=dtype)
+        assert_close(dkv_h[s:s + 1], want[3], dtype, f"dKV_in {what}")
