@@ -146,6 +146,33 @@ def test_strided_views(device):
     assert_close(kv.cpu().numpy(), kv_ref, "bf16", "strided KV")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_padded_row_strides(device, dtype, d):
+    # rows of a wider buffer: storage [B, N, H, d + 24], the kernels see the first d features of
+    # each (b, n, h) row, so stride_h = d + 24 and stride_n = H (d + 24); chunked and ragged
+    torch = _torch()
+    B, H, N, pad = 2, 3, 1500, 24
+    exact, raw = inputs(39, B, H, N, d, dtype)
+
+    def padded(x):
+        full = np.zeros((B, N, H, d + pad), dtype=x.dtype)
+        full[..., :d] = x.transpose(0, 2, 1, 3)
+        return to_device(full, dtype, device)[..., :d].permute(0, 2, 1, 3)
+
+    q, k, v = (padded(x) for x in raw)
+    o_full = torch.zeros((B, N, H, d + pad), dtype=q.dtype, device=device)
+    o = o_full[..., :d].permute(0, 2, 1, 3)
+    assert q.stride() == o.stride() == (N * H * (d + pad), d + pad, H * (d + pad), 1)
+    sl = np.array([0.5, 2.0 ** -4, 2.0 ** -9], np.float32)
+    kv = torch.zeros(B, H, d, d, device=device)
+    la.la_prefill(q, k, v, torch.from_numpy(sl).to(device), kv, o=o, chunk_tokens=512)
+    torch.cuda.synchronize()
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, sl)
+    assert_close(to_host(o), o_ref, dtype, f"padded O ({dtype}, d={d})", stored=dtype)
+    assert_close(kv.cpu().numpy(), kv_ref, dtype, f"padded KV ({dtype}, d={d})")
+    assert float(o_full[..., d:].abs().max()) == 0.0  # nothing written outside the d features
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_impulse(device, dtype):
     B, H, N, d, src = 1, 1, 300, 128, 100
