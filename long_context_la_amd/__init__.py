@@ -10,7 +10,8 @@ Names follow the C entry points: la_state_init, la_prefill,
 la_prefill_workspace_size, la_prefill_chunk_tokens, la_prefill_varlen,
 la_prefill_varlen_workspace_size, la_prefill_varlen_chunk_tokens, la_decode,
 la_status_string, la_last_error.  mixed_step issues a decode group and a
-varlen prefill group on two streams (two library calls, nothing else).
+varlen prefill group on two streams (two library calls, nothing else);
+lightning_attention wraps la_prefill and la_backward as one differentiable op.
 """
 from __future__ import annotations
 
@@ -442,3 +443,51 @@ def la_backward_varlen(q, k, v, dout, slopes, cu_seqlens, kv_in=None, dkv_out=No
                                   _ptr(dkv_in), _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
     _check(st, "la_backward_varlen")
     return outs[0], outs[1], outs[2], dkv_in
+
+
+_autograd_cls = None
+
+
+def _autograd():
+    """torch.autograd.Function over la_prefill (forward) and la_backward (backward), built once."""
+    global _autograd_cls
+    if _autograd_cls is not None:
+        return _autograd_cls
+    import torch
+
+    class LightningAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, slopes, kv_in):
+            B, H, N, d = q.shape
+            kv = (torch.zeros(B, H, d, d, dtype=torch.float32, device=q.device) if kv_in is None
+                  else kv_in.detach().clone().contiguous())
+            o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+            la_prefill(q, k, v, slopes, kv, o=o)
+            ctx.save_for_backward(q, k, v, slopes, kv_in)
+            ctx.mark_non_differentiable(slopes)
+            return o, kv
+
+        @staticmethod
+        def backward(ctx, do, dkv):
+            q, k, v, slopes, kv_in = ctx.saved_tensors
+            if do is None:
+                do = torch.zeros_like(q)
+            if not (_same_strides(do, q) and do.dtype == q.dtype):
+                # la_backward takes one set of strides for q, k, v and dL/dO
+                q, k, v = (t.contiguous() for t in (q, k, v))
+                do = do.to(q.dtype).contiguous()
+            dkv_out = None if dkv is None else dkv.to(torch.float32).contiguous()
+            dq, dk, dv, dkv_in = la_backward(q, k, v, do, slopes,
+                                             kv_in=None if kv_in is None else kv_in.detach().contiguous(),
+                                             dkv_out=dkv_out)
+            return dq, dk, dv, None, (dkv_in if kv_in is not None else None)
+
+    _autograd_cls = LightningAttention
+    return _autograd_cls
+
+
+def lightning_attention(q, k, v, slopes, kv_in=None):
+    """Differentiable prefill for training: (o, kv_out) = the prefill of q, k, v [B,H,N,d] from
+    kv_in [B,H,d,d] float32 (None: zero).  Gradients reach q, k, v and kv_in through la_backward;
+    the decay slopes are constants.  Both passes run in the library's kernels."""
+    return _autograd().apply(q, k, v, slopes, kv_in)

@@ -72,7 +72,7 @@ def test_backward_chunked_f32(device):
 
 
 def test_backward_chunked_bf16_d64(device):
-    # bfloat16 at d = 64 runs on the VALU tile kernel, chunked like the others
+    # bfloat16 at d = 64 (two value slices per head), chunked like the others
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 2, 3000, 64) < 3000
     run_backward(1, 2, 3000, 64, "bf16", device, states=True, seed=94)
 
@@ -146,7 +146,6 @@ def run_backward_varlen(lengths, H, d, dtype, device, slopes, seed, states=True)
     """la_backward_varlen on one packed batch; every sequence against the oracle on its own tokens
     (an empty sequence passes dL/dKV_final through unchanged)."""
     torch = _torch()
-    import synth
 
     cu = [0] + list(np.cumsum(lengths))
     T = cu[-1]
@@ -182,3 +181,29 @@ def run_backward_varlen(lengths, H, d, dtype, device, slopes, seed, states=True)
         for name, g_, r in zip(("dq", "dk", "dv"), got, want[:3]):
             assert_close(g_[:, :, a:b], r, dtype, f"{name} {what}", stored=dtype)
         assert_close(dkv_h[s:s + 1], want[3], dtype, f"dKV_in {what}")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_autograd_function(device, dtype, d):
+    # lightning_attention under torch autograd: a loss on both outputs, gradients for q, k, v and
+    # the incoming state, against the oracle's reverse recurrence
+    torch = _torch()
+    B, H, N = 1, 2, 300
+    exact, raw = inputs(120, B, H, N, d, dtype)
+    q, k, v = (to_device(x, dtype, device).requires_grad_(True) for x in raw)
+    slopes = np.array([2.0 ** -2, 2.0 ** -6], np.float32)
+    rng = np.random.default_rng(121)
+    kv0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    g_o = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    g_kv = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    if dtype == "bf16":
+        g_o = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(g_o))
+    kv_in = torch.from_numpy(kv0).to(device).requires_grad_(True)
+    o, kv_out = la.lightning_attention(q, k, v, torch.from_numpy(slopes).to(device), kv_in)
+    loss = (o.float() * torch.from_numpy(g_o).to(device)).sum() + (kv_out * torch.from_numpy(g_kv).to(device)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    want = oracle.backward_recurrent(*exact, g_o, slopes, kv_in=kv0, dkv_out=g_kv)
+    for name, t, r in zip(("dq", "dk", "dv"), (q, k, v), want[:3]):
+        assert_close(to_host(t.grad), r, dtype, f"autograd {name} ({dtype}, d={d})", stored=dtype)
+    assert_close(kv_in.grad.cpu().numpy(), want[3], dtype, f"autograd dKV_in ({dtype}, d={d})")
