@@ -11,7 +11,8 @@ la_prefill_workspace_size, la_prefill_chunk_tokens, la_prefill_varlen,
 la_prefill_varlen_workspace_size, la_prefill_varlen_chunk_tokens, la_decode,
 la_status_string, la_last_error.  mixed_step issues a decode group and a
 varlen prefill group on two streams (two library calls, nothing else);
-lightning_attention wraps la_prefill and la_backward as one differentiable op.
+lightning_attention and lightning_attention_varlen wrap the prefill and its
+backward as differentiable ops.
 """
 from __future__ import annotations
 
@@ -482,7 +483,35 @@ def _autograd():
                                              dkv_out=dkv_out)
             return dq, dk, dv, None, (dkv_in if kv_in is not None else None)
 
-    _autograd_cls = LightningAttention
+    class LightningAttentionVarlen(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, slopes, kv_in, cu_seqlens):
+            T, H, d = q.shape
+            n_seq = len(cu_seqlens) - 1
+            kv = (torch.zeros(n_seq, H, d, d, dtype=torch.float32, device=q.device) if kv_in is None
+                  else kv_in.detach().clone().contiguous())
+            o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+            la_prefill_varlen(q, k, v, slopes, kv, cu_seqlens, o=o)
+            ctx.save_for_backward(q, k, v, slopes, kv_in)
+            ctx.cu_seqlens = list(cu_seqlens)
+            ctx.mark_non_differentiable(slopes)
+            return o, kv
+
+        @staticmethod
+        def backward(ctx, do, dkv):
+            q, k, v, slopes, kv_in = ctx.saved_tensors
+            if do is None:
+                do = torch.zeros_like(q)
+            if not (_same_strides(do, q) and do.dtype == q.dtype):
+                q, k, v = (t.contiguous() for t in (q, k, v))
+                do = do.to(q.dtype).contiguous()
+            dkv_out = None if dkv is None else dkv.to(torch.float32).contiguous()
+            dq, dk, dv, dkv_in = la_backward_varlen(q, k, v, do, slopes, ctx.cu_seqlens,
+                                                    kv_in=None if kv_in is None else kv_in.detach().contiguous(),
+                                                    dkv_out=dkv_out)
+            return dq, dk, dv, None, (dkv_in if kv_in is not None else None), None
+
+    _autograd_cls = (LightningAttention, LightningAttentionVarlen)
     return _autograd_cls
 
 
@@ -490,4 +519,11 @@ def lightning_attention(q, k, v, slopes, kv_in=None):
     """Differentiable prefill for training: (o, kv_out) = the prefill of q, k, v [B,H,N,d] from
     kv_in [B,H,d,d] float32 (None: zero).  Gradients reach q, k, v and kv_in through la_backward;
     the decay slopes are constants.  Both passes run in the library's kernels."""
-    return _autograd().apply(q, k, v, slopes, kv_in)
+    return _autograd()[0].apply(q, k, v, slopes, kv_in)
+
+
+def lightning_attention_varlen(q, k, v, slopes, cu_seqlens, kv_in=None):
+    """Differentiable packed prefill: (o, kv_out) for q, k, v [T,H,d] holding the sequences
+    cu_seqlens[s]:cu_seqlens[s+1] (host offsets), each from its own state kv_in[s] (None: zero).
+    Gradients reach q, k, v and kv_in through la_backward_varlen."""
+    return _autograd()[1].apply(q, k, v, slopes, kv_in, list(cu_seqlens))

@@ -207,3 +207,38 @@ def test_autograd_function(device, dtype, d):
     for name, t, r in zip(("dq", "dk", "dv"), (q, k, v), want[:3]):
         assert_close(to_host(t.grad), r, dtype, f"autograd {name} ({dtype}, d={d})", stored=dtype)
     assert_close(kv_in.grad.cpu().numpy(), want[3], dtype, f"autograd dKV_in ({dtype}, d={d})")
+
+
+def test_autograd_function_varlen(device):
+    # lightning_attention_varlen under autograd on a packed batch (empty, short, tiled, chunked)
+    torch = _torch()
+    lengths, H, d, dtype = [200, 0, 3, 2500], 2, 128, "bf16"
+    cu = [0] + [int(x) for x in np.cumsum(lengths)]
+    T = cu[-1]
+    exact, raw = inputs(130, 1, H, T, d, dtype)
+    rng = np.random.default_rng(131)
+    kv0 = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32)
+    g_kv = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32)
+    g_o = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((T, H, d)).astype(np.float32)))
+    slopes = np.array([2.0 ** -3, 2.0 ** -7], np.float32)
+    q, k, v = (to_device(np.ascontiguousarray(x[0].transpose(1, 0, 2)), dtype, device).requires_grad_(True)
+               for x in raw)
+    kv_in = torch.from_numpy(kv0).to(device).requires_grad_(True)
+    o, kv_out = la.lightning_attention_varlen(q, k, v, torch.from_numpy(slopes).to(device), cu, kv_in)
+    loss = (o.float() * torch.from_numpy(g_o).to(device)).sum() + (kv_out * torch.from_numpy(g_kv).to(device)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    grads = [to_host(t.grad) for t in (q, k, v)]
+    dkv = kv_in.grad.cpu().numpy()
+    for s, n in enumerate(lengths):
+        a, b = cu[s], cu[s + 1]
+        if n == 0:
+            np.testing.assert_allclose(dkv[s], g_kv[s], rtol=1e-6, atol=1e-6)
+            continue
+        go = np.ascontiguousarray(g_o[a:b].transpose(1, 0, 2))[None]
+        want = oracle.backward_recurrent(*(x[:, :, a:b] for x in exact), go, slopes, kv_in=kv0[s:s + 1],
+                                         dkv_out=g_kv[s:s + 1])
+        for name, g_, r in zip(("dq", "dk", "dv"), grads, want[:3]):
+            assert_close(np.ascontiguousarray(g_[a:b].transpose(1, 0, 2))[None], r, dtype,
+                         f"autograd varlen {name} sequence {s}", stored=dtype)
+        assert_close(dkv[s:s + 1], want[3], dtype, f"autograd varlen dKV_in sequence {s}")
