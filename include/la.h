@@ -182,7 +182,9 @@ la_status la_prefill_ex(la_dtype dt, const void* q, const void* k, const void* v
  *                the call enqueues an asynchronous host-to-device copy of
  *                those tables into it, so it must not be in use by other
  *                work on other streams.
- * No checkpoints.  Supported dtypes and d as for la_prefill.
+ * No checkpoints.  Supported dtypes and d as for la_prefill; n_seq*heads and
+ * (chunks of the sequences longer than 8 tokens)*heads at most 2^20, else
+ * LA_ERR_UNSUPPORTED.
  */
 size_t la_prefill_varlen_workspace_size(la_dtype dt, int64_t n_seq, const int64_t* cu_seqlens, int64_t heads,
                                         int64_t d);
