@@ -93,3 +93,50 @@ def test_prefill_in_a_graph(device):
         assert torch.equal(o, o_ref), f"replay {rep}: outputs differ from eager"
         assert torch.equal(kv, kv_ref), f"replay {rep}: states differ from eager"
         torch.matmul(kv_ref[0, 0], kv_ref[0, 1]).sum().item()
+
+
+def test_backward_and_fused_prefill_in_a_graph(device):
+    # la_backward (three prefill passes and the state preparations) and a fused prefill with the
+    # norm pass, captured together and replayed three times against the eager results
+    torch = _torch()
+    B, H, N, d = 1, 8, 3000, 128
+    raw = [synth.generate(t, 53, d, nb=B, nh=H, nt=N, dtype="bf16") for t in (synth.Q, synth.K, synth.V, synth.V)]
+    q, k, v, do = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device) for x in raw)
+    slopes = torch.from_numpy(synth.WORKLOADS["share"].slopes().copy()).to(device)
+    kv_in = torch.randn(B, H, d, d, device=device)
+    dkv_out = torch.randn(B, H, d, d, device=device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dkv_in = torch.empty(B, H, d, d, device=device)
+    ws_b = torch.empty(la.la_backward_workspace_size(la.LA_BF16, B, H, N, d), dtype=torch.uint8, device=device)
+    kv = torch.empty(B, H, d, d, device=device)
+    o = torch.empty_like(q)
+    gate = torch.randn(B, H, N, d, device=device).to(torch.bfloat16)
+    ws_f = torch.empty(max(la.la_prefill_workspace_size(la.LA_BF16, B, H, N, d), 1), dtype=torch.uint8,
+                       device=device)
+
+    def run():
+        s = torch.cuda.current_stream()
+        la.la_backward(q, k, v, do, slopes, kv_in=kv_in, dkv_out=dkv_out, dq=dq, dk=dk, dv=dv, dkv_in=dkv_in,
+                       workspace=ws_b, stream=s)
+        la.la_state_init(kv, kv_in, stream=s)
+        la.la_prefill_fused(q, k, v, slopes, kv, o, silu_q=True, silu_k=True, norm_eps=1e-5, gate=gate,
+                            workspace=ws_f, stream=s)
+
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, B, H, N, d) < N  # chunked: summaries and scans too
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dq, dk, dv, dkv_in, o, kv)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for t in (dq, dk, dv, o):
+            t.zero_()
+        dkv_in.fill_(3.0)
+        kv.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("dq", "dk", "dv", "dkv_in", "o", "kv"), (dq, dk, dv, dkv_in, o, kv), ref):
+            assert torch.equal(t, r), f"replay {rep}: {name} differs from eager"
+        torch.matmul(ref[3][0, 0], ref[3][0, 1]).sum().item()
