@@ -242,3 +242,24 @@ def test_autograd_function_varlen(device):
             assert_close(np.ascontiguousarray(g_[a:b].transpose(1, 0, 2))[None], r, dtype,
                          f"autograd varlen {name} sequence {s}", stored=dtype)
         assert_close(dkv[s:s + 1], want[3], dtype, f"autograd varlen dKV_in sequence {s}")
+
+
+def test_backward_in_place_state_gradient(device):
+    # dkv_in may alias dkv_out: the gradient of the incoming state overwrites dL/dKV_final
+    torch = _torch()
+    B, H, N, d, dtype = 1, 2, 500, 128, "bf16"
+    exact, raw = inputs(140, B, H, N, d, dtype)
+    q, k, v = (to_device(x, dtype, device) for x in raw)
+    rng = np.random.default_rng(141)
+    g_o = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((B, H, N, d)).astype(np.float32)))
+    kv0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    g_kv = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    do = to_device(synth.f32_to_bf16_bits(g_o), dtype, device)
+    slopes = np.array([2.0 ** -3, 2.0 ** -8], np.float32)
+    buf = torch.from_numpy(g_kv.copy()).to(device)
+    _, _, _, out = la.la_backward(q, k, v, do, torch.from_numpy(slopes).to(device),
+                                  kv_in=torch.from_numpy(kv0).to(device), dkv_out=buf, dkv_in=buf)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == buf.data_ptr()
+    want = oracle.backward_recurrent(*exact, g_o, slopes, kv_in=kv0, dkv_out=g_kv)
+    assert_close(buf.cpu().numpy(), want[3], dtype, "in-place dKV_in")

@@ -286,3 +286,19 @@ def test_bf16_chunked_batch_with_states(device):
     kv0 = np.random.default_rng(9).standard_normal((2, 2, 128, 128)).astype(np.float32)
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 2, 2, 5000, 128) < 5000
     check_prefill(28, 2, 2, 5000, 128, "bf16", SL2, device, kv_in=kv0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_aliased_inputs(device, dtype):
+    # q, k and v may be one tensor (self-similarity attention): the same values as three copies
+    torch = _torch()
+    B, H, N, d = 1, 2, 700, 128
+    exact, raw = inputs(40, B, H, N, d, dtype)
+    x = to_device(raw[0], dtype, device)
+    kv = torch.zeros(B, H, d, d, device=device)
+    o = torch.empty_like(x)
+    la.la_prefill(x, x, x, torch.from_numpy(SL2).to(device), kv, o=o, chunk_tokens=256)
+    torch.cuda.synchronize()
+    o_ref, kv_ref, _ = oracle.recurrent(exact[0], exact[0], exact[0], SL2)
+    assert_close(to_host(o), o_ref, dtype, "aliased O", stored=dtype)
+    assert_close(kv.cpu().numpy(), kv_ref, dtype, "aliased KV")
