@@ -263,3 +263,24 @@ def test_backward_in_place_state_gradient(device):
     assert out.data_ptr() == buf.data_ptr()
     want = oracle.backward_recurrent(*exact, g_o, slopes, kv_in=kv0, dkv_out=g_kv)
     assert_close(buf.cpu().numpy(), want[3], dtype, "in-place dKV_in")
+
+
+def test_backward_state_gradient_over_incoming_state(device):
+    # dkv_in may alias kv_in: the incoming state is read before its gradient overwrites it
+    torch = _torch()
+    B, H, N, d, dtype = 1, 2, 400, 64, "f32"
+    exact, raw = inputs(150, B, H, N, d, dtype)
+    q, k, v = (to_device(x, dtype, device) for x in raw)
+    rng = np.random.default_rng(151)
+    g_o = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    kv0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    g_kv = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    slopes = np.array([2.0 ** -2, 2.0 ** -6], np.float32)
+    buf = torch.from_numpy(kv0.copy()).to(device)
+    dq, dk, dv, _ = la.la_backward(q, k, v, torch.from_numpy(g_o).to(device), torch.from_numpy(slopes).to(device),
+                                   kv_in=buf, dkv_out=torch.from_numpy(g_kv).to(device), dkv_in=buf)
+    torch.cuda.synchronize()
+    want = oracle.backward_recurrent(*exact, g_o, slopes, kv_in=kv0, dkv_out=g_kv)
+    for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), want[:3]):
+        assert_close(to_host(t), r, dtype, f"{name} with dkv_in over kv_in", stored=dtype)
+    assert_close(buf.cpu().numpy(), want[3], dtype, "dKV_in over kv_in")
