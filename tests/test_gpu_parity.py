@@ -173,6 +173,33 @@ def test_padded_row_strides(device, dtype, d):
     assert float(o_full[..., d:].abs().max()) == 0.0  # nothing written outside the d features
 
 
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 0), ("bf16", 64), ("f32", 0)])
+def test_maximum_row_stride(device, dtype, chunk):
+    # stride_n at the documented maximum of 2^22 elements: a 64-row tile then spans 512 MiB (bf16)
+    # or 1 GiB (f32) of 32-bit buffer offsets; 2 heads side by side in each row, 3 tiles (ragged)
+    torch = _torch()
+    B, H, N, d, S = 1, 2, 130, 128, 1 << 22
+    exact, raw = inputs(41, B, H, N, d, dtype)
+
+    def strided(t):
+        full = torch.zeros((N, S), dtype=t.dtype, device=device)
+        view = full[:, :H * d].view(N, H, d).permute(1, 0, 2).unsqueeze(0)
+        view.copy_(t)
+        return full, view
+
+    q, k, v = (strided(to_device(x, dtype, device))[1] for x in raw)
+    o_full, o = strided(torch.zeros((B, H, N, d), dtype=q.dtype, device=device))
+    assert q.stride()[1:] == o.stride()[1:] == (d, S, 1)
+    sl = np.array([2.0 ** -3, 2.0 ** -7], np.float32)
+    kv = torch.zeros(B, H, d, d, device=device)
+    la.la_prefill(q, k, v, torch.from_numpy(sl).to(device), kv, o=o, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, sl)
+    assert_close(to_host(o), o_ref, dtype, f"O at stride_n 2^22 ({dtype}, chunk {chunk})", stored=dtype)
+    assert_close(kv.cpu().numpy(), kv_ref, dtype, f"KV at stride_n 2^22 ({dtype}, chunk {chunk})")
+    assert float(o_full[:, H * d:].abs().max()) == 0.0  # nothing written outside the heads' features
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_impulse(device, dtype):
     B, H, N, d, src = 1, 1, 300, 128, 100
