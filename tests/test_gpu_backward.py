@@ -284,3 +284,38 @@ def test_backward_state_gradient_over_incoming_state(device):
     for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), want[:3]):
         assert_close(to_host(t), r, dtype, f"{name} with dkv_in over kv_in", stored=dtype)
     assert_close(buf.cpu().numpy(), want[3], dtype, "dKV_in over kv_in")
+
+
+def test_backward_maximum_row_stride(device):
+    # stride_n at the documented maximum of 2^22 elements through the three runs (two of them
+    # walking the tiles backwards, whose rows past a ragged tail wrap above the tile's range)
+    torch = _torch()
+    B, H, N, d, S, dtype, seed = 1, 2, 130, 128, 1 << 22, "bf16", 97
+    exact, raw = inputs(seed, B, H, N, d, dtype)
+    dout_raw = synth.generate(synth.V, seed + 500, d, nb=B, nh=H, nt=N, dtype=dtype)
+    slopes = np.array([2.0 ** -3, 2.0 ** -7], dtype=np.float32)
+    rng = np.random.default_rng(seed + 1)
+    kv_in = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dkv_out = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    fulls = []
+
+    def strided(t):
+        full = torch.zeros((N, S), dtype=t.dtype, device=device)
+        view = full[:, :H * d].view(N, H, d).permute(1, 0, 2).unsqueeze(0)
+        view.copy_(t)
+        fulls.append(full)
+        return view
+
+    q, k, v, do = (strided(to_device(x, dtype, device)) for x in (*raw, dout_raw))
+    dq, dk, dv = (strided(torch.zeros_like(to_device(raw[0], dtype, device))) for _ in range(3))
+    assert q.stride()[1:] == dq.stride()[1:] == (d, S, 1)
+    _, _, _, dkv = la.la_backward(q, k, v, do, torch.from_numpy(slopes).to(device),
+                                  kv_in=torch.from_numpy(kv_in).to(device),
+                                  dkv_out=torch.from_numpy(dkv_out).to(device), dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    want = oracle.backward_recurrent(*exact, synth.bf16_bits_to_f32(dout_raw), slopes, kv_in=kv_in, dkv_out=dkv_out)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want[:3]):
+        assert_close(to_host(got), ref, dtype, f"{name} at stride_n 2^22", stored=dtype)
+    assert_close(dkv.cpu().numpy(), want[3], dtype, "dkv_in at stride_n 2^22")
+    for full in fulls[4:]:
+        assert float(full[:, H * d:].abs().max()) == 0.0  # nothing written outside the heads' features
