@@ -80,7 +80,8 @@ namespace {
 // offsets above the tile's range): a row stride of at most 2^22 elements keeps that within reach.
 constexpr int64_t kMaxRowStride = int64_t(1) << 22;
 // Work items of one launch: (batch, head) pairs, or (sequence or batch, head, chunk) triples.  At
-// most 2^20 keeps every grid (4 value slices x 512 threads per item) under 2^31 work-items.
+// most 2^20 keeps every grid (4 value slices x 512 threads per item) at or below 2^31 work-items,
+// within the dispatch's 32-bit grid size.
 constexpr int64_t kMaxUnits = int64_t(1) << 20;
 
 la_status check_shape(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)

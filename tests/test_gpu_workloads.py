@@ -293,3 +293,41 @@ def test_backward_full_layer_windows(device):
                 assert_close(got, r[:, :, :length], "bf16", f"full {name} head {h} tokens {begin}..", stored="bf16")
             if begin == 0:
                 assert_close(dkv[0:1, h:h + 1].cpu().numpy(), ref[3], "bf16", f"full dKV_in head {h}")
+
+
+def test_maximum_units_prefill_then_decode(device):
+    # batch * heads at the documented maximum of 2^20 units (16384 sequences x 64 heads, d = 64):
+    # a 3-token prefill (one ragged tile per unit) and then one decode step, checked against the
+    # oracle's 4-token recurrence on sampled units, the first and the last among them
+    import torch
+
+    B, H, N, d, seed = 16384, 64, 3, 64, 23
+    slopes = np.array([2.0 ** (-(h + 1) / 8) for h in range(H)], dtype=np.float32)
+    pre = [synth.generate(t, seed, d, nb=B, nh=H, nt=N, dtype="bf16") for t in (synth.Q, synth.K, synth.V)]
+    step = [synth.generate(t, seed, d, nb=B, nh=H, t0=N, nt=1, dtype="bf16")[:, :, 0] for t in (synth.Q, synth.K, synth.V)]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+    q, k, v = (up(x) for x in pre)
+    o = torch.empty_like(q)
+    kv = torch.empty(B, H, d, d, dtype=torch.float32, device=device)
+    sl = torch.from_numpy(slopes).to(device)
+    la.la_state_init(kv)
+    la.la_prefill(q, k, v, sl, kv, o=o)
+    del q, k, v
+    qd, kd, vd = (up(x) for x in step)
+    od = torch.empty_like(qd)
+    la.la_decode(qd, kd, vd, sl, kv, od)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    units = [0, 1, H - 1, 4097, (1 << 19) + 13, (1 << 20) - 1] + [int(u) for u in rng.integers(0, B * H, 10)]
+    for u in units:
+        b, h = divmod(u, H)
+        ex = [synth.bf16_bits_to_f32(np.concatenate([p[b, h], s[b, h][None]])[None, None]) for p, s in zip(pre, step)]
+        o_ref, kv_ref, _ = oracle.recurrent(*ex, slopes[h:h + 1])
+        what = f"unit {u} (b={b}, h={h})"
+        assert_close(to_host(o[b:b + 1, h:h + 1]), o_ref[:, :, :N], "bf16", f"prefill O {what}", stored="bf16")
+        assert_close(to_host(od[b:b + 1, h:h + 1])[:, :, None], o_ref[:, :, N:], "bf16", f"decode o {what}",
+                     stored="bf16")
+        assert_close(kv[b:b + 1, h:h + 1].cpu().numpy(), kv_ref, "bf16", f"KV {what}")
