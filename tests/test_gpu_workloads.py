@@ -331,3 +331,40 @@ def test_maximum_units_prefill_then_decode(device):
         assert_close(to_host(od[b:b + 1, h:h + 1])[:, :, None], o_ref[:, :, N:], "bf16", f"decode o {what}",
                      stored="bf16")
         assert_close(kv[b:b + 1, h:h + 1].cpu().numpy(), kv_ref, "bf16", f"KV {what}")
+
+
+def test_maximum_units_packed_short_sequences(device):
+    # n_seq * heads at the documented maximum of 2^20 (16384 packed sequences x 64 heads, d = 64),
+    # every sequence 1..8 tokens long (the token-by-token launch, one workgroup per unit, plus a
+    # few empty ones), from random incoming states; sampled sequences against the oracle
+    import torch
+
+    S, H, d, seed = 16384, 64, 64, 29
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 9, S)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    slopes = np.array([2.0 ** (-(h + 1) / 8) for h in range(H)], dtype=np.float32)
+    raw = [synth.generate(t, seed, d, nh=H, nt=T, dtype="bf16")[0].transpose(1, 0, 2) for t in (synth.Q, synth.K, synth.V)]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+    q, k, v = (up(x) for x in raw)  # [T, H, d]
+    o = torch.zeros_like(q)
+    kv = torch.randn(S, H, d, d, generator=torch.Generator(device=device).manual_seed(seed), device=device)
+    picks = [0, 1, S // 2, S - 1] + [int(s) for s in rng.integers(0, S, 12)] + [int(np.argmin(lens))]
+    kv0 = {s: kv[s].cpu().numpy() for s in picks}
+    la.la_prefill_varlen(q, k, v, torch.from_numpy(slopes).to(device), kv, cu, o=o)
+    torch.cuda.synchronize()
+    for s in picks:
+        a, b = int(cu[s]), int(cu[s + 1])
+        what = f"sequence {s} ({b - a} tokens)"
+        if b == a:
+            assert np.array_equal(kv[s].cpu().numpy(), kv0[s]), f"{what}: an empty sequence changed its state"
+            continue
+        ex = [synth.bf16_bits_to_f32(np.ascontiguousarray(x[a:b].transpose(1, 0, 2))[None]) for x in raw]
+        o_ref, kv_ref, _ = oracle.recurrent(*ex, slopes, kv_in=kv0[s][None])
+        assert_close(np.ascontiguousarray(to_host(o[a:b]).transpose(1, 0, 2))[None], o_ref, "bf16", f"O {what}",
+                     stored="bf16")
+        assert_close(kv[s].cpu().numpy()[None], kv_ref, "bf16", f"KV {what}")
