@@ -20,8 +20,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates no device memory and keeps no state between calls other than
- *     a thread-local error string.
+ *     allocates no device memory.  Between calls it keeps a thread-local error
+ *     string and, for the packed (varlen) entry points, a small ring of
+ *     page-locked host buffers per device that stage their chunk tables.
  *   - Every call only enqueues work on `stream` (a hipStream_t passed as void*,
  *     NULL = the default stream) and returns; device-side faults appear at the
  *     caller's next synchronisation.
@@ -36,7 +37,8 @@
  *     copy), so a sequence of them can be captured into a graph and replayed;
  *     the replay reads the tensors at the captured addresses.
  *     la_prefill_varlen enqueues a host-to-device copy of its chunk tables
- *     from a temporary host buffer and must not be captured.
+ *     from a page-locked staging buffer that later calls reuse, so it must not
+ *     be captured.
  */
 #ifndef LIGHTNING_LA_H
 #define LIGHTNING_LA_H
@@ -118,7 +120,10 @@ size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int6
  *   q, k, v, o : element (b, h, t, e) at base + b*stride_b + h*stride_h +
  *                t*stride_n + e (strides in elements, shared by all four;
  *                the last dimension is contiguous).  q, k, v are read-only and
- *                may alias each other; o must not overlap q, k, v or kv.
+ *                may alias each other; o must not overlap q, k, v or kv, and
+ *                its rows must be pairwise disjoint (no stride 0 on a
+ *                dimension longer than one, no two (b, h, t) rows sharing an
+ *                element), else LA_ERR_INVALID_ARGUMENT.
  *                Pointers 16-byte aligned; strides multiples of 8 elements
  *                (bf16) or 4 (f32); d <= stride_n <= 2^22 (a 64-row tile
  *                then spans under 2 GiB, the reach of a 32-bit buffer
@@ -129,7 +134,11 @@ size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int6
  *   kv         : [batch][heads][d][d] float32, read then overwritten.
  *   ckpt       : NULL, or [batch][heads][n / ckpt_every][d][d] float32 that
  *                receives the state after token (m+1)*ckpt_every - 1 in slot m.
- *                ckpt_every must be a positive multiple of 64.
+ *                ckpt_every must be positive (else LA_ERR_INVALID_ARGUMENT).
+ *                Multiples of 64 (the kernel tile) are stored by the prefill
+ *                kernels at tile ends at no extra cost; any other value runs
+ *                the sequence as one prefill per ckpt_every tokens, each
+ *                followed by a copy of the state into its slot.
  *   workspace  : device scratch of at least la_prefill_workspace_size() bytes
  *                (may be NULL when that size is 0); contents are clobbered.
  * Supported: d in {64, 128} for both dtypes (bfloat16 runs on the MFMA
@@ -172,16 +181,19 @@ la_status la_prefill_ex(la_dtype dt, const void* q, const void* k, const void* v
  * inputs), so short and long sequences share the GPU without padding.
  *   q, k, v, o : element (t, h, e) at base + t*stride_n + h*stride_h + e, t =
  *                packed token index (e.g. [total][heads][d] has stride_n =
- *                heads*d, stride_h = d); rules as for la_prefill.
+ *                heads*d, stride_h = d); rules as for la_prefill (o's rows
+ *                pairwise disjoint).
  *   cu_seqlens : HOST array of n_seq + 1 int64, cu_seqlens[0] = 0,
  *                nondecreasing (empty sequences allowed: their state is left
  *                unchanged).  Read during the call only.
  *   kv         : [n_seq][heads][d][d] float32, read then overwritten.
  *   workspace  : device scratch of at least la_prefill_varlen_workspace_size()
  *                bytes (never 0 bytes: it also receives the chunk tables);
- *                the call enqueues an asynchronous host-to-device copy of
- *                those tables into it, so it must not be in use by other
- *                work on other streams.
+ *                the call copies those tables into it asynchronously on
+ *                `stream`, from page-locked staging buffers that the library
+ *                reuses only once the copy has completed, so cu_seqlens may be
+ *                released as soon as the call returns.  The workspace must not
+ *                be in use by other work on other streams.
  * No checkpoints.  Supported dtypes and d as for la_prefill; n_seq*heads and
  * (chunks of the sequences longer than 8 tokens)*heads at most 2^20, else
  * LA_ERR_UNSUPPORTED.
@@ -254,7 +266,9 @@ la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, vo
  *   dkv_out             : dL/dKV_final [batch][heads][d][d] float32, or NULL (zero).
  *                         Requires s_h < 80 (lambda > e^-80): it is scaled by 1/lambda.
  *   dq, dk, dv          : outputs, same layout and dtype; must not overlap the
- *                         inputs or each other.
+ *                         inputs or each other, and their rows must be pairwise
+ *                         disjoint as for la_prefill's o (else
+ *                         LA_ERR_INVALID_ARGUMENT).
  *   dkv_in              : output dL/dKV_in [batch][heads][d][d] float32, or NULL
  *                         (not wanted); may alias kv_in or dkv_out.
  *   workspace           : at least la_backward_workspace_size() bytes (never 0).

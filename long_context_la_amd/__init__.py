@@ -115,6 +115,81 @@ def lib():
     return L
 
 
+def _rows_disjoint(t) -> bool:
+    """True when no two rows (all indices but the last, which is contiguous) of the strided tensor
+    t share an element: with the dimensions longer than one sorted by stride, each stride is at
+    least the span of the faster ones (the same rule the library applies to its outputs)."""
+    span = t.shape[-1]
+    for st, n in sorted((st, n) for st, n in zip(t.stride()[:-1], t.shape[:-1]) if n > 1):
+        if st < span:
+            return False
+        span += st * (n - 1)
+    return True
+
+
+def _check_f32(t, shape, name):
+    """t is None or a contiguous float32 tensor of exactly this shape (states, checkpoints)."""
+    import torch
+
+    if t is None:
+        return
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} "
+                         f"(got {t.dtype}, {tuple(t.shape)}, contiguous={t.is_contiguous()})")
+
+
+def _check_slopes(slopes, heads):
+    import torch
+
+    if (slopes.dtype != torch.float32 or slopes.dim() != 1 or slopes.numel() != heads
+            or not slopes.is_contiguous()):
+        raise ValueError(f"slopes must be a contiguous 1-D float32 tensor of {heads} elements "
+                         f"(got {slopes.dtype}, {tuple(slopes.shape)})")
+
+
+def _check_qkv(q, k, v, ndim):
+    if q.dim() != ndim:
+        raise ValueError(f"q, k, v must be {ndim}-D")
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
+        raise ValueError("q, k, v must share strides with a contiguous last dimension")
+
+
+def _check_out(t, q, name):
+    """An output (or gate) tensor laid out like q; outputs must also have disjoint rows."""
+    if t is None:
+        return
+    if t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype:
+        raise ValueError(f"{name} must match q in shape, strides and dtype")
+    if not _rows_disjoint(t):
+        raise ValueError(f"the rows of {name} overlap (a zero stride on a dimension longer than one, or "
+                         "strides that map two rows onto shared elements)")
+
+
+def _dense_layout(*ts):
+    """The inputs as they are when their rows are disjoint, else contiguous copies (an expanded
+    view has stride 0, and outputs allocated with its strides would overlap)."""
+    if all(_rows_disjoint(t) for t in ts):
+        return ts
+    return tuple(t.contiguous() for t in ts)
+
+
+def _on_stream(stream, *ts):
+    """Temporaries used by work enqueued on a stream other than the current one are recorded on
+    it, so the caching allocator does not hand their memory out again before that work is done."""
+    import torch
+
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream(stream.device)
+    if stream == cur:
+        return
+    for t in ts:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _same_strides(t, ref) -> bool:
     """Same element strides as ref on every dimension longer than 1 (a dimension of size 1 is
     never stepped over, so its stride does not matter; the library takes ref's)."""
@@ -163,8 +238,12 @@ def _require_cuda(*ts):
 
 def la_state_init(kv, kv0=None, stream=None) -> None:
     """kv[B,H,d,d] (float32) := 0, or a copy of kv0."""
-    _require_cuda(kv, kv0)
+    if kv.dim() != 4 or kv.shape[2] != kv.shape[3]:
+        raise ValueError("kv must be [B, H, d, d]")
     B, H, d, _ = kv.shape
+    _check_f32(kv, (B, H, d, d), "kv")
+    _check_f32(kv0, (B, H, d, d), "kv0")
+    _require_cuda(kv, kv0)
     _check(lib().la_state_init(_ptr(kv), _ptr(kv0), B, H, d, _stream_ptr(stream, kv.device)), "la_state_init")
 
 
@@ -184,20 +263,21 @@ def la_prefill(q, k, v, slopes, kv, o=None, ckpt=None, ckpt_every: int = 0, work
     la_prefill_workspace_size() bytes is allocated here when not supplied."""
     import torch
 
-    _require_cuda(q, k, v, slopes, kv, o, ckpt, workspace)
+    _check_qkv(q, k, v, 4)
     dt = _dtype_code(q)
     B, H, N, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
-    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
-        raise ValueError("q, k, v must share strides with a contiguous last dimension")
-    if o is not None and (o.shape != q.shape or not _same_strides(o, q) or o.dtype != q.dtype):
-        raise ValueError("o must match q in shape, strides and dtype")
-    if slopes.dtype != torch.float32 or kv.dtype != torch.float32:
-        raise ValueError("slopes and kv must be float32")
+    _check_out(o, q, "o")
+    _check_slopes(slopes, H)
+    _check_f32(kv, (B, H, d, d), "kv")
+    if ckpt is not None:
+        if ckpt_every <= 0:
+            raise ValueError("ckpt_every must be positive when ckpt is given")
+        _check_f32(ckpt, (B, H, N // ckpt_every, d, d), "ckpt")
+    _require_cuda(q, k, v, slopes, kv, o, ckpt, workspace)
     need = la_prefill_workspace_size(dt, B, H, N, d, chunk_tokens)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _on_stream(stream, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sb, sh, sn, _ = q.stride()
     st = lib().la_prefill_ex(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, sb, sh, sn,
@@ -208,12 +288,16 @@ def la_prefill(q, k, v, slopes, kv, o=None, ckpt=None, ckpt_every: int = 0, work
 
 def la_decode(q, k, v, slopes, kv, o, stream=None) -> None:
     """One decode step: kv <- lambda*kv + k^T v ; o = q . kv.  q,k,v,o contiguous [B,H,d]."""
-    _require_cuda(q, k, v, slopes, kv, o)
+    if q.dim() != 3:
+        raise ValueError("q, k, v, o must be [B,H,d]")
     dt = _dtype_code(q)
     B, H, d = q.shape
     for t in (q, k, v, o):
         if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k, v, o must be contiguous [B,H,d] tensors of one dtype")
+    _check_slopes(slopes, H)
+    _check_f32(kv, (B, H, d, d), "kv")
+    _require_cuda(q, k, v, slopes, kv, o)
     st = lib().la_decode(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d, _ptr(slopes), _ptr(kv),
                          _stream_ptr(stream, q.device))
     _check(st, "la_decode")
@@ -243,23 +327,20 @@ def la_prefill_varlen(q, k, v, slopes, kv, cu_seqlens, o=None, workspace=None, c
     The workspace (la_prefill_varlen_workspace_size bytes) is allocated here if not given."""
     import torch
 
-    _require_cuda(q, k, v, slopes, kv, o, workspace)
+    _check_qkv(q, k, v, 3)
     dt = _dtype_code(q)
     T, H, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
-    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
-        raise ValueError("q, k, v must share strides with a contiguous last dimension")
-    if o is not None and (o.shape != q.shape or not _same_strides(o, q) or o.dtype != q.dtype):
-        raise ValueError("o must match q in shape, strides and dtype")
-    if slopes.dtype != torch.float32 or kv.dtype != torch.float32:
-        raise ValueError("slopes and kv must be float32")
+    _check_out(o, q, "o")
+    _check_slopes(slopes, H)
     cu, n_seq = _cu_array(cu_seqlens)
     if cu[n_seq] != T:
         raise ValueError("cu_seqlens[-1] must equal the packed token count")
+    _check_f32(kv, (n_seq, H, d, d), "kv")
+    _require_cuda(q, k, v, slopes, kv, o, workspace)
     need = int(lib().la_prefill_varlen_workspace_size_ex(dt, n_seq, cu, H, d, chunk_tokens))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _on_stream(stream, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sn, sh, _ = q.stride()
     st = lib().la_prefill_varlen_ex(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), n_seq, cu, H, d, sh, sn,
@@ -312,21 +393,24 @@ def la_prefill_fused(q, k, v, slopes, kv, o, silu_q=False, silu_k=False, silu_v=
     o * sigmoid(gate) (gate: q's shape, strides and dtype).  o is required."""
     import torch
 
-    _require_cuda(q, k, v, slopes, kv, o, workspace, norm_weight, gate)
+    _check_qkv(q, k, v, 4)
     dt = _dtype_code(q)
     B, H, N, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
-    if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
-        raise ValueError("q, k, v must share strides with a contiguous last dimension")
-    for t in (o, gate):
-        if t is not None and (t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype):
-            raise ValueError("o and gate must match q in shape, strides and dtype")
-    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d):
-        raise ValueError("norm_weight must be a float32 tensor of d elements")
+    if o is None:
+        raise ValueError("la_prefill_fused needs an output tensor o")
+    _check_out(o, q, "o")
+    if gate is not None and (gate.shape != q.shape or not _same_strides(gate, q) or gate.dtype != q.dtype):
+        raise ValueError("gate must match q in shape, strides and dtype")
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d
+                                    or not norm_weight.is_contiguous()):
+        raise ValueError("norm_weight must be a contiguous float32 tensor of d elements")
+    _check_slopes(slopes, H)
+    _check_f32(kv, (B, H, d, d), "kv")
+    _require_cuda(q, k, v, slopes, kv, o, workspace, norm_weight, gate)
     need = la_prefill_workspace_size(dt, B, H, N, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _on_stream(stream, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sb, sh, sn, _ = q.stride()
     fu = _fusion(silu_q, silu_k, silu_v, norm_eps, norm_weight, gate)
@@ -340,14 +424,19 @@ def la_decode_fused(q, k, v, slopes, kv, o, silu_q=False, silu_k=False, silu_v=F
     """la_decode with the fused prologue/epilogue (see la_prefill_fused); gate is [B,H,d]."""
     import torch
 
-    _require_cuda(q, k, v, slopes, kv, o, norm_weight, gate)
+    if q.dim() != 3:
+        raise ValueError("q, k, v, o must be [B,H,d]")
     dt = _dtype_code(q)
     B, H, d = q.shape
     for t in (q, k, v, o) + ((gate,) if gate is not None else ()):
         if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k, v, o (and gate) must be contiguous [B,H,d] tensors of one dtype")
-    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d):
-        raise ValueError("norm_weight must be a float32 tensor of d elements")
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d
+                                    or not norm_weight.is_contiguous()):
+        raise ValueError("norm_weight must be a contiguous float32 tensor of d elements")
+    _check_slopes(slopes, H)
+    _check_f32(kv, (B, H, d, d), "kv")
+    _require_cuda(q, k, v, slopes, kv, o, norm_weight, gate)
     fu = _fusion(silu_q, silu_k, silu_v, norm_eps, norm_weight, gate)
     st = lib().la_decode_fused(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d, _ptr(slopes), _ptr(kv),
                                ctypes.byref(fu), _stream_ptr(stream, q.device))
@@ -367,29 +456,32 @@ def la_backward(q, k, v, dout, slopes, kv_in=None, dkv_out=None, dq=None, dk=Non
     zero).  Outputs are allocated when not given (dq, dk, dv like q)."""
     import torch
 
-    _require_cuda(q, k, v, dout, slopes, kv_in, dkv_out, dq, dk, dv, dkv_in, workspace)
-    dt = _dtype_code(q)
-    B, H, N, d = q.shape
+    if q.dim() != 4:
+        raise ValueError("q, k, v, dout must be [B,H,N,d]")
     for t in (k, v, dout):
         if t.shape != q.shape or t.dtype != q.dtype or not _same_strides(t, q):
             raise ValueError("q, k, v, dout must share shape, strides and dtype")
     if q.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
-    outs = []
-    for t in (dq, dk, dv):
-        if t is None:
-            t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-        elif t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype:
-            raise ValueError("dq, dk, dv must match q in shape, strides and dtype")
-        outs.append(t)
-    for t in (kv_in, dkv_out, dkv_in):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, d, d) or not t.is_contiguous()):
-            raise ValueError("states must be contiguous float32 [B,H,d,d]")
+    dt = _dtype_code(q)
+    B, H, N, d = q.shape
+    _check_slopes(slopes, H)
+    for t, name in ((kv_in, "kv_in"), (dkv_out, "dkv_out"), (dkv_in, "dkv_in")):
+        _check_f32(t, (B, H, d, d), name)
+    if all(t is None for t in (dq, dk, dv)):
+        q, k, v, dout = _dense_layout(q, k, v, dout)   # gradients are allocated with q's strides
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_out(t, q, name)
+    _require_cuda(q, k, v, dout, slopes, kv_in, dkv_out, dq, dk, dv, dkv_in, workspace)
+    outs = [torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if t is None else t
+            for t in (dq, dk, dv)]
     if dkv_in is None:
         dkv_in = torch.empty(B, H, d, d, dtype=torch.float32, device=q.device)
     need = la_backward_workspace_size(dt, B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _on_stream(stream, workspace)
+    _on_stream(stream, *(o for o, given in zip(outs, (dq, dk, dv)) if given is None))
     ws_bytes = workspace.numel() * workspace.element_size()
     sb, sh, sn, _ = q.stride()
     st = lib().la_backward(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, sb, sh, sn, _ptr(slopes),
@@ -411,32 +503,35 @@ def la_backward_varlen(q, k, v, dout, slopes, cu_seqlens, kv_in=None, dkv_out=No
     states are [n_seq, H, d, d] float32.  Returns (dq, dk, dv, dkv_in)."""
     import torch
 
-    _require_cuda(q, k, v, dout, slopes, kv_in, dkv_out, dq, dk, dv, dkv_in, workspace)
-    dt = _dtype_code(q)
-    T, H, d = q.shape
+    if q.dim() != 3:
+        raise ValueError("q, k, v, dout must be [T,H,d]")
     for t in (k, v, dout):
         if t.shape != q.shape or t.dtype != q.dtype or not _same_strides(t, q):
             raise ValueError("q, k, v, dout must share shape, strides and dtype")
     if q.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
+    dt = _dtype_code(q)
+    T, H, d = q.shape
+    _check_slopes(slopes, H)
     cu, n_seq = _cu_array(cu_seqlens)
     if cu[n_seq] != T:
         raise ValueError("cu_seqlens[-1] must equal the number of packed tokens")
-    outs = []
-    for t in (dq, dk, dv):
-        if t is None:
-            t = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-        elif t.shape != q.shape or not _same_strides(t, q) or t.dtype != q.dtype:
-            raise ValueError("dq, dk, dv must match q in shape, strides and dtype")
-        outs.append(t)
-    for t in (kv_in, dkv_out, dkv_in):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (n_seq, H, d, d) or not t.is_contiguous()):
-            raise ValueError("states must be contiguous float32 [n_seq, H, d, d]")
+    for t, name in ((kv_in, "kv_in"), (dkv_out, "dkv_out"), (dkv_in, "dkv_in")):
+        _check_f32(t, (n_seq, H, d, d), name)
+    if all(t is None for t in (dq, dk, dv)):
+        q, k, v, dout = _dense_layout(q, k, v, dout)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_out(t, q, name)
+    _require_cuda(q, k, v, dout, slopes, kv_in, dkv_out, dq, dk, dv, dkv_in, workspace)
+    outs = [torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if t is None else t
+            for t in (dq, dk, dv)]
     if dkv_in is None:
         dkv_in = torch.empty(n_seq, H, d, d, dtype=torch.float32, device=q.device)
     need = int(lib().la_backward_varlen_workspace_size(dt, n_seq, cu, H, d))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _on_stream(stream, workspace)
+    _on_stream(stream, *(o for o, given in zip(outs, (dq, dk, dv)) if given is None))
     ws_bytes = workspace.numel() * workspace.element_size()
     sn, sh, _ = q.stride()
     st = lib().la_backward_varlen(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), n_seq, cu, H, d, sh, sn, _ptr(slopes),
@@ -462,6 +557,7 @@ def _autograd():
             B, H, N, d = q.shape
             kv = (torch.zeros(B, H, d, d, dtype=torch.float32, device=q.device) if kv_in is None
                   else kv_in.detach().clone().contiguous())
+            q, k, v = _dense_layout(q, k, v)
             o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
             la_prefill(q, k, v, slopes, kv, o=o)
             ctx.save_for_backward(q, k, v, slopes, kv_in)
@@ -490,6 +586,7 @@ def _autograd():
             n_seq = len(cu_seqlens) - 1
             kv = (torch.zeros(n_seq, H, d, d, dtype=torch.float32, device=q.device) if kv_in is None
                   else kv_in.detach().clone().contiguous())
+            q, k, v = _dense_layout(q, k, v)
             o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
             la_prefill_varlen(q, k, v, slopes, kv, cu_seqlens, o=o)
             ctx.save_for_backward(q, k, v, slopes, kv_in)

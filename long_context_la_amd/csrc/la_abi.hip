@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <exception>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -84,6 +85,30 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 22;
 // within the dispatch's 32-bit grid size.
 constexpr int64_t kMaxUnits = int64_t(1) << 20;
 
+// Rows of a strided output (d contiguous elements per (batch, head, token)) are pairwise disjoint:
+// with the dimensions of more than one element sorted by stride, each stride is at least the span
+// of the faster ones.  A zero stride or rows of different heads that overlap would make several
+// workgroups write different values to one element.
+bool rows_disjoint(int64_t d, int64_t s0, int64_t n0, int64_t s1, int64_t n1, int64_t s2, int64_t n2)
+{
+    int64_t st[3] = {s0, s1, s2}, sz[3] = {n0, n1, n2};
+    for (int i = 0; i < 3; ++i)  // insertion sort by stride
+        for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+            const int64_t a = st[j], b = sz[j];
+            st[j] = st[j - 1];
+            sz[j] = sz[j - 1];
+            st[j - 1] = a;
+            sz[j - 1] = b;
+        }
+    int64_t span = d;
+    for (int i = 0; i < 3; ++i) {
+        if (sz[i] <= 1) continue;
+        if (st[i] < span) return false;
+        span += st[i] * (sz[i] - 1);
+    }
+    return true;
+}
+
 la_status check_shape(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)
 {
     if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_INVALID_ARGUMENT, "dtype must be LA_F32 or LA_BF16");
@@ -134,18 +159,51 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     if (!kv || !slopes) return fail(LA_ERR_INVALID_ARGUMENT, "kv and slopes must not be NULL");
     if (chunk_tokens < 0 || (chunk_tokens > 0 && chunk_tokens % kBlock != 0))
         return fail(LA_ERR_INVALID_ARGUMENT, "chunk_tokens must be 0 or a positive multiple of 64");
-    if (ckpt && (ckpt_every <= 0 || ckpt_every % kBlock != 0))
-        return fail(LA_ERR_UNSUPPORTED, "ckpt_every must be a positive multiple of 64");
+    if (ckpt && ckpt_every <= 0) return fail(LA_ERR_INVALID_ARGUMENT, "ckpt_every must be positive");
     if (n == 0) return LA_OK;
     if (!q || !k || !v) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v must not be NULL");
     const int64_t align = (dt == LA_BF16) ? 8 : 4;
     if (sn < d || sb < 0 || sh < 0 || sb % align || sh % align || sn % align)
         return fail(LA_ERR_INVALID_ARGUMENT, "strides must be >= 0, multiples of 16 bytes, stride_n >= d");
     if (sn > kMaxRowStride) return fail(LA_ERR_UNSUPPORTED, "stride_n above 2^22 elements");
+    if (o && !rows_disjoint(d, sn, n, sh, heads, sb, batch))
+        return fail(LA_ERR_INVALID_ARGUMENT, "output rows overlap: the strides map two (batch, head, token) rows onto "
+                                             "shared elements");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) || !aligned16(kv) ||
         (ckpt && !aligned16(ckpt)))
         return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
 
+    if (ckpt && ckpt_every % kBlock != 0) {
+        // Checkpoints inside a tile: the sequence runs as one prefill per checkpoint segment of
+        // ckpt_every tokens (the state carried in kv), each followed by a copy of the state into
+        // its slot.  Multiples of the tile are stored by the tile kernels themselves.
+        s = device_check();
+        if (s != LA_OK) return s;
+        const int64_t n_ck = n / ckpt_every;
+        const size_t esz = dt == LA_BF16 ? 2 : 4;
+        auto at = [&](const void* base, int64_t t) -> const char* {
+            return static_cast<const char*>(base) + (size_t)t * (size_t)sn * esz;
+        };
+        for (int64_t m = 0, t0 = 0; t0 < n; ++m) {
+            const int64_t len = m < n_ck ? ckpt_every : n - t0;
+            // a segment is chunked only when its own chunk workspace fits in the caller's
+            int64_t ct = chunk_tokens;
+            if (ct == 0 && workspace_bytes_for(make_plan(batch, heads, len, d, 0), batch, heads, d) >
+                               (workspace ? workspace_bytes : 0))
+                ct = ((len + kBlock - 1) / kBlock) * kBlock;
+            s = prefill_impl(dt, at(q, t0), at(k, t0), at(v, t0), o ? (void*)at(o, t0) : nullptr, batch, heads, len, d,
+                             sb, sh, sn, slopes, kv, nullptr, 0, ct, workspace, workspace_bytes, stream, fu, rev);
+            if (s != LA_OK) return s;
+            if (m < n_ck) {
+                s = launch_status(launch_state_to_slot(ckpt, kv, batch * heads, (int)d, n_ck, m,
+                                                       static_cast<hipStream_t>(stream)),
+                                  "checkpoint copy");
+                if (s != LA_OK) return s;
+            }
+            t0 += len;
+        }
+        return LA_OK;
+    }
     const Plan p = make_plan(batch, heads, n, d, chunk_tokens);
     const int64_t n_sub = p.n_chunks > 1 ? (p.n_chunks - 1) * p.sub : 0;
     if (batch * heads * (p.n_chunks > n_sub ? p.n_chunks : n_sub) > kMaxUnits)
@@ -258,6 +316,9 @@ la_status backward_impl(la_dtype dt, const void* q, const void* k, const void* v
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk, dv must not be NULL");
     if ((kv_in && !aligned16(kv_in)) || (dkv_out && !aligned16(dkv_out)) || (dkv_in && !aligned16(dkv_in)))
         return fail(LA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
+    if (n > 0 && !rows_disjoint(d, sn, n, sh, heads, sb, batch))
+        return fail(LA_ERR_INVALID_ARGUMENT, "gradient rows overlap: the strides map two (batch, head, token) rows onto "
+                                             "shared elements");
     const Plan p = make_plan(batch, heads, n, d, 0);
     const size_t sbytes = state_bytes(batch, heads, d);
     const size_t need = sbytes + workspace_bytes_for(p, batch, heads, d);
@@ -380,6 +441,57 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
     return LA_OK;
 }
 
+// Page-locked staging for the chunk tables of packed batches: a ring of host buffers per device,
+// each reused only after the event recorded behind its last copy has completed.  The copy is then
+// asynchronous and never reads host memory that has been released.
+struct Staging {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+constexpr int kStageDevices = 16, kStageRing = 8;
+std::mutex g_stage_mu;
+Staging g_stage[kStageDevices][kStageRing];
+unsigned g_stage_next[kStageDevices];
+
+la_status upload_tables(void* dst, const std::vector<int64_t>& tab, hipStream_t st)
+{
+    const size_t bytes = tab.size() * sizeof(int64_t);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStageDevices)
+        return fail(LA_ERR_DEVICE, "table upload: no current device (or more than 16 devices)");
+    std::lock_guard<std::mutex> lock(g_stage_mu);
+    Staging& b = g_stage[dev][g_stage_next[dev]++ % kStageRing];
+    if (b.pending) {
+        const hipError_t e = hipEventSynchronize(b.ev);
+        if (e != hipSuccess) return fail(LA_ERR_DEVICE, std::string("table upload: ") + hipGetErrorString(e));
+        b.pending = false;
+    }
+    if (b.cap < bytes) {
+        if (b.host) (void)hipHostFree(b.host);
+        b.host = nullptr;
+        b.cap = 0;
+        size_t cap = 4096;
+        while (cap < bytes) cap *= 2;
+        if (hipHostMalloc(&b.host, cap, hipHostMallocDefault) != hipSuccess) {
+            b.host = nullptr;
+            return fail(LA_ERR_DEVICE, "table upload: page-locked host allocation failed");
+        }
+        b.cap = cap;
+    }
+    if (!b.ev && hipEventCreateWithFlags(&b.ev, hipEventDisableTiming) != hipSuccess) {
+        b.ev = nullptr;
+        return fail(LA_ERR_DEVICE, "table upload: event creation failed");
+    }
+    memcpy(b.host, tab.data(), bytes);
+    hipError_t e = hipMemcpyAsync(dst, b.host, bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipEventRecord(b.ev, st);
+    if (e != hipSuccess) return fail(LA_ERR_DEVICE, std::string("table upload: ") + hipGetErrorString(e));
+    b.pending = true;
+    return LA_OK;
+}
+
 la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
                               int64_t sh, int64_t sn, const float* slopes, float* kv, int64_t chunk_tokens,
@@ -395,6 +507,9 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     if (sn < d || sh < 0 || sh % align || sn % align)
         return fail(LA_ERR_INVALID_ARGUMENT, "strides must be >= 0, multiples of 16 bytes, stride_n >= d");
     if (sn > kMaxRowStride) return fail(LA_ERR_UNSUPPORTED, "stride_n above 2^22 elements");
+    if (o && !rows_disjoint(d, sn, cu[n_seq], sh, heads, 0, 1))
+        return fail(LA_ERR_INVALID_ARGUMENT, "output rows overlap: the strides map two (token, head) rows onto shared "
+                                             "elements");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) || !aligned16(kv))
         return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
     const size_t need = varlen_workspace_bytes(p, heads, d);
@@ -403,11 +518,8 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     s = device_check();
     if (s != LA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // the chunk and sequence tables go to the front of the workspace (a copy from pageable host
-    // memory: HIP stages it before the call returns, so the host table may go out of scope)
-    s = launch_status(hipMemcpyAsync(workspace, p.tab.data(), p.tab.size() * sizeof(int64_t),
-                                     hipMemcpyHostToDevice, st),
-                      "table upload");
+    // the chunk and sequence tables go to the front of the workspace, through page-locked staging
+    s = upload_tables(workspace, p.tab, st);
     if (s != LA_OK) return s;
     const int64_t* ctab = static_cast<const int64_t*>(workspace);
     FwdArgs a;
@@ -468,6 +580,9 @@ la_status backward_varlen_impl(la_dtype dt, const void* q, const void* k, const 
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk, dv must not be NULL");
     if ((kv_in && !aligned16(kv_in)) || (dkv_out && !aligned16(dkv_out)) || (dkv_in && !aligned16(dkv_in)))
         return fail(LA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
+    if (cu[n_seq] > 0 && !rows_disjoint(d, sn, cu[n_seq], sh, heads, 0, 1))
+        return fail(LA_ERR_INVALID_ARGUMENT, "gradient rows overlap: the strides map two (token, head) rows onto shared "
+                                             "elements");
     const size_t sbytes = state_bytes(n_seq, heads, d);
     if (!workspace || workspace_bytes < backward_varlen_bytes(p, n_seq, heads, d) || !aligned16(workspace))
         return fail(LA_ERR_WORKSPACE, "workspace missing, misaligned or smaller than la_backward_varlen_workspace_size");

@@ -154,6 +154,9 @@ hipError_t launch_scan_sub(float* pref, const float* sub, const float* kv, const
 hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
                               int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream);
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);
+// ckpt[u][m] := kv[u] for the bh states u of d x d floats; ckpt holds n_ckpt slots per state.
+hipError_t launch_state_to_slot(float* ckpt, const float* kv, int64_t bh, int d, int64_t n_ckpt, int64_t m,
+                                hipStream_t stream);
 // dst[u] := scale_u * src[u] (or its transpose), for the bh d x d states u; src == NULL gives
 // zeros.  scale_u = exp(power * s_h), h = u % heads, power in {-1, 0, 1}.  dst may equal src
 // only without the transpose.

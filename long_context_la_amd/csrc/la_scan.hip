@@ -133,6 +133,18 @@ __global__ __launch_bounds__(256) void k_state_prep(float* __restrict__ dst, con
     }
 }
 
+// Checkpoint slot m of every (batch, head): ckpt[u][m] := kv[u] for the bh states u (d2 floats each,
+// n_ckpt slots per state in ckpt).
+__global__ __launch_bounds__(256) void k_state_to_slot(float* __restrict__ ckpt, const float* __restrict__ kv,
+                                                       int64_t bh, int64_t d2, int64_t n_ckpt, int64_t m)
+{
+    const int64_t per4 = d2 / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < bh * per4; i += (int64_t)gridDim.x * 256) {
+        const int64_t u = i / per4, e = i % per4;
+        reinterpret_cast<float4*>(ckpt + (u * n_ckpt + m) * d2)[e] = reinterpret_cast<const float4*>(kv + u * d2)[e];
+    }
+}
+
 // Grid of a grid-stride kernel over `items` threads' worth of work (256 per block), capped so the
 // launch stays far inside the 32-bit work-item count of a dispatch.
 dim3 stride_grid(int64_t items)
@@ -182,6 +194,15 @@ hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, c
     const int64_t threads = n_seq * heads * (d2 / 4);
     const dim3 grid = stride_grid(threads), block(256);
     hipLaunchKernelGGL(k_scan_varlen, grid, block, 0, stream, ws, kv, slopes, stab, n_seq, heads, chunk, d2);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_to_slot(float* ckpt, const float* kv, int64_t bh, int d, int64_t n_ckpt, int64_t m,
+                                hipStream_t stream)
+{
+    const int64_t d2 = (int64_t)d * d;
+    const dim3 grid = stride_grid(bh * (d2 / 4)), block(256);
+    hipLaunchKernelGGL(k_state_to_slot, grid, block, 0, stream, ckpt, kv, bh, d2, n_ckpt, m);
     return hipGetLastError();
 }
 

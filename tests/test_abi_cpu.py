@@ -59,10 +59,19 @@ def test_prefill_validation_codes():
     assert _prefill(sn=64) == la.LA_ERR_INVALID_ARGUMENT            # stride_n < d
     assert _prefill(sn=(1 << 22) + 8) == la.LA_ERR_UNSUPPORTED      # 32-bit tile offsets
     assert _prefill(B=1 << 10, H=(1 << 10) + 1) == la.LA_ERR_UNSUPPORTED   # > 2^20 (batch, head) pairs
-    assert _prefill(N=1 << 30, chunk=64) == la.LA_ERR_UNSUPPORTED          # > 2^20 (head, chunk) items
+    assert _prefill(N=1 << 30, sh=128 << 30, sb=8 * (128 << 30), chunk=64) == la.LA_ERR_UNSUPPORTED  # > 2^20 items
     assert _prefill(q=ctypes.c_void_p((1 << 20) + 2)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned
-    assert _prefill(ckpt=FAKE, ckpt_every=100) == la.LA_ERR_UNSUPPORTED
-    assert _prefill(ckpt=FAKE, ckpt_every=0) == la.LA_ERR_UNSUPPORTED
+    assert _prefill(ckpt=FAKE, ckpt_every=0) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(ckpt=FAKE, ckpt_every=-64) == la.LA_ERR_INVALID_ARGUMENT
+    # output rows must be pairwise disjoint: stride 0 over heads, or heads closer than d
+    assert _prefill(sh=0) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(sh=64, sb=1 << 24) == la.LA_ERR_INVALID_ARGUMENT
+    assert _prefill(B=2, sb=0) == la.LA_ERR_INVALID_ARGUMENT
+    assert "overlap" in la.la_last_error()
+    # ... which inputs may break when there is no output (state only)
+    if not gpu_available():
+        assert _prefill(sh=0, o=None) == la.LA_ERR_DEVICE
+        assert _prefill(ckpt=FAKE, ckpt_every=100) == la.LA_ERR_DEVICE   # any positive interval is valid
     assert _prefill(chunk=100) == la.LA_ERR_INVALID_ARGUMENT
     assert "64" in la.la_last_error()
     # chunked plan without (enough) workspace
@@ -166,6 +175,7 @@ def test_varlen_validation_codes():
     assert _varlen([10, 20], d=64, sh=64, sn=512, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE  # bf16 d = 64: valid
     assert _varlen([10, 20], sn=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], sn=(1 << 22) + 8) == la.LA_ERR_UNSUPPORTED
+    assert _varlen([10, 20], sh=0) == la.LA_ERR_INVALID_ARGUMENT                   # output heads overlap
     assert _varlen([1 << 30, 20], chunk=64) == la.LA_ERR_UNSUPPORTED        # > 2^20 (chunk, head) items
     assert _varlen([10, 20], chunk=100) == la.LA_ERR_INVALID_ARGUMENT
     assert _varlen([10, 20], ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
@@ -228,6 +238,7 @@ def test_backward_validation_codes():
     assert _backward(dkv_out=ctypes.c_void_p((1 << 20) + 4)) == la.LA_ERR_INVALID_ARGUMENT  # misaligned state
     assert _backward(ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
     assert _backward(ws_bytes=need - 16) == la.LA_ERR_WORKSPACE
+    assert _backward(sh=0) == la.LA_ERR_INVALID_ARGUMENT                          # gradient rows overlap
     if not gpu_available():
         assert _backward(ws_bytes=need) == la.LA_ERR_DEVICE
         assert _backward(N=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) == la.LA_ERR_DEVICE
