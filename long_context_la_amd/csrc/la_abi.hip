@@ -145,12 +145,11 @@ la_status check_fusion(const la_fusion* fu, const void* o)
     return LA_OK;
 }
 
-la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
-                       int64_t batch, int64_t heads, int64_t n, int64_t d,
-                       int64_t sb, int64_t sh, int64_t sn, const float* slopes, float* kv,
-                       float* ckpt, int64_t ckpt_every, int64_t chunk_tokens,
-                       void* workspace, size_t workspace_bytes, void* stream, const la_fusion* fu = nullptr,
-                       bool rev = false)
+// Host-side argument checks of a prefill (everything but the workspace and the device).
+la_status prefill_checks(la_dtype dt, const void* q, const void* k, const void* v, const void* o,
+                         int64_t batch, int64_t heads, int64_t n, int64_t d,
+                         int64_t sb, int64_t sh, int64_t sn, const float* slopes, const float* kv,
+                         const float* ckpt, int64_t ckpt_every, int64_t chunk_tokens, const la_fusion* fu)
 {
     la_status s = check_shape(dt, batch, heads, n, d);
     if (s != LA_OK) return s;
@@ -172,6 +171,19 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) || !aligned16(kv) ||
         (ckpt && !aligned16(ckpt)))
         return fail(LA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    return LA_OK;
+}
+
+la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                       int64_t batch, int64_t heads, int64_t n, int64_t d,
+                       int64_t sb, int64_t sh, int64_t sn, const float* slopes, float* kv,
+                       float* ckpt, int64_t ckpt_every, int64_t chunk_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream, const la_fusion* fu = nullptr,
+                       bool rev = false)
+{
+    la_status s = prefill_checks(dt, q, k, v, o, batch, heads, n, d, sb, sh, sn, slopes, kv, ckpt, ckpt_every,
+                                 chunk_tokens, fu);
+    if (s != LA_OK || n == 0) return s;
 
     if (ckpt && ckpt_every % kBlock != 0) {
         // Checkpoints inside a tile: the sequence runs as one prefill per checkpoint segment of
