@@ -37,7 +37,7 @@ EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_si
             "la_prefill_varlen_chunk_tokens", "la_prefill_varlen", "la_prefill_varlen_ex", "la_decode",
             "la_prefill_fused", "la_decode_fused", "la_backward_workspace_size", "la_backward",
             "la_backward_varlen_workspace_size", "la_backward_varlen",
-            "la_status_string", "la_last_error"]
+            "la_prefill_noalloc", "la_status_string", "la_last_error"]
 
 LA_SILU_Q = 1
 LA_SILU_K = 2
@@ -80,6 +80,8 @@ def lib():
     L.la_prefill_workspace_size_ex.argtypes = [i32, i64, i64, i64, i64, i64]
     L.la_prefill.restype = i32
     L.la_prefill.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, p, sz, p]
+    L.la_prefill_noalloc.restype = i32
+    L.la_prefill_noalloc.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, p]
     L.la_prefill_ex.restype = i32
     L.la_prefill_ex.argtypes = [i32, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, p, p, p, i64, i64, p, sz, p]
     L.la_prefill_varlen_workspace_size.restype = sz

@@ -302,6 +302,58 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
                          "normalisation launch");
 }
 
+// ---------------------------------------------------------------- prefill without allocation
+// Device scratch for la_prefill_noalloc: the chunk states of a prefill live in this file-scope
+// array instead of a caller-supplied workspace.  Every GPU the library runs on holds its own copy
+// (until the process ends); host code reaches it only through the device address taken once per
+// device with hipGetSymbolAddress -- in host code the array's name is not a device address.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kScratchDevices = 16;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+la_status scratch_for_current_device(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+        (void)hipGetLastError();
+        return fail(LA_ERR_DEVICE, "no current device (or more than 16 devices) for the scratch array");
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(LA_ERR_DEVICE, std::string("scratch array address: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LA_OK;
+}
+
+la_status prefill_noalloc_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o, int64_t batch,
+                               int64_t heads, int64_t n, int64_t d, int64_t sb, int64_t sh, int64_t sn,
+                               const float* slopes, float* kv, float* ckpt, int64_t ckpt_every, void* stream)
+{
+    la_status s = prefill_checks(dt, q, k, v, o, batch, heads, n, d, sb, sh, sn, slopes, kv, ckpt, ckpt_every, 0,
+                                 nullptr);
+    if (s != LA_OK || n == 0) return s;
+    const size_t need = workspace_bytes_for(make_plan(batch, heads, n, d, 0), batch, heads, d);
+    if (need > kScratchBytes)
+        return fail(LA_ERR_UNSUPPORTED, "this shape needs " + std::to_string(need) +
+                                            " bytes of chunk states; la_prefill_noalloc holds " +
+                                            std::to_string(kScratchBytes));
+    s = device_check();
+    if (s != LA_OK) return s;
+    void* ws = nullptr;
+    s = scratch_for_current_device(&ws);
+    if (s != LA_OK) return s;
+    // the chunk states are written before they are read within one call, so nothing needs clearing
+    return prefill_impl(dt, q, k, v, o, batch, heads, n, d, sb, sh, sn, slopes, kv, ckpt, ckpt_every, 0, ws,
+                        kScratchBytes, stream);
+}
+
 // ---------------------------------------------------------------- backward pass
 // Gradients of a loss through the recurrence (the reverse state recurrence that the training side
 // of LASP+, page "MiniMax-01: Scaling Foundation Models with Lightning Attention | Summary",
@@ -743,6 +795,21 @@ la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, v
 {
     return la_prefill_ex(dt, q, k, v, o, batch, heads, n, d, stride_b, stride_h, stride_n, slopes, kv, ckpt,
                          ckpt_every, 0, workspace, workspace_bytes, stream);
+}
+
+la_status la_prefill_noalloc(la_dtype dt, const void* q, const void* k, const void* v, void* o,
+                             int64_t batch, int64_t heads, int64_t n, int64_t d,
+                             int64_t stride_b, int64_t stride_h, int64_t stride_n,
+                             const float* slopes, float* kv, float* ckpt, int64_t ckpt_every, void* stream)
+{
+    try {
+        return prefill_noalloc_impl(dt, q, k, v, o, batch, heads, n, d, stride_b, stride_h, stride_n, slopes, kv,
+                                    ckpt, ckpt_every, stream);
+    } catch (const std::exception& e) {
+        return fail(LA_ERR_INTERNAL, e.what());
+    } catch (...) {
+        return fail(LA_ERR_INTERNAL, "unknown error");
+    }
 }
 
 la_status la_decode_fused(la_dtype dt, const void* q, const void* k, const void* v, void* o,
