@@ -78,7 +78,7 @@ def test_bf16_ragged(device, N):
 
 @pytest.mark.parametrize("N", [1, 63, 65, 1000])
 def test_bf16_d64_ragged(device, N):
-    # bfloat16 at d = 64: the VALU tile kernel with bfloat16 loads and stores
+    # bfloat16 at d = 64: the MFMA tile kernel instantiated for the head dimension 64
     check_prefill(35, 2, 3, N, 64, "bf16", np.array([0.5, 2.0 ** -3, 2.0 ** -7], np.float32), device)
 
 
@@ -301,7 +301,7 @@ def test_n_zero_is_noop(device):
 
 
 def test_bf16_d64_chunked_with_states(device):
-    # chunks and sub-chunk summaries through the VALU tile kernel's summary mode
+    # chunks and sub-chunk summaries through the MFMA tile kernel's sliced summary mode (d = 64)
     kv0 = np.random.default_rng(10).standard_normal((1, 2, 64, 64)).astype(np.float32)
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 2, 9000, 64) < 9000
     check_prefill(36, 1, 2, 9000, 64, "bf16", SL2, device, kv_in=kv0)

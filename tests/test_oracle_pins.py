@@ -493,3 +493,30 @@ def test_backward_planted_mistakes_are_caught(kind):
 
     assert caught(*_mutant_backward(q, k, v, do, slopes, kv, g, kind))
     assert not caught(*_mutant_backward(q, k, v, do, slopes, kv, g, "correct"))
+
+
+def test_p18_nan_and_inf_stay_in_their_head_row_and_column():
+    """The recurrence's own confinement, which the GPU test mirrors: a NaN in one head's q
+    reaches only that head's output row (q is not part of the state); an Inf in another head's v
+    reaches only that head's value column, from its token on, in outputs and state; every other
+    head, row and column is unchanged bit for bit."""
+    rng = np.random.default_rng(80)
+    H, N, d = 4, 40, 8
+    q, k, v = (rng.standard_normal((1, H, N, d)).astype(np.float32) for _ in range(3))
+    s = np.array([0.9, 0.25, 2.0 ** -8, 0.0])
+    o0, kv0, _ = oracle.recurrent(q, k, v, s)
+    q1, v1 = q.copy(), v.copy()
+    q1[0, 1, 17, 2] = np.nan
+    v1[0, 2, 9, 5] = np.inf
+    with np.errstate(invalid="ignore"):
+        o1, kv1, _ = oracle.recurrent(q1, k, v1, s)
+    for h in (0, 3):
+        assert np.array_equal(o1[0, h], o0[0, h]) and np.array_equal(kv1[0, h], kv0[0, h])
+    rows = np.arange(N) != 17
+    assert np.array_equal(o1[0, 1, rows], o0[0, 1, rows]) and np.isnan(o1[0, 1, 17]).all()
+    assert np.array_equal(kv1[0, 1], kv0[0, 1])
+    cols = np.arange(d) != 5
+    assert np.array_equal(o1[0, 2][:, cols], o0[0, 2][:, cols])
+    assert np.array_equal(o1[0, 2, :9], o0[0, 2, :9])
+    assert not np.isfinite(o1[0, 2, 9:, 5]).any()
+    assert np.array_equal(kv1[0, 2][:, cols], kv0[0, 2][:, cols]) and not np.isfinite(kv1[0, 2][:, 5]).any()
