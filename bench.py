@@ -24,8 +24,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (datasheet); the run's peaks come from device_peaks()
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (datasheet), replaced at run time
 MODEL_TILE = 256               # the pages' tile: flop model 4*B*d + 4*d^2 per token-head
 BYTES_PER_TOKEN_HEAD = 4 * 128 * 2   # q, k, v read + o write, bf16, d = 128
 BWD_BYTES_PER_TOKEN_HEAD = 7 * 128 * 2  # backward: q, k, v, dO read + dq, dk, dv write, bf16
@@ -40,35 +40,35 @@ MIXED_LENGTHS = [50, 50] + [1] * 18
 
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_SOURCE = os.path.join(ROOT, "long_context_la_amd", "csrc", "la_prefill_bf16.hip")
+FLUSH_BYTES = 512 << 20   # written between timed steps of the cache-sized legs (256 MB Infinity Cache)
 
 
 def source_digest(path=PREFILL_SOURCE):
-    import hashlib
+    from long_context_la_amd import profiling
 
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    return profiling.source_digest(path)
 
 
 def measured_traffic(workload):
     """HBM bytes per prefill launch from the committed rocprofv3 counter summary (FETCH_SIZE and
     WRITE_SIZE per dispatch, each scaled by the same counter's reading for a plain copy of known
     size), or None when there is none for this workload or the kernel source changed since."""
-    path = os.path.join(PROFILES, f"prefill_{workload}_hbm_traffic.txt")
-    if not os.path.exists(path):
+    from long_context_la_amd import profiling
+
+    return profiling.current_value(os.path.join(PROFILES, f"prefill_{workload}_hbm_traffic.txt"), "traffic_bytes")
+
+
+def measured_mfma():
+    """Counter-based MFMA utilisation and cycles per tile of the full-layer prefill kernel from the
+    committed rocprofv3 summary, or None when the kernel source changed since it was taken."""
+    from long_context_la_amd import profiling
+
+    path = os.path.join(PROFILES, "prefill_full_mfma_util.txt")
+    util = profiling.current_value(path, "mfma_utilisation")
+    if util is None:
         return None
-    vals = {}
-    for line in open(path):
-        if "=" in line and not line.lstrip().startswith("#"):
-            key, _, val = line.partition("=")
-            vals[key.strip()] = val.strip()
-    try:
-        if vals.get("kernel_source_sha256_16") != source_digest():
-            return None
-        fetch = float(vals["fetch_kib_per_dispatch"]) * 1024 * float(vals["copy_fetch_factor"])
-        write = float(vals["write_kib_per_dispatch"]) * 1024 * float(vals["copy_write_factor"])
-    except (KeyError, ValueError):
-        return None
-    return fetch + write
+    return {"mfma_utilisation": util, "cycles_per_tile": profiling.current_value(path, "cycles_per_tile"),
+            "source": "profiles/prefill_full_mfma_util.txt"}
 
 
 def copy_probe(device, gib=4, reps=3):
@@ -141,7 +141,7 @@ def make_prefill_inputs(w, device, head_group=8):
     return out
 
 
-def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True):
+def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True, flush=False):
     import torch
 
     import long_context_la_amd as la
@@ -168,22 +168,38 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    # the prefill kernel alone (state init excluded), timed on the same stream
+    # flush: before each timed step (outside its events) a 512 MB buffer is written, so a workload
+    # about the size of the 256 MB Infinity Cache starts every step from HBM
+    junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device) if flush else None
+    if flush:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            junk.fill_(1)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    else:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+    # the prefill kernel(s) alone (state init excluded), timed on the same stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:
         la.la_state_init(kv)
+        if flush:
+            junk.fill_(1)
         a.record(stream)
         la.la_prefill(q, k, v, slopes, kv, o=o, ckpt=ck, ckpt_every=w.ckpt_every, workspace=ws)
         b.record(stream)
     torch.cuda.synchronize()
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    del junk
     n_chunks = -(-w.n // la.la_prefill_chunk_tokens(la.LA_BF16, w.batch, w.heads, w.n, w.d))
     varlen = None
     if with_varlen and w.batch == 1 and sum(VARLEN_LENGTHS) == w.n:
@@ -413,11 +429,35 @@ def time_decode(w, steps, device, prefix_slab=16):
     return us
 
 
+def cpu_baseline_decode(wd, steps=10):
+    """The oracle's decode step (fp64, OpenMP over the units) on all 128 x 64 units of the decode
+    workload for `steps` steps from a random state, extrapolated to the 1000 timed steps.  The cost
+    of a step does not depend on the state's values, so the 4096-token prefix is not replayed."""
+    import oracle
+    import synth
+
+    B, H, d = wd.batch, wd.heads, wd.d
+    rng = np.random.default_rng(0)
+    state = rng.standard_normal((B, H, d, d))
+    toks = [synth.bf16_bits_to_f32(synth.generate(t, wd.seed, d, nb=B, nh=H, t0=wd.n, nt=steps, dtype="bf16"))
+            for t in (synth.Q, synth.K, synth.V)]
+    slopes = wd.slopes()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        oracle.decode_step(*(np.ascontiguousarray(x[:, :, s]) for x in toks), slopes, state)
+    dt = (time.perf_counter() - t0) / steps
+    return {"us_per_step": dt * 1e6, "GB/s": B * H * DECODE_BYTES_PER_UNIT / dt / 1e9,
+            "seconds_for_1000_steps": dt * 1000,
+            "sample": f"{steps} steps of all {B * H} units (fp64), extrapolated to 1000"}
+
+
 def cpu_baseline(w, target_s=15.0):
     """The fp64 oracle (token recurrence, OpenMP over heads) on the host cores, on a bounded
     sample of the workload: all heads, the first T tokens, T sized to ~target_s of CPU work."""
     import oracle
     import synth
+
+    from long_context_la_amd import profiling
 
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
 
@@ -432,8 +472,9 @@ def cpu_baseline(w, target_s=15.0):
     dt = run(T)
     T = int(min(w.n, max(256, T * target_s / max(dt, 1e-3))) // 256 * 256)
     dt = run(T)
+    cpu = profiling.cpu_description()
     return {"value": w.batch * T / dt, "unit": "tokens/s", "cores": min(cores, w.batch * w.heads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu["model"], "logical_cpus": cpu["logical_cpus"],
             "sample": f"all {w.heads} heads x first {T} tokens of the {w.n}-token workload "
                       f"(fp64 recurrence, {dt:.1f} s)"}
 
@@ -455,6 +496,8 @@ def main():
                     help="skip the informational share (8 x 32K), long (8 x 1M) and d = 64 full-layer prefill legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (counter calibration for the traffic figure)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only run the 128 x 64 decode leg (for its counter passes)")
     args = ap.parse_args()
     set_settle(args.settle_s)
     if args.gpus != 1:
@@ -472,6 +515,18 @@ def main():
         copy_probe(device)
         return
     la.lib()
+    from long_context_la_amd import profiling
+
+    global PEAK_HBM_GBS, PEAK_BF16_TFLOPS
+    peaks = profiling.device_peaks()
+    PEAK_HBM_GBS, PEAK_BF16_TFLOPS = peaks["hbm_gbs"], peaks["bf16_tflops"]
+    if args.decode_only:
+        wd = synth.WORKLOADS["decode"]
+        us = time_decode(wd, args.decode_steps, device)
+        gbs = wd.batch * wd.heads * DECODE_BYTES_PER_UNIT / (us * 1e-6) / 1e9
+        print(json.dumps({"decode_only": True, "us_per_step": us, "GB/s": gbs, "frac": gbs / PEAK_HBM_GBS}),
+              flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     ms, kernel_ms, n_chunks, varlen, backward = time_prefill(w, args.steps, args.warmup, device,
                                                              with_backward=not args.no_backward,
@@ -503,6 +558,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": alg_bytes / (kernel_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": measured_traffic(w.name)},
+        "peaks": peaks,
+        "counters": measured_mfma() if w.name == "full" else None,
     }
     if varlen is not None:
         result["varlen"] = varlen
@@ -512,14 +569,21 @@ def main():
         others = {}
         for name, steps in (("share", 20), ("long", 3), ("full_d64", 20)):
             wo = synth.WORKLOADS[name]
-            ms_o, kms_o, nch_o, _, _ = time_prefill(wo, steps, 1, device, with_backward=False, with_varlen=False)
+            # the share workload (268 MB moved) is about the size of the Infinity Cache: each of its
+            # timed steps starts from a flushed cache
+            flush = name == "share"
+            ms_o, kms_o, nch_o, _, _ = time_prefill(wo, steps, 1, device, with_backward=False, with_varlen=False,
+                                                    flush=flush)
             th = wo.batch * wo.heads * wo.n
-            log(f"prefill {name}: {ms_o:.3f} ms/step, kernel(s) {kms_o:.3f} ms, {nch_o} chunk(s)")
+            log(f"prefill {name}: {ms_o:.3f} ms/step, kernel(s) {kms_o:.3f} ms, {nch_o} chunk(s)"
+                + (" (cache flushed before each step)" if flush else ""))
             others[name] = {"workload": f"batch {wo.batch}, {wo.heads} heads, d={wo.d}, N={wo.n}, bf16, "
                                         f"{nch_o} chunks (LASP+ summaries + prefix combine)",
                             "ms_per_step": ms_o, "kernel_ms": kms_o, "tokens_per_s": wo.batch * wo.n / (ms_o * 1e-3),
                             "hbm_frac": 4 * wo.d * 2 * th / (kms_o * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                            "mfma_frac": model_flops_per_token_head(wo.d) * th / (ms_o * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                            "mfma_frac": model_flops_per_token_head(wo.d) * th / (ms_o * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                            "cache_flushed_between_steps": flush,
+                            "traffic": measured_traffic(name) if wo.d == 128 else None}
         result["other_workloads"] = others
     if not args.no_decode:
         result["mixed_batch"] = time_mixed(device)
@@ -534,6 +598,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w)
+        if not args.no_decode:
+            result["cpu_baseline"]["decode"] = cpu_baseline_decode(synth.WORKLOADS["decode"])
     print(json.dumps(result), flush=True)
 
 

@@ -45,6 +45,7 @@ def _summary(path, digest, fetch_kib, write_kib, ff, wf):
         f.write(f"kernel_source_sha256_16 = {digest}\n")
         f.write(f"fetch_kib_per_dispatch = {fetch_kib}\nwrite_kib_per_dispatch = {write_kib}\n")
         f.write(f"copy_fetch_factor = {ff}\ncopy_write_factor = {wf}\n")
+        f.write(f"traffic_bytes = {(fetch_kib * ff + write_kib * wf) * 1024}\n")
 
 
 def test_traffic_is_read_only_for_the_profiled_source(tmp_path, monkeypatch):
@@ -66,7 +67,8 @@ def test_committed_traffic_summary_is_well_formed():
             key, _, val = line.partition("=")
             vals[key.strip()] = val.strip()
     assert len(vals["kernel_source_sha256_16"]) == 16
-    for key in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_factor", "copy_write_factor"):
+    for key in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_factor", "copy_write_factor",
+                "traffic_bytes", "algorithmic_bytes"):
         assert float(vals[key]) > 0
     # whichever source it was taken on, the summary names the command that made it
     assert "rocprofv3 --pmc FETCH_SIZE" in open(path).read()
