@@ -63,6 +63,21 @@ typedef enum {
     LA_F32 = 0,  /* q, k, v, o are float32 */
     LA_BF16 = 1  /* q, k, v, o are bfloat16; accumulation and state are float32 */
 } la_dtype;
+/*
+ * Value range of LA_BF16 prefills with outputs.  Their products run on float16
+ * matrix-core operands.  q, k and v are converted exactly for magnitudes in
+ * [2^-14, 65504) (larger ones overflow to Inf).  The decay-weighted score block
+ * q k^T, v weighted by its decay, and the float32 state enter their products
+ * scaled by 2^-8, so each score and each state element must stay below
+ * 65504 * 2^8 (about 1.7e7) in magnitude.  Operands round to 2^-11 relative
+ * down to 2^-14 (inputs) and 2^-6 (scaled quantities); below that float16 keeps
+ * fewer bits, which costs nothing where a small operand sits beside large ones
+ * but loses relative precision for a head whose inputs are all far below unit
+ * scale (the operation is linear in q and in v: scale them up and the outputs
+ * down).  The float32 state itself is accumulated and stored at full precision.
+ * State-only prefills (o == NULL) and chunk summaries keep bfloat16 operands
+ * with a hi + lo split of the float32 ones, over float32's whole range.
+ */
 
 /*
  * Optional prologue and epilogue fused into the attention kernels.  Section 2.2

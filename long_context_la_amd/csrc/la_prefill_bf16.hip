@@ -9,13 +9,21 @@
 //     P[r][c]   = lambda^(r-c) S[r][c]  (c <= r), 0 otherwise
 //     O         = diag(lambda^(r+1)) Q KV + P V    (MFMA, k = feature dim, then k = token)
 //     KV       <- lambda^L KV + K^T (W V),  W = diag(lambda^(L-1-c))   (MFMA, k = token)
-// Inputs are bfloat16.  P, W V and the operand copy of the state are carried
-// as bfloat16 hi + lo pairs (x = hi + lo, both parts bf16, two MFMAs per
-// product), which keeps them to about float32 precision: rounding them to a
-// single bf16 costs about 2e-2 of the output RMS on fast-decaying heads (P),
-// 1.6e-2 of the state RMS (W V), and up to 2.5e-2 of the output RMS right
-// after a large incoming state (KV).  Every product accumulates in float32 and
-// the state itself stays float32 in accumulators.
+// Inputs are bfloat16; every product accumulates in float32 and the state itself
+// stays float32 in accumulators.  The operands that are not inputs -- P, W V and
+// the operand copy of the state -- need more than bf16's 8 mantissa bits:
+// rounded to one bf16 they cost about 2e-2 of the output RMS on fast-decaying
+// heads (P), 1.6e-2 of the state RMS (W V) and up to 2.5e-2 of the output RMS
+// after a large incoming state (KV).  With outputs, every product therefore runs
+// on float16 operands (v_mfma_f32_16x16x32_f16): 11 mantissa bits keep each of
+// those roundings near 2.4e-4 relative, with one MFMA per product, and the bf16
+// inputs convert to float16 exactly.  Float16's range is met by scaling: P, W V
+// and the state (held scaled in its accumulators) carry a factor 2^-8 that the
+// output and the stored states take back.  Inputs must stay below 65504 in
+// magnitude, scores and state elements below 65504 * 2^8 (bf16 activations of
+// a working model are far below both).  Without
+// outputs (state-only and chunk-summary modes) the state update keeps bfloat16
+// operands, with W V as a hi + lo pair (x = hi + lo, two MFMAs).
 //
 // Decomposition.  A workgroup owns one (batch, head, chunk, slice of 32 value
 // columns): both the state's columns and the outputs' columns split by value
@@ -34,13 +42,13 @@
 // consecutive value columns of one row and stages them with one 8-byte LDS
 // write before the 16-byte global stores.  State waves 4..7: the global
 // loads and LDS staging of K and V, the decay-weighted W V, and the state
-// update, with the state's 16 tiles of 16x16 split 6/5/3/2 so that each SIMD
-// (output wave w + state wave w) issues the same 48 MFMAs per tile.  The state
-// waves publish the state after tile b (bf16 hi/lo copy in LDS) for the output
-// waves' inter term of tile b+1.  Without outputs (state-only modes) the
+// update, with the state's 16 tiles of 16x16 split 8/5/2/1 (more state work
+// on the SIMDs whose output waves own the earlier, lighter query rows).  The
+// state waves publish the state after tile b (a float16 copy in LDS) for the
+// output waves' inter term of tile b+1.  Without outputs (state-only modes) the
 // kernel runs the four state waves alone.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, C 16x16 fp32; lane l holds
+// MFMA: v_mfma_f32_16x16x32_f16 / _bf16 (A 16x32, B 32x16, C 16x16 fp32; lane l holds
 // A row l%16 / B column l%16 and 8 k-values of group g = l/16; C column l%16,
 // rows 4g..4g+3).  The sum over k does not care which k a slot holds as long
 // as A and B agree, which is used twice:
@@ -150,6 +158,33 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Float16 operands: 8 values per lane, the same lane layout as the bf16 products.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 mfma_h(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                   0);
+}
+// Two floats -> packed float16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t cvt2h(float a, float b)
+{
+    const f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// 8 packed bf16 values -> 8 packed float16 values (exact for |x| < 65504; the bit patterns are
+// returned in a bf16x8 so they travel through the same registers and LDS tiles).
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 x)
+{
+    const uint32_t in[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = cvt2h(__uint_as_float(in[e] << 16), __uint_as_float(in[e] & 0xffff0000u));
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+// Scale of the float16 operands that are not inputs (P, W V, the state).
+constexpr float kHalfScale = 0.00390625f;  // 2^-8
+
 __device__ __forceinline__ void wave_lds_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -191,6 +226,9 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     static_assert(!(GATE && REV), "the reverse walk has no epilogue");
     static_assert(D == 64 || D == 128, "head dimension 64 or 128");
     constexpr bool OUT = MODE == kModeOut;
+    // float16 products with outputs; bf16 (W V as hi + lo) in the state-only and summary modes
+    constexpr bool F16 = OUT;
+    constexpr float kSc = F16 ? kHalfScale : 1.f, kScInv = F16 ? 1.f / kHalfScale : 1.f;
     constexpr int KS = kKS<D>;
     constexpr int NQ = D / 32;   // 32-feature steps of a score or inter product; also Q, K loads per lane
     constexpr int CPR = D / 8, CPR_LOG = D == 128 ? 4 : 3;  // 16-byte chunks per row of Q or K
@@ -201,8 +239,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     __shared__ __attribute__((aligned(16))) u16 sV[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sVWh[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sVWl[2][BK * VS];
-    __shared__ __attribute__((aligned(16))) u16 sSh[2][SW * D];
-    __shared__ __attribute__((aligned(16))) u16 sSl[2][SW * D];
+    __shared__ __attribute__((aligned(16))) u16 sS[2][SW * D];
     __shared__ __attribute__((aligned(16))) u16 sO[BK * OS];
 
     int64_t group;
@@ -266,15 +303,17 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     // ------------------------------------------------------------------ state waves
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
     // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), D/8 of them, of state
-    // wave sw: [first, first + count).  With outputs the split evens out the MFMAs per SIMD (output
-    // wave w + state wave w): 6/5/3/2 of 16 at d = 128, 3/3/1/1 of 8 at d = 64; equal shares without.
+    // wave sw: [first, first + count).  With outputs the split moves state work off the SIMDs whose
+    // output waves own the later query rows (more score blocks): 8/5/2/1 of 16 at d = 128 (measured
+    // 1.2% faster than 6/5/3/2, which evens out the MFMA counts), 3/3/1/1 of 8 at d = 64; equal shares
+    // without outputs.
     auto st_first = [](int sw) constexpr {
         if (!OUT) return (D / 32) * sw;
-        return D == 128 ? (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14) : (sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7);
+        return D == 128 ? (sw == 0 ? 0 : sw == 1 ? 8 : sw == 2 ? 13 : 15) : (sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7);
     };
     auto st_count = [](int sw) constexpr {
         if (!OUT) return D / 32;
-        return D == 128 ? (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2) : (sw <= 1 ? 3 : 1);
+        return D == 128 ? (sw == 0 ? 8 : sw == 1 ? 5 : sw == 2 ? 2 : 1) : (sw <= 1 ? 3 : 1);
     };
 
     auto load_kv = [&](KR& R, int tile) __attribute__((always_inline)) {
@@ -292,41 +331,52 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     // tile's end) and lambda^L for the state, for a full tile and for the last tile, the only one
     // that can be shorter.
     const int L_last = tile_len(n_tiles - 1);
-    const float wt_full = decay_pow(nsl, (float)(BK - 1 - (st_id >> 2)));
+    const float wt_full = decay_pow(nsl, (float)(BK - 1 - (st_id >> 2))) * kSc;
     const float dl_full = decay_pow(nsl, (float)BK);
-    const float wt_last = ((st_id >> 2) < L_last) ? decay_pow(nsl, (float)(L_last - 1 - (st_id >> 2))) : 0.f;
+    const float wt_last = ((st_id >> 2) < L_last) ? decay_pow(nsl, (float)(L_last - 1 - (st_id >> 2))) * kSc : 0.f;
     const float dl_last = decay_pow(nsl, (float)L_last);
-    // K and V rows into LDS buffer `buf`, with the decay-weighted V as bf16 hi + lo.
+    // K and V rows into LDS buffer `buf` with the decay-weighted V: float16 (and W V scaled by 2^-8)
+    // with outputs, else bf16 with W V as a hi + lo pair.
     auto stage_tile = [&](const KR& R, int buf, int tile) __attribute__((always_inline)) {
         const int L = tile_len(tile);
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
             const int c = st_id + 256 * ((m + slice) & (NQ - 1));
-            *reinterpret_cast<uint4*>(&sK[buf][(c >> CPR_LOG) * KS + 8 * (c & (CPR - 1))]) = silu_k ? silu8(R.k[m]) : R.k[m];
+            const uint4 kx = silu_k ? silu8(R.k[m]) : R.k[m];
+            *reinterpret_cast<uint4*>(&sK[buf][(c >> CPR_LOG) * KS + 8 * (c & (CPR - 1))]) = F16 ? bf16x8_to_f16(kx) : kx;
         }
         const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
         const uint4 vx = silu_v ? silu8(R.v) : R.v;
-        *reinterpret_cast<uint4*>(&sV[buf][off]) = vx;
         const float wt = (L == BK) ? wt_full : wt_last;
         const uint32_t in[4] = {vx.x, vx.y, vx.z, vx.w};
-        uint32_t hi[4], lo[4];
+        if constexpr (F16) {
+            uint32_t hv[4], hw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
-        *reinterpret_cast<uint4*>(&sVWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        *reinterpret_cast<uint4*>(&sVWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            for (int e = 0; e < 4; ++e) {
+                const float a = bits_to_f32(in[e] & 0xffffu), b = hi_to_f32(in[e]);
+                hv[e] = cvt2h(a, b);
+                hw[e] = cvt2h(a * wt, b * wt);
+            }
+            *reinterpret_cast<uint4*>(&sV[buf][off]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+            *reinterpret_cast<uint4*>(&sVWh[buf][off]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        } else {
+            *reinterpret_cast<uint4*>(&sV[buf][off]) = vx;
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
+            *reinterpret_cast<uint4*>(&sVWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4*>(&sVWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
     };
-    // state copy for the inter term: KV^T[value col][key row], 4 consecutive key rows per lane
+    // float16 state copy for the inter term (the accumulators hold the state scaled by 2^-8):
+    // KV^T[value col][key row], 4 consecutive key rows per lane
     auto write_state_copy = [&](auto swc, const f32x4* st, int buf) __attribute__((always_inline)) {
         constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
 #pragma unroll
         for (int k = 0; k < C; ++k) {
             const int q = F + k;
-            uint32_t h01, l01, h23, l23;
-            split2(st[k][0], st[k][1], h01, l01);
-            split2(st[k][2], st[k][3], h23, l23);
             const int off = ss_off<D>(16 * (q & 1) + lr, 16 * (q >> 1) + 4 * g);
-            *reinterpret_cast<uint2*>(&sSh[buf][off]) = make_uint2(h01, h23);
-            *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(l01, l23);
+            *reinterpret_cast<uint2*>(&sS[buf][off]) = make_uint2(cvt2h(st[k][0], st[k][1]), cvt2h(st[k][2], st[k][3]));
         }
     };
     auto store_state = [&](auto swc, const f32x4* st, float* dst) __attribute__((always_inline)) {
@@ -336,7 +386,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const int q = F + k;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                dst[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] = st[k][t];
+                dst[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] = st[k][t] * kScInv;
         }
     };
     auto load_state = [&](auto swc, f32x4* st, const float* src) __attribute__((always_inline)) {
@@ -346,7 +396,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const int q = F + k;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                st[k][t] = src ? src[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] : 0.f;
+                st[k][t] = src ? src[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] * kSc : 0.f;
         }
     };
     // KV <- lambda^L KV + K^T (W V) on this wave's state tiles
@@ -366,7 +416,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             for (int jt = 0; jt < 2; ++jt) {
                 const int o = (k0 + tr_row) * VS + 16 * jt + tr_col;
                 vh[ks][jt] = join(lds_tr(&sVWh[buf][o]), lds_tr(&sVWh[buf][o + 4 * VS]));
-                vl[ks][jt] = join(lds_tr(&sVWl[buf][o]), lds_tr(&sVWl[buf][o + 4 * VS]));
+                if constexpr (!F16) vl[ks][jt] = join(lds_tr(&sVWl[buf][o]), lds_tr(&sVWl[buf][o + 4 * VS]));
             }
 #pragma unroll
             for (int n = 0; n < NIT; ++n) {
@@ -380,14 +430,19 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 #pragma unroll
             for (int k = 0; k < C; ++k) {
                 const int q = F + k;
-                st[k] = mfma(ka[ks][(q >> 1) - IT0], vh[ks][q & 1], st[k]);
-                st[k] = mfma(ka[ks][(q >> 1) - IT0], vl[ks][q & 1], st[k]);
+                if constexpr (F16) {
+                    st[k] = mfma_h(ka[ks][(q >> 1) - IT0], vh[ks][q & 1], st[k]);
+                } else {
+                    st[k] = mfma(ka[ks][(q >> 1) - IT0], vh[ks][q & 1], st[k]);
+                    st[k] = mfma(ka[ks][(q >> 1) - IT0], vl[ks][q & 1], st[k]);
+                }
             }
     };
 
     // ------------------------------------------------------------------ output waves
-    // dmask[ct][t] = lambda^(r - c) for query r = 16w + lr and key c = 16ct + 4g + t (0 if c > r);
-    // drow = lambda^(r+1) for this lane's output row r = 16w + lr.
+    // dmask[ct][t] = 2^-8 lambda^(r - c) for query r = 16w + lr and key c = 16ct + 4g + t (0 if c > r);
+    // drow = lambda^(r+1) for this lane's output row r = 16w + lr.  P and the state copy both carry
+    // the factor 2^-8, which the output takes back once before it is stored.
     float dmask[4][4], drow = 0.f;
     if (OUT && !is_state) {
 #pragma unroll
@@ -395,7 +450,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int e = 16 * (w - ct) + lr - 4 * g - t;
-                dmask[ct][t] = (e >= 0) ? decay_pow(nsl, (float)e) : 0.f;
+                dmask[ct][t] = (e >= 0) ? decay_pow(nsl, (float)e) * kHalfScale : 0.f;
             }
         drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
@@ -412,7 +467,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int64_t t0 = tile_row0(tile);
         bf16x8 qf[NQ];
 #pragma unroll
-        for (int ks = 0; ks < NQ; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, silu_q ? silu8(R.q[ks]) : R.q[ks]);
+        for (int ks = 0; ks < NQ; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, bf16x8_to_f16(silu_q ? silu8(R.q[ks]) : R.q[ks]));
         // the gate values of this lane's outputs (row 16W + lr, columns 16jt + 4g..+3), read early
         // so the loads are long done when the products are
         uint2 gx[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
@@ -425,15 +480,12 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // Issue every LDS operand read of the inter and score products up front (the fence keeps
         // the scheduler from sinking them next to their MFMAs, which would expose each read's
         // latency in turn).
-        bf16x8 sh[2][NQ], sl[2][NQ], kop[W + 1][NQ];
+        bf16x8 sh[2][NQ], kop[W + 1][NQ];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) {
-                const int off = ss_off<D>(16 * jt + lr, 32 * ((ks + slice) & (NQ - 1)) + 8 * g);
-                sh[jt][ks] = lds8(&sSh[buf][off]);
-                sl[jt][ks] = lds8(&sSl[buf][off]);
-            }
+            for (int ks = 0; ks < NQ; ++ks)
+                sh[jt][ks] = lds8(&sS[buf][ss_off<D>(16 * jt + lr, 32 * ((ks + slice) & (NQ - 1)) + 8 * g)]);
 #pragma unroll
         for (int ct = 0; ct <= W; ++ct)
 #pragma unroll
@@ -447,10 +499,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int jt = 0; jt < 2; ++jt) {
             acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) {
-                acc[jt] = mfma(sh[jt][ks], qf[ks], acc[jt]);
-                acc[jt] = mfma(sl[jt][ks], qf[ks], acc[jt]);
-            }
+            for (int ks = 0; ks < NQ; ++ks) acc[jt] = mfma_h(sh[jt][ks], qf[ks], acc[jt]);
         }
         // intra-tile scores S^T for key tiles 0..W (later key tiles are fully masked)
         float p[4][4];
@@ -459,7 +508,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             if (ct <= W) {
                 f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NQ; ++ks) s = mfma(kop[ct][ks], qf[ks], s);
+                for (int ks = 0; ks < NQ; ++ks) s = mfma_h(kop[ct][ks], qf[ks], s);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) p[ct][t] = s[t] * dmask[ct][t];
             } else {
@@ -487,19 +536,15 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
 #pragma unroll
         for (int k2 = 0; k2 < NK2; ++k2) {
-            uint32_t hh[4], ll[4];
-            split2(p[2 * k2][0], p[2 * k2][1], hh[0], ll[0]);
-            split2(p[2 * k2][2], p[2 * k2][3], hh[1], ll[1]);
-            split2(p[2 * k2 + 1][0], p[2 * k2 + 1][1], hh[2], ll[2]);
-            split2(p[2 * k2 + 1][2], p[2 * k2 + 1][3], hh[3], ll[3]);
-            const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
-            const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+            const bf16x8 ph = __builtin_bit_cast(
+                bf16x8, make_uint4(cvt2h(p[2 * k2][0], p[2 * k2][1]), cvt2h(p[2 * k2][2], p[2 * k2][3]),
+                                   cvt2h(p[2 * k2 + 1][0], p[2 * k2 + 1][1]), cvt2h(p[2 * k2 + 1][2], p[2 * k2 + 1][3])));
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                acc[jt] = mfma(vop[k2][jt], ph, acc[jt]);
-                acc[jt] = mfma(vop[k2][jt], pl, acc[jt]);
-            }
+            for (int jt = 0; jt < 2; ++jt) acc[jt] = mfma_h(vop[k2][jt], ph, acc[jt]);
         }
+        // undo the 2^-8 of P and of the state copy
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) acc[jt] *= 1.f / kHalfScale;
         // gate in float32, so the output is rounded to bf16 once
         if constexpr (GATE)
 #pragma unroll
@@ -609,7 +654,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 // but for a summary alone it makes each slice re-read all of K.  Here one workgroup owns a whole
 // (sequence, head, sub-chunk) and its full d x d state: K and V are read once.  Per 64-token tile
 // the state is decayed by lambda^L and K^T (W V) is added, with W V staged as bf16 hi + lo as in
-// the tile kernel.  Eight waves split the 8 x 8 state tiles of 16 x 16 as 2 key-row halves x 4
+// the tile kernel's summary modes.  Eight waves split the 8 x 8 state tiles of 16 x 16 as 2 key-row halves x 4
 // value-column quarters.  No SiLU prologue (the fused path keeps the sliced summaries).
 struct SumRegs { uint4 k[2]; uint4 v[2]; };  // 16-byte chunks tid and tid + 512 of the K and V tiles
 

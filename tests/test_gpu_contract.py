@@ -255,3 +255,30 @@ def test_expanded_inputs_through_autograd(device):
     assert torch.equal(grads[0][0], grads[1][0])
     assert torch.equal(grads[0][1], grads[1][1])
     assert torch.isfinite(grads[0][1]).all()
+
+
+
+@pytest.mark.parametrize("chunk", [0, 512])
+@pytest.mark.parametrize("scale,kv_scale", [((40.0, 40.0, 500.0), 1e6), ((2.0 ** -4,) * 3, 1e-2)])
+def test_bf16_products_far_from_unit_scale(device, chunk, scale, kv_scale):
+    """The bf16 path's products take float16 operands (inputs converted exactly; scores, weighted
+    values and the state scaled by 2^-8).  Inputs up to a few thousand with states of order 1e6,
+    and inputs of order 2^-4 with states of order 1e-2, stay inside that format's normal range
+    where it matters and meet the bf16 bar."""
+    import torch
+
+    B, H, N, d = 1, 2, 2000, 128
+    exact, _ = inputs(58, B, H, N, d, "bf16")
+    scaled = [synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x * c)) for x, c in zip(exact, scale)]
+    q, k, v = (to_device(synth.f32_to_bf16_bits(x), "bf16", device) for x in scaled)
+    kv0 = (np.random.default_rng(59).standard_normal((B, H, d, d)) * kv_scale).astype(np.float32)
+    kv = torch.from_numpy(kv0).to(device)
+    o = torch.empty_like(q)
+    slopes = np.array([2.0 ** -2, 2.0 ** -12], dtype=np.float32)    # the second head keeps kv0
+    la.la_prefill(q, k, v, torch.from_numpy(slopes).to(device), kv, o=o, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    o_ref, kv_ref, _ = oracle.recurrent(*scaled, slopes, kv_in=kv0)
+    if kv_scale > 1:
+        assert max(float(np.abs(x).max()) for x in scaled) > 2000 and np.abs(kv_ref).max() > 1e6
+    assert_close(to_host(o), o_ref, "bf16", "O", stored="bf16")
+    assert_close(kv.cpu().numpy(), kv_ref, "bf16", "KV")
