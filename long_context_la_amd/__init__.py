@@ -121,6 +121,8 @@ def _rows_disjoint(t) -> bool:
     """True when no two rows (all indices but the last, which is contiguous) of the strided tensor
     t share an element: with the dimensions longer than one sorted by stride, each stride is at
     least the span of the faster ones (the same rule the library applies to its outputs)."""
+    if t.is_contiguous():
+        return True
     span = t.shape[-1]
     for st, n in sorted((st, n) for st, n in zip(t.stride()[:-1], t.shape[:-1]) if n > 1):
         if st < span:
@@ -150,9 +152,10 @@ def _check_slopes(slopes, heads):
 
 
 def _check_qkv(q, k, v, ndim):
-    if q.dim() != ndim:
+    shape, dtype = q.shape, q.dtype
+    if len(shape) != ndim:
         raise ValueError(f"q, k, v must be {ndim}-D")
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+    if k.shape != shape or v.shape != shape or k.dtype != dtype or v.dtype != dtype:
         raise ValueError("q, k, v must share shape and dtype")
     if not _same_strides(k, q) or not _same_strides(v, q) or q.stride(-1) != 1:
         raise ValueError("q, k, v must share strides with a contiguous last dimension")
@@ -195,7 +198,8 @@ def _on_stream(stream, *ts):
 def _same_strides(t, ref) -> bool:
     """Same element strides as ref on every dimension longer than 1 (a dimension of size 1 is
     never stepped over, so its stride does not matter; the library takes ref's)."""
-    return all(a == b for a, b, n in zip(t.stride(), ref.stride(), ref.shape) if n > 1)
+    ts, rs = t.stride(), ref.stride()
+    return ts == rs or all(a == b for a, b, n in zip(ts, rs, ref.shape) if n > 1)
 
 
 def la_status_string(status: int) -> str:
@@ -339,10 +343,11 @@ def la_prefill_varlen(q, k, v, slopes, kv, cu_seqlens, o=None, workspace=None, c
         raise ValueError("cu_seqlens[-1] must equal the packed token count")
     _check_f32(kv, (n_seq, H, d, d), "kv")
     _require_cuda(q, k, v, slopes, kv, o, workspace)
-    need = int(lib().la_prefill_varlen_workspace_size_ex(dt, n_seq, cu, H, d, chunk_tokens))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        _on_stream(stream, workspace)
+    if workspace is None:
+        need = int(lib().la_prefill_varlen_workspace_size_ex(dt, n_seq, cu, H, d, chunk_tokens))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _on_stream(stream, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sn, sh, _ = q.stride()
     st = lib().la_prefill_varlen_ex(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), n_seq, cu, H, d, sh, sn,
