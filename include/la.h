@@ -36,9 +36,11 @@
  *     and la_backward enqueue kernels only (no allocation, memset or host
  *     copy), so a sequence of them can be captured into a graph and replayed;
  *     the replay reads the tensors at the captured addresses.
- *     la_prefill_varlen enqueues a host-to-device copy of its chunk tables
- *     from a page-locked staging buffer that later calls reuse, so it must not
- *     be captured.
+ *     la_prefill_varlen and la_backward_varlen pass chunk tables of up to 384
+ *     int64 words (5 per chunk, 2 per sequence, 3 more per sequence of at most
+ *     8 tokens) by value in kernel arguments, which a captured graph replays;
+ *     larger tables are copied from a page-locked staging buffer that later
+ *     calls reuse, so such calls must not be captured.
  */
 #ifndef LIGHTNING_LA_H
 #define LIGHTNING_LA_H
@@ -75,8 +77,9 @@ typedef enum {
  * but loses relative precision for a head whose inputs are all far below unit
  * scale (the operation is linear in q and in v: scale them up and the outputs
  * down).  The float32 state itself is accumulated and stored at full precision.
- * State-only prefills (o == NULL) and chunk summaries keep bfloat16 operands
- * with a hi + lo split of the float32 ones, over float32's whole range.
+ * State-only prefills (o == NULL), chunk summaries and the backward pass keep
+ * bfloat16 operands with a hi + lo split of the float32 ones, over float32's
+ * whole range.
  */
 
 /*
@@ -293,7 +296,10 @@ la_status la_decode(la_dtype dt, const void* q, const void* k, const void* v, vo
  *   dq_t = do_t KV_t^T,  dk_t = v_t G_t^T,  dv_t = k_t G_t,  dkv_in = lambda G_0.
  * The slopes are constants (no gradient).  Computed as three runs of the
  * prefill kernels (one forward, two walking the sequence backwards), so it
- * costs about three prefills.
+ * costs about three prefills.  With LA_BF16 the runs use full-range operands
+ * (bfloat16 hi + lo pairs, not the forward's float16): gradients of a loss over
+ * many elements are often far below float16's normal range, and every
+ * magnitude bfloat16 holds is computed to the same relative precision.
  *   q, k, v, dout       : inputs of the forward pass and dL/dO, layout and
  *                         strides as for la_prefill (read-only, may alias).
  *   kv_in               : the forward pass's incoming state, or NULL (zero).

@@ -179,7 +179,7 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
                        int64_t sb, int64_t sh, int64_t sn, const float* slopes, float* kv,
                        float* ckpt, int64_t ckpt_every, int64_t chunk_tokens,
                        void* workspace, size_t workspace_bytes, void* stream, const la_fusion* fu = nullptr,
-                       bool rev = false)
+                       bool rev = false, bool wide = false)
 {
     la_status s = prefill_checks(dt, q, k, v, o, batch, heads, n, d, sb, sh, sn, slopes, kv, ckpt, ckpt_every,
                                  chunk_tokens, fu);
@@ -204,7 +204,7 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
                                (workspace ? workspace_bytes : 0))
                 ct = ((len + kBlock - 1) / kBlock) * kBlock;
             s = prefill_impl(dt, at(q, t0), at(k, t0), at(v, t0), o ? (void*)at(o, t0) : nullptr, batch, heads, len, d,
-                             sb, sh, sn, slopes, kv, nullptr, 0, ct, workspace, workspace_bytes, stream, fu, rev);
+                             sb, sh, sn, slopes, kv, nullptr, 0, ct, workspace, workspace_bytes, stream, fu, rev, wide);
             if (s != LA_OK) return s;
             if (m < n_ck) {
                 s = launch_status(launch_state_to_slot(ckpt, kv, batch * heads, (int)d, n_ck, m,
@@ -251,6 +251,7 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     a.act = ff & (LA_SILU_Q | LA_SILU_K | LA_SILU_V);
     a.gate = ((ff & LA_GATE) && !(ff & LA_NORM)) ? fu->gate : nullptr;  // gate alone: in the store
     a.rev = rev ? 1 : 0;
+    a.wide = (rev || wide) ? 1 : 0;
     const int64_t bh = batch * heads;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool mfma = dt == LA_BF16;  // the bf16 MFMA kernels; float32 runs on the VALU tile kernel
@@ -399,11 +400,12 @@ la_status backward_impl(la_dtype dt, const void* q, const void* k, const void* v
         return launch_status(launch_state_prep(dst, src, slopes, bh, heads, (int)d, tr, power, st), "state set-up launch");
     };
     if (n == 0) return dkv_in ? prep(dkv_in, dkv_out, false, 0) : LA_OK;
-    // dQ: (dO, V, K) forward from KV_in^T
+    // dQ: (dO, V, K) forward from KV_in^T.  Every pass runs on full-range operands: dO can be
+    // far smaller than activations.
     s = prep(S, kv_in, true, 0);
     if (s == LA_OK)
         s = prefill_impl(dt, dout, v, k, dq, batch, heads, n, d, sb, sh, sn, slopes, S, nullptr, 0, 0, chunk_ws,
-                         chunk_bytes, stream);
+                         chunk_bytes, stream, nullptr, false, true);
     // dK: (V, dO, Q) backwards from (dL/dKV_final / lambda)^T
     if (s == LA_OK) s = prep(S, dkv_out, true, dkv_out ? 1 : 0);
     if (s == LA_OK)
@@ -505,8 +507,21 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
     return LA_OK;
 }
 
-// Page-locked staging for the chunk tables of packed batches: a ring of host buffers per device,
-// each reused only after the event recorded behind its last copy has completed.  The copy is then
+// Small tables travel by value in the arguments of a one-block kernel that writes them to the
+// workspace: no copy call, nothing on the host to keep alive, and a captured graph replays the
+// same values.  kTableArgWords * 8 bytes stays well inside the 4 KiB kernel-argument limit.
+constexpr int kTableArgWords = 384;
+struct TableArg {
+    int64_t n;
+    int64_t v[kTableArgWords];
+};
+__global__ __launch_bounds__(128) void k_write_table(int64_t* dst, TableArg t)
+{
+    for (int64_t i = threadIdx.x; i < t.n; i += blockDim.x) dst[i] = t.v[i];
+}
+
+// Larger tables go through page-locked staging: a ring of host buffers per device, each reused
+// only after the event recorded behind its last copy has completed.  The copy is then
 // asynchronous and never reads host memory that has been released.
 struct Staging {
     void* host = nullptr;
@@ -521,6 +536,13 @@ unsigned g_stage_next[kStageDevices];
 
 la_status upload_tables(void* dst, const std::vector<int64_t>& tab, hipStream_t st)
 {
+    if (tab.size() <= (size_t)kTableArgWords) {
+        TableArg t;
+        t.n = (int64_t)tab.size();
+        memcpy(t.v, tab.data(), tab.size() * sizeof(int64_t));
+        hipLaunchKernelGGL(k_write_table, dim3(1), dim3(128), 0, st, static_cast<int64_t*>(dst), t);
+        return launch_status(hipGetLastError(), "table upload");
+    }
     const size_t bytes = tab.size() * sizeof(int64_t);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStageDevices)
@@ -559,7 +581,8 @@ la_status upload_tables(void* dst, const std::vector<int64_t>& tab, hipStream_t 
 la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                               int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
                               int64_t sh, int64_t sn, const float* slopes, float* kv, int64_t chunk_tokens,
-                              void* workspace, size_t workspace_bytes, void* stream, bool rev = false)
+                              void* workspace, size_t workspace_bytes, void* stream, bool rev = false,
+                              bool wide = false)
 {
     VarPlan p;
     la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, chunk_tokens, p);
@@ -604,6 +627,7 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     a.stab = ctab + 5 * p.total_chunks;
     a.groups = p.total_chunks * heads;
     a.rev = rev ? 1 : 0;
+    a.wide = (rev || wide) ? 1 : 0;
     auto run = [&](int mode) -> hipError_t {
         return dt == LA_BF16 ? launch_fwd_bf16(a, (int)d, mode, st) : launch_fwd_f32(a, (int)d, mode, st);
     };
@@ -662,7 +686,8 @@ la_status backward_varlen_impl(la_dtype dt, const void* q, const void* k, const 
     };
     s = prep(S, kv_in, true, 0);
     if (s == LA_OK)
-        s = prefill_varlen_impl(dt, dout, v, k, dq, n_seq, cu, heads, d, sh, sn, slopes, S, 0, vws, vbytes, stream);
+        s = prefill_varlen_impl(dt, dout, v, k, dq, n_seq, cu, heads, d, sh, sn, slopes, S, 0, vws, vbytes, stream,
+                                false, true);
     if (s == LA_OK) s = prep(S, dkv_out, true, dkv_out ? 1 : 0);
     if (s == LA_OK)
         s = prefill_varlen_impl(dt, v, dout, q, dk, n_seq, cu, heads, d, sh, sn, slopes, S, 0, vws, vbytes, stream, true);

@@ -75,6 +75,9 @@ struct FwdArgs {
     // Reverse walk: token t of the recurrence is memory row rev_end-1-t of its sequence (see
     // Work); outputs are written to the same rows.  Used by the backward pass.
     int rev;
+    // Full-range products for the outputs (bf16 hi + lo operands instead of float16): the
+    // backward's passes, whose gradient inputs can lie far below float16's normal range.
+    int wide;
 };
 
 // SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), in float32.

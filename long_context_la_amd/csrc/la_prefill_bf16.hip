@@ -21,9 +21,12 @@
 // and the state (held scaled in its accumulators) carry a factor 2^-8 that the
 // output and the stored states take back.  Inputs must stay below 65504 in
 // magnitude, scores and state elements below 65504 * 2^8 (bf16 activations of
-// a working model are far below both).  Without
-// outputs (state-only and chunk-summary modes) the state update keeps bfloat16
-// operands, with W V as a hi + lo pair (x = hi + lo, two MFMAs).
+// a working model are far below both).  Gradients are not: the backward's
+// passes, whose inputs include dL/dO, run a full-range instantiation (WIDE)
+// with bf16 inputs as they are and P, W V and the state copy as bf16 hi + lo
+// pairs (x = hi + lo, two MFMAs per product), which covers float32's range.
+// Without outputs (state-only and chunk-summary modes) the state update keeps
+// bfloat16 operands, with W V as a hi + lo pair.
 //
 // Decomposition.  A workgroup owns one (batch, head, chunk, slice of 32 value
 // columns): both the state's columns and the outputs' columns split by value
@@ -220,14 +223,17 @@ template <int D> struct KVRegs { uint4 k[D / 32]; uint4 v; };
 // memory row n-1-t), the order of the reverse state recurrence of the backward pass.  ACT enables
 // the SiLU prologue (which of q, k, v is chosen at run time); without it no activation code is
 // compiled in, since untaken branches inside the tile loops still cost about 10% here.
-template <int MODE, bool GATE, bool REV, bool ACT, int D>
+template <int MODE, bool GATE, bool REV, bool ACT, int D, bool WIDE>
 __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
     static_assert(!(GATE && REV), "the reverse walk has no epilogue");
     static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+    static_assert(!WIDE || MODE == kModeOut, "full-range operands matter only with outputs");
     constexpr bool OUT = MODE == kModeOut;
-    // float16 products with outputs; bf16 (W V as hi + lo) in the state-only and summary modes
-    constexpr bool F16 = OUT;
+    // float16 products with outputs; bf16 (P, W V and the state copy as hi + lo pairs) with WIDE
+    // outputs and in the state-only and summary modes
+    constexpr bool F16 = OUT && !WIDE;
+    constexpr float kPSc = F16 ? kHalfScale : 1.f;  // scale of P
     constexpr float kSc = F16 ? kHalfScale : 1.f, kScInv = F16 ? 1.f / kHalfScale : 1.f;
     constexpr int KS = kKS<D>;
     constexpr int NQ = D / 32;   // 32-feature steps of a score or inter product; also Q, K loads per lane
@@ -240,6 +246,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     __shared__ __attribute__((aligned(16))) u16 sVWh[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sVWl[2][BK * VS];
     __shared__ __attribute__((aligned(16))) u16 sS[2][SW * D];
+    __shared__ __attribute__((aligned(16))) u16 sSl[OUT && !F16 ? 2 : 1][OUT && !F16 ? SW * D : 8];
     __shared__ __attribute__((aligned(16))) u16 sO[BK * OS];
 
     int64_t group;
@@ -304,16 +311,19 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
     // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), D/8 of them, of state
     // wave sw: [first, first + count).  With outputs the split moves state work off the SIMDs whose
-    // output waves own the later query rows (more score blocks): 8/5/2/1 of 16 at d = 128 (measured
-    // 1.2% faster than 6/5/3/2, which evens out the MFMA counts), 3/3/1/1 of 8 at d = 64; equal shares
-    // without outputs.
+    // output waves own the later query rows (more score blocks): at d = 128, 8/5/2/1 of 16 with
+    // float16 operands (measured 1.2% faster than 6/5/3/2) and 6/5/3/2 with hi + lo pairs (which evens
+    // out their MFMA counts and keeps the registers of a pair within budget); 3/3/1/1 of 8 at d = 64;
+    // equal shares without outputs.
     auto st_first = [](int sw) constexpr {
         if (!OUT) return (D / 32) * sw;
-        return D == 128 ? (sw == 0 ? 0 : sw == 1 ? 8 : sw == 2 ? 13 : 15) : (sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7);
+        if (D == 64) return sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7;
+        return F16 ? (sw == 0 ? 0 : sw == 1 ? 8 : sw == 2 ? 13 : 15) : (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14);
     };
     auto st_count = [](int sw) constexpr {
         if (!OUT) return D / 32;
-        return D == 128 ? (sw == 0 ? 8 : sw == 1 ? 5 : sw == 2 ? 2 : 1) : (sw <= 1 ? 3 : 1);
+        if (D == 64) return sw <= 1 ? 3 : 1;
+        return F16 ? (sw == 0 ? 8 : sw == 1 ? 5 : sw == 2 ? 2 : 1) : (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2);
     };
 
     auto load_kv = [&](KR& R, int tile) __attribute__((always_inline)) {
@@ -368,15 +378,23 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             *reinterpret_cast<uint4*>(&sVWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
     };
-    // float16 state copy for the inter term (the accumulators hold the state scaled by 2^-8):
-    // KV^T[value col][key row], 4 consecutive key rows per lane
+    // state copy for the inter term, KV^T[value col][key row], 4 consecutive key rows per lane:
+    // float16 (the accumulators hold the state scaled by 2^-8), or a bf16 hi + lo pair when WIDE
     auto write_state_copy = [&](auto swc, const f32x4* st, int buf) __attribute__((always_inline)) {
         constexpr int F = st_first(decltype(swc)::value), C = st_count(decltype(swc)::value);
 #pragma unroll
         for (int k = 0; k < C; ++k) {
             const int q = F + k;
             const int off = ss_off<D>(16 * (q & 1) + lr, 16 * (q >> 1) + 4 * g);
-            *reinterpret_cast<uint2*>(&sS[buf][off]) = make_uint2(cvt2h(st[k][0], st[k][1]), cvt2h(st[k][2], st[k][3]));
+            if constexpr (F16) {
+                *reinterpret_cast<uint2*>(&sS[buf][off]) = make_uint2(cvt2h(st[k][0], st[k][1]), cvt2h(st[k][2], st[k][3]));
+            } else {
+                uint32_t h01, l01, h23, l23;
+                split2(st[k][0], st[k][1], h01, l01);
+                split2(st[k][2], st[k][3], h23, l23);
+                *reinterpret_cast<uint2*>(&sS[buf][off]) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2*>(&sSl[buf][off]) = make_uint2(l01, l23);
+            }
         }
     };
     auto store_state = [&](auto swc, const f32x4* st, float* dst) __attribute__((always_inline)) {
@@ -440,9 +458,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     };
 
     // ------------------------------------------------------------------ output waves
-    // dmask[ct][t] = 2^-8 lambda^(r - c) for query r = 16w + lr and key c = 16ct + 4g + t (0 if c > r);
-    // drow = lambda^(r+1) for this lane's output row r = 16w + lr.  P and the state copy both carry
-    // the factor 2^-8, which the output takes back once before it is stored.
+    // dmask[ct][t] = 2^-8 lambda^(r - c) (lambda^(r - c) when WIDE) for query r = 16w + lr and key
+    // c = 16ct + 4g + t (0 if c > r); drow = lambda^(r+1) for this lane's output row r = 16w + lr.
+    // With float16 operands P and the state copy both carry the factor 2^-8, which the output takes
+    // back once before it is stored.
     float dmask[4][4], drow = 0.f;
     if (OUT && !is_state) {
 #pragma unroll
@@ -450,7 +469,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int e = 16 * (w - ct) + lr - 4 * g - t;
-                dmask[ct][t] = (e >= 0) ? decay_pow(nsl, (float)e) * kHalfScale : 0.f;
+                dmask[ct][t] = (e >= 0) ? decay_pow(nsl, (float)e) * kPSc : 0.f;
             }
         drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
@@ -467,7 +486,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         const int64_t t0 = tile_row0(tile);
         bf16x8 qf[NQ];
 #pragma unroll
-        for (int ks = 0; ks < NQ; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, bf16x8_to_f16(silu_q ? silu8(R.q[ks]) : R.q[ks]));
+        for (int ks = 0; ks < NQ; ++ks) {
+            const uint4 qx = silu_q ? silu8(R.q[ks]) : R.q[ks];
+            qf[ks] = __builtin_bit_cast(bf16x8, F16 ? bf16x8_to_f16(qx) : qx);
+        }
         // the gate values of this lane's outputs (row 16W + lr, columns 16jt + 4g..+3), read early
         // so the loads are long done when the products are
         uint2 gx[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
@@ -480,12 +502,15 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // Issue every LDS operand read of the inter and score products up front (the fence keeps
         // the scheduler from sinking them next to their MFMAs, which would expose each read's
         // latency in turn).
-        bf16x8 sh[2][NQ], kop[W + 1][NQ];
+        bf16x8 sh[2][NQ], sl[2][NQ], kop[W + 1][NQ];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks)
-                sh[jt][ks] = lds8(&sS[buf][ss_off<D>(16 * jt + lr, 32 * ((ks + slice) & (NQ - 1)) + 8 * g)]);
+            for (int ks = 0; ks < NQ; ++ks) {
+                const int off = ss_off<D>(16 * jt + lr, 32 * ((ks + slice) & (NQ - 1)) + 8 * g);
+                sh[jt][ks] = lds8(&sS[buf][off]);
+                if constexpr (!F16) sl[jt][ks] = lds8(&sSl[buf][off]);
+            }
 #pragma unroll
         for (int ct = 0; ct <= W; ++ct)
 #pragma unroll
@@ -499,7 +524,14 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int jt = 0; jt < 2; ++jt) {
             acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) acc[jt] = mfma_h(sh[jt][ks], qf[ks], acc[jt]);
+            for (int ks = 0; ks < NQ; ++ks) {
+                if constexpr (F16) {
+                    acc[jt] = mfma_h(sh[jt][ks], qf[ks], acc[jt]);
+                } else {
+                    acc[jt] = mfma(sh[jt][ks], qf[ks], acc[jt]);
+                    acc[jt] = mfma(sl[jt][ks], qf[ks], acc[jt]);
+                }
+            }
         }
         // intra-tile scores S^T for key tiles 0..W (later key tiles are fully masked)
         float p[4][4];
@@ -508,7 +540,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             if (ct <= W) {
                 f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NQ; ++ks) s = mfma_h(kop[ct][ks], qf[ks], s);
+                for (int ks = 0; ks < NQ; ++ks) s = F16 ? mfma_h(kop[ct][ks], qf[ks], s) : mfma(kop[ct][ks], qf[ks], s);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) p[ct][t] = s[t] * dmask[ct][t];
             } else {
@@ -536,15 +568,32 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
 #pragma unroll
         for (int k2 = 0; k2 < NK2; ++k2) {
-            const bf16x8 ph = __builtin_bit_cast(
-                bf16x8, make_uint4(cvt2h(p[2 * k2][0], p[2 * k2][1]), cvt2h(p[2 * k2][2], p[2 * k2][3]),
-                                   cvt2h(p[2 * k2 + 1][0], p[2 * k2 + 1][1]), cvt2h(p[2 * k2 + 1][2], p[2 * k2 + 1][3])));
+            if constexpr (F16) {
+                const bf16x8 ph = __builtin_bit_cast(
+                    bf16x8, make_uint4(cvt2h(p[2 * k2][0], p[2 * k2][1]), cvt2h(p[2 * k2][2], p[2 * k2][3]),
+                                       cvt2h(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
+                                       cvt2h(p[2 * k2 + 1][2], p[2 * k2 + 1][3])));
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) acc[jt] = mfma_h(vop[k2][jt], ph, acc[jt]);
+                for (int jt = 0; jt < 2; ++jt) acc[jt] = mfma_h(vop[k2][jt], ph, acc[jt]);
+            } else {
+                uint32_t hh[4], ll[4];
+                split2(p[2 * k2][0], p[2 * k2][1], hh[0], ll[0]);
+                split2(p[2 * k2][2], p[2 * k2][3], hh[1], ll[1]);
+                split2(p[2 * k2 + 1][0], p[2 * k2 + 1][1], hh[2], ll[2]);
+                split2(p[2 * k2 + 1][2], p[2 * k2 + 1][3], hh[3], ll[3]);
+                const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
+                const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    acc[jt] = mfma(vop[k2][jt], ph, acc[jt]);
+                    acc[jt] = mfma(vop[k2][jt], pl, acc[jt]);
+                }
+            }
         }
         // undo the 2^-8 of P and of the state copy
+        if constexpr (F16)
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) acc[jt] *= 1.f / kHalfScale;
+            for (int jt = 0; jt < 2; ++jt) acc[jt] *= 1.f / kHalfScale;
         // gate in float32, so the output is rounded to bf16 once
         if constexpr (GATE)
 #pragma unroll
@@ -808,12 +857,14 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
                 dst[(16 * (it0 + i) + 4 * g + t) * D + 16 * (jt0 + j) + lr] = st[2 * i + j][t];
 }
 
-template <bool GATE, bool REV, bool ACT, int D>
+template <bool GATE, bool REV, bool ACT, int D, bool WIDE>
 void launch_mode(const FwdArgs& a, int mode, dim3 grid, hipStream_t stream)
 {
-    if (mode == kModeOut) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT, D>), grid, dim3(512), 0, stream, a);
-    else if (mode == kModeState) hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT, D>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT, D>), grid, dim3(256), 0, stream, a);
+    if (mode == kModeOut)
+        hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT, D, WIDE>), grid, dim3(512), 0, stream, a);
+    else if (mode == kModeState)
+        hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT, D, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT, D, false>), grid, dim3(256), 0, stream, a);
 }
 
 template <int D>
@@ -821,11 +872,13 @@ void launch_d(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
     const bool gate = a.gate && mode == kModeOut, act = a.act != 0;
-    if (a.rev) launch_mode<false, true, false, D>(a, mode, grid, stream);  // the backward pass: plain inputs
-    else if (gate && act) launch_mode<true, false, true, D>(a, mode, grid, stream);
-    else if (gate) launch_mode<true, false, false, D>(a, mode, grid, stream);
-    else if (act) launch_mode<false, false, true, D>(a, mode, grid, stream);
-    else launch_mode<false, false, false, D>(a, mode, grid, stream);
+    // the backward's passes: plain inputs, full-range operands
+    if (a.rev) launch_mode<false, true, false, D, true>(a, mode, grid, stream);
+    else if (a.wide) launch_mode<false, false, false, D, true>(a, mode, grid, stream);
+    else if (gate && act) launch_mode<true, false, true, D, false>(a, mode, grid, stream);
+    else if (gate) launch_mode<true, false, false, D, false>(a, mode, grid, stream);
+    else if (act) launch_mode<false, false, true, D, false>(a, mode, grid, stream);
+    else launch_mode<false, false, false, D, false>(a, mode, grid, stream);
 }
 
 }  // namespace

@@ -19,16 +19,22 @@ def _torch():
     return torch
 
 
-def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, layout="bhnd"):
+def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, layout="bhnd", grad_scale=1.0):
+    """grad_scale (a power of two, so the scaling is exact) multiplies dL/dO and dL/dKV_final."""
     torch = _torch()
     exact, raw = inputs(seed, B, H, N, d, dtype)
     dout_raw = synth.generate(synth.V, seed + 500, d, nb=B, nh=H, nt=N, dtype=dtype)
     dout_exact = synth.bf16_bits_to_f32(dout_raw) if dtype == "bf16" else dout_raw
+    if grad_scale != 1.0:
+        dout_exact = (dout_exact * np.float32(grad_scale)).astype(np.float32)
+        dout_raw = synth.f32_to_bf16_bits(dout_exact) if dtype == "bf16" else dout_exact
+        if dtype == "bf16":
+            assert np.array_equal(synth.bf16_bits_to_f32(dout_raw), dout_exact)
     if slopes is None:
         slopes = np.array([2.0 ** (-2 - 3 * h) for h in range(H)], dtype=np.float32)
     rng = np.random.default_rng(seed + 1)
     kv_in = rng.standard_normal((B, H, d, d)).astype(np.float32) if states else None
-    dkv_out = rng.standard_normal((B, H, d, d)).astype(np.float32) if states else None
+    dkv_out = (rng.standard_normal((B, H, d, d)) * grad_scale).astype(np.float32) if states else None
 
     def dev(x):
         t = to_device(x, dtype, device)
@@ -53,6 +59,14 @@ def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, l
 @pytest.mark.parametrize("states", [False, True])
 def test_backward_small(device, dtype, d, states):
     run_backward(1, 2, 200, d, dtype, device, states=states)
+
+
+@pytest.mark.parametrize("grad_log2", [-24, -40])
+@pytest.mark.parametrize("N,d", [(300, 128), (5000, 128), (700, 64)])
+def test_backward_tiny_gradients_bf16(device, grad_log2, N, d):
+    # gradients of a mean loss over a large tensor sit far below float16's normal range (2^-14):
+    # every backward pass runs on full-range (bf16 hi + lo) operands and keeps the bf16 bar
+    run_backward(1, 2, N, d, "bf16", device, states=True, seed=95, grad_scale=2.0 ** grad_log2)
 
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 129])
@@ -126,6 +140,12 @@ def test_backward_varlen_packed(device, dtype, d):
     run_backward_varlen(lengths, 2, d, dtype, device, np.array([2.0 ** -2, 2.0 ** -7], np.float32), seed=96)
 
 
+def test_backward_varlen_tiny_gradients_bf16(device):
+    # packed sequences (token by token, tiled, chunked) with gradients of order 2^-30
+    run_backward_varlen([300, 5, 4100], 2, 128, "bf16", device, np.array([2.0 ** -2, 2.0 ** -7], np.float32),
+                        seed=97, grad_scale=2.0 ** -30)
+
+
 @pytest.mark.parametrize("i", range(6))
 def test_backward_varlen_sweep(device, i):
     # seeded random packed batches through the backward: lengths (empty, token by token, tiled,
@@ -142,9 +162,10 @@ def test_backward_varlen_sweep(device, i):
     run_backward_varlen(lengths, H, d, dtype, device, slopes, seed=9100 + 10 * i, states=bool(rng.random() < 0.6))
 
 
-def run_backward_varlen(lengths, H, d, dtype, device, slopes, seed, states=True):
+def run_backward_varlen(lengths, H, d, dtype, device, slopes, seed, states=True, grad_scale=1.0):
     """la_backward_varlen on one packed batch; every sequence against the oracle on its own tokens
-    (an empty sequence passes dL/dKV_final through unchanged)."""
+    (an empty sequence passes dL/dKV_final through unchanged).  grad_scale (a power of two)
+    multiplies dL/dO and dL/dKV_final."""
     torch = _torch()
 
     cu = [0] + list(np.cumsum(lengths))
@@ -152,9 +173,13 @@ def run_backward_varlen(lengths, H, d, dtype, device, slopes, seed, states=True)
     exact, raw = inputs(seed, 1, H, T, d, dtype)
     graw = synth.generate(synth.V, seed + 1, d, nh=H, nt=T, dtype=dtype)
     gex = synth.bf16_bits_to_f32(graw) if dtype == "bf16" else graw
+    if grad_scale != 1.0:
+        gex = (gex * np.float32(grad_scale)).astype(np.float32)
+        graw = synth.f32_to_bf16_bits(gex) if dtype == "bf16" else gex
     rng = np.random.default_rng(seed + 2)
     kv_in = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32) if states else None
-    dkv_out = rng.standard_normal((len(lengths), H, d, d)).astype(np.float32) if states else None
+    dkv_out = ((rng.standard_normal((len(lengths), H, d, d)) * grad_scale).astype(np.float32)
+               if states else None)
 
     def packed(x):  # [1, H, T, d] -> device [T, H, d]
         return to_device(np.ascontiguousarray(x[0].transpose(1, 0, 2)), dtype, device)

@@ -176,7 +176,8 @@ def test_nan_in_decode_stays_confined(device):
 
 def test_varlen_back_to_back_calls_reuse_staging(device):
     """Twenty packed prefills enqueued without a synchronisation in between, with tables of
-    growing size, so the page-locked staging ring wraps and regrows while copies are in flight."""
+    growing size: small ones travel in kernel arguments, larger ones through the page-locked
+    staging ring, which wraps and regrows while copies are in flight."""
     import torch
 
     H, d = 2, 128
@@ -184,10 +185,10 @@ def test_varlen_back_to_back_calls_reuse_staging(device):
     sl = torch.from_numpy(SL2).to(device)
     runs = []
     for i in range(20):
-        if i < 15:
-            lengths = [int(x) for x in rng.integers(0, 300, size=4 + 3 * i)]
-        else:  # many short sequences: tables large enough to regrow the staging buffers
-            lengths = [int(x) for x in rng.integers(0, 40, size=200 + 150 * (i - 15))]
+        if i < 8:
+            lengths = [int(x) for x in rng.integers(0, 300, size=4 + 5 * i)]
+        else:  # many short sequences: tables past the kernel-argument size, growing
+            lengths = [int(x) for x in rng.integers(0, 40, size=120 + 60 * (i - 8))]
         cu = [0] + list(np.cumsum(lengths))
         T = cu[-1]
         exact, raw = inputs(100 + i, 1, H, T, d, "bf16")
