@@ -702,18 +702,21 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 // The tile kernel above slices the value columns over four workgroups, which suits the outputs,
 // but for a summary alone it makes each slice re-read all of K.  Here one workgroup owns a whole
 // (sequence, head, sub-chunk) and its full d x d state: K and V are read once.  Per 64-token tile
-// the state is decayed by lambda^L and K^T (W V) is added, with W V staged as bf16 hi + lo as in
-// the tile kernel's summary modes.  Eight waves split the 8 x 8 state tiles of 16 x 16 as 2 key-row halves x 4
-// value-column quarters.  No SiLU prologue (the fused path keeps the sliced summaries).
+// the state is decayed by lambda^L and K^T (W V) is added.  F16 (summaries for a prefill with
+// float16 outputs, which bounds the inputs the same way): K and W V as float16, one MFMA per
+// product; W V needs no scale here, as no copy of the state enters a product.  Otherwise (state-only
+// prefills and the backward) bf16 K and W V as a bf16 hi + lo pair, over float32's range.  Eight
+// waves split the 8 x 8 state tiles of 16 x 16 as 2 key-row halves x 4 value-column quarters.  No
+// SiLU prologue (the fused path keeps the sliced summaries).
 struct SumRegs { uint4 k[2]; uint4 v[2]; };  // 16-byte chunks tid and tid + 512 of the K and V tiles
 
-template <bool REV>
+template <bool REV, bool F16>
 __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
 {
     constexpr int D = 128, KS = kKS<D>;  // (d = 128 only: at d = 64 the sliced summaries serve)
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sWh[2][BK * KS];
-    __shared__ __attribute__((aligned(16))) u16 sWl[2][BK * KS];
+    __shared__ __attribute__((aligned(16))) u16 sWl[F16 ? 1 : 2][F16 ? 8 : BK * KS];
 
     const int64_t group = blockIdx.x;
     if (group >= a.groups) return;
@@ -781,14 +784,22 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int c = tid + 512 * m, r = c >> 4, off = r * KS + 8 * (c & 15);
-            *reinterpret_cast<uint4*>(&sK[buf][off]) = R.k[m];
+            *reinterpret_cast<uint4*>(&sK[buf][off]) = F16 ? bf16x8_to_f16(R.k[m]) : R.k[m];
             const float wt = (L == BK) ? wt_full[m] : wt_last[m];
             const uint32_t in[4] = {R.v[m].x, R.v[m].y, R.v[m].z, R.v[m].w};
-            uint32_t hi[4], lo[4];
+            if constexpr (F16) {
+                uint32_t hw[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
-            *reinterpret_cast<uint4*>(&sWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4*>(&sWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                for (int e = 0; e < 4; ++e) hw[e] = cvt2h(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt);
+                *reinterpret_cast<uint4*>(&sWh[buf][off]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            } else {
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    split2(bits_to_f32(in[e] & 0xffffu) * wt, hi_to_f32(in[e]) * wt, hi[e], lo[e]);
+                *reinterpret_cast<uint4*>(&sWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                *reinterpret_cast<uint4*>(&sWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            }
         }
     };
     f32x4 st[8];
@@ -812,15 +823,19 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
             for (int j = 0; j < 2; ++j) {
                 const int o = (k0 + tr_row) * KS + 16 * (jt0 + j) + tr_col;
                 vh[j] = join(lds_tr(&sWh[buf][o]), lds_tr(&sWh[buf][o + 4 * KS]));
-                vl[j] = join(lds_tr(&sWl[buf][o]), lds_tr(&sWl[buf][o + 4 * KS]));
+                if constexpr (!F16) vl[j] = join(lds_tr(&sWl[buf][o]), lds_tr(&sWl[buf][o + 4 * KS]));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    st[2 * i + j] = mfma(ka[i], vh[j], st[2 * i + j]);
-                    st[2 * i + j] = mfma(ka[i], vl[j], st[2 * i + j]);
+                    if constexpr (F16) {
+                        st[2 * i + j] = mfma_h(ka[i], vh[j], st[2 * i + j]);
+                    } else {
+                        st[2 * i + j] = mfma(ka[i], vh[j], st[2 * i + j]);
+                        st[2 * i + j] = mfma(ka[i], vl[j], st[2 * i + j]);
+                    }
                 }
         }
     };
@@ -893,8 +908,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mode, hipStream_t stream
 hipError_t launch_summary_bf16(const FwdArgs& a, hipStream_t stream)
 {
     const dim3 grid((unsigned)a.groups), block(512);
-    if (a.rev) hipLaunchKernelGGL((k_summary_bf16<true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_summary_bf16<false>), grid, block, 0, stream, a);
+    // float16 operands only for a prefill with float16 outputs (whose inputs are bounded alike)
+    if (a.rev) hipLaunchKernelGGL((k_summary_bf16<true, false>), grid, block, 0, stream, a);
+    else if (a.o && !a.wide) hipLaunchKernelGGL((k_summary_bf16<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_summary_bf16<false, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
