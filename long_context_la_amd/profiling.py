@@ -228,6 +228,10 @@ def mfma_utilisation(pmc_csv, pattern, simds, xcds, tiles_per_simd=None, workgro
 # ------------------------------------------------------------------ the profiling runs
 BENCH = "python3 {root}/bench.py"
 ONLY_FULL = "--no-cpu-baseline --no-decode --no-backward --no-varlen --no-other-workloads"
+# The full-layer prefill kernel: outputs, no gate, forward walk, no SiLU prologue, d = 128, float16
+# operands (k_fwd_bf16<MODE, GATE, REV, ACT, D, WIDE>).
+MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false>"
+
 RUNS = {
     # name: (rocprofv3 arguments, bench arguments)
     "stats_full": ("--kernel-trace --stats", "--steps 5 --warmup 1 " + ONLY_FULL),
@@ -378,7 +382,7 @@ def summarize_all(out_root, profiles_dir=PROFILES):
         "kernel_stats_prefill_full_64x131072.txt": lambda: summarize_stats(
             out_root, "stats_full", "kernel statistics of the full-layer prefill (1 x 64 heads x 131072 tokens, d=128, "
             "bf16): settling, 1 warm-up, 5 timed steps and 5 per-kernel timings",
-            (r"k_fwd_bf16<0, false, false, false, 128>", 256, 5)),
+            (MAIN_KERNEL, 256, 5)),
         "kernel_stats_bench_all_legs.txt": lambda: summarize_stats(
             out_root, "stats_all", "kernel statistics of bench.py: full-layer prefill (1 x 64 heads x 131072 tokens, "
             "d=128, bf16), backward, packed and mixed legs, decode (128 x 64 units, 100 steps)"),
@@ -388,18 +392,18 @@ def summarize_all(out_root, profiles_dir=PROFILES):
             out_root, "stats_long", "kernel statistics of the chunked long-context prefill (1 x 8 heads x 1048576, "
             "d=128, checkpoints every 65536)"),
         "prefill_full_hbm_traffic.txt": lambda: summarize_traffic(
-            out_root, "full", r"k_fwd_bf16<0, false, false, false, 128>", full_bytes, 256),
+            out_root, "full", MAIN_KERNEL, full_bytes, 256),
         "prefill_share_hbm_traffic.txt": lambda: summarize_traffic(
-            out_root, "share", r"k_fwd_bf16<0, false, false, false, 128>", eight_heads(32768), 256,
+            out_root, "share", MAIN_KERNEL, eight_heads(32768), 256,
             extra_kernels=(("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
                            ("prefix combine (k_scan_sub)", r"k_scan_sub", None))),
         "prefill_long_hbm_traffic.txt": lambda: summarize_traffic(
-            out_root, "long", r"k_fwd_bf16<0, false, false, false, 128>", eight_heads(1 << 20), 256,
+            out_root, "long", MAIN_KERNEL, eight_heads(1 << 20), 256,
             extra_kernels=(("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
                            ("prefix combine (k_scan_sub)", r"k_scan_sub", None))),
         "decode_128x64_hbm_traffic.txt": lambda: summarize_traffic(
             out_root, "decode", r"k_decode", 8192 * (2 * 128 * 128 * 4 + 4 * 128 * 2), 8192),
-        "prefill_full_mfma_util.txt": lambda: summarize_mfma(out_root, 2048, r"k_fwd_bf16<0, false, false, false, 128>",
+        "prefill_full_mfma_util.txt": lambda: summarize_mfma(out_root, 2048, MAIN_KERNEL,
                                                              256),
     }
     written = []
