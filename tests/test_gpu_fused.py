@@ -111,6 +111,45 @@ CASES = [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 64)]
 
 
 @pytest.mark.parametrize("dtype,d", CASES)
+@pytest.mark.parametrize("norm,weight,gate", [(True, True, True), (True, False, False), (False, False, True)])
+def test_epilogue_on_the_kernels_own_output(device, dtype, d, norm, weight, gate):
+    """The epilogue alone, held to its definition element by element: the fused call's output
+    against the oracle's RMS norm and sigmoid gate applied in float64 to the same kernels' output
+    without the epilogue (the kernels are deterministic, so that output is exactly what the
+    epilogue received, or for the gate in the store its rounding).  Bar: one ulp of the result,
+    plus for float32 2^-14 relative (the epilogue's float32 sum of squares, square root and
+    exponential), plus, for the gate in the store, half an ulp of the pre-epilogue value times
+    the gate (that value is rounded in the run without the epilogue, not in the fused one)."""
+    torch = _torch()
+    B, H, N = 1, 2, 333
+    exact, raw = inputs(47, B, H, N, d, dtype)
+    slopes = torch.from_numpy(np.array([2.0 ** -2, 2.0 ** -8], dtype=np.float32)).to(device)
+    g, w = gate_and_weight(48, (B, H, N, d), d, dtype)
+    q, k, v = (to_device(x, dtype, device) for x in raw)
+
+    def run(**kw):
+        kv = torch.zeros(B, H, d, d, dtype=torch.float32, device=device)
+        o = torch.empty_like(q)
+        la.la_prefill_fused(q, k, v, slopes, kv, o, silu_q=True, silu_k=True, silu_v=True, **kw)
+        torch.cuda.synchronize()
+        return to_host(o).astype(np.float64)
+
+    pre = run()
+    got = run(norm_eps=1e-5 if norm else None, norm_weight=torch.from_numpy(w).to(device) if weight else None,
+              gate=dev(g, dtype, device) if gate else None)
+    want = oracle.rms_norm(pre, 1e-5, w if weight else None) if norm else pre
+    sig = oracle.sigmoid(g) if gate else 1.0
+    want = want * sig
+    allow = 2.0 * half_ulp(got, dtype) + (2.0 ** -14 * np.abs(want) if dtype == "f32" else 0.0)
+    if gate and not norm:
+        allow = allow + half_ulp(pre, dtype) * sig
+    excess = np.abs(got - want) - allow
+    i = np.unravel_index(np.argmax(excess), excess.shape)
+    assert excess.max() <= 0.0, (f"epilogue (norm={norm}, weight={weight}, gate={gate}, {dtype}, d={d}) at {i}: "
+                                 f"got {got[i]:.8g}, want {want[i]:.8g}, allowed {allow[i]:.3g}")
+
+
+@pytest.mark.parametrize("dtype,d", CASES)
 def test_prologue_silu_qk(device, dtype, d):
     run_prefill_fused(1, 2, 200, d, dtype, device, silu=(True, True, False))
 
