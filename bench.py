@@ -40,7 +40,7 @@ MIXED_LENGTHS = [50, 50] + [1] * 18
 
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_SOURCE = os.path.join(ROOT, "long_context_la_amd", "csrc", "la_prefill_bf16.hip")
-FLUSH_BYTES = 512 << 20   # written between timed steps of the cache-sized legs (256 MB Infinity Cache)
+FLUSH_BYTES = 512 << 20   # read between timed steps of the cache-sized legs (256 MB Infinity Cache)
 
 
 def source_digest(path=PREFILL_SOURCE):
@@ -168,18 +168,27 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True,
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # flush: before each timed step (outside its events) a 512 MB buffer is written, so a workload
-    # about the size of the 256 MB Infinity Cache starts every step from HBM
-    junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device) if flush else None
-    if flush:
+    # flush: before each timed step (outside its events) a 512 MB buffer is read, so a workload
+    # about the size of the 256 MB Infinity Cache starts every step from HBM, and the write-back of
+    # the previous step's dirty lines happens before the step.  A flush that writes the buffer
+    # instead leaves ~256 MB of dirty lines whose write-back then falls inside the next step; that
+    # figure is reported beside it.
+    junk = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=device) if flush else None
+    flush_write = None
+
+    def flushed_steps(flush_op):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in ev:
-            junk.fill_(1)
+            flush_op()
             a.record(stream)
             step()
             b.record(stream)
         torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    if flush:
+        ms = flushed_steps(lambda: junk.max())
+        flush_write = flushed_steps(lambda: junk.fill_(1))
     else:
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
@@ -193,7 +202,7 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True,
     for a, b in ev:
         la.la_state_init(kv)
         if flush:
-            junk.fill_(1)
+            junk.max()
         a.record(stream)
         la.la_prefill(q, k, v, slopes, kv, o=o, ckpt=ck, ckpt_every=w.ckpt_every, workspace=ws)
         b.record(stream)
@@ -206,7 +215,7 @@ def time_prefill(w, steps, warmup, device, with_backward=True, with_varlen=True,
         varlen = time_varlen_packed(q, k, v, o, slopes, w, steps, warmup, device)
     backward = time_backward(q, k, v, o, slopes, w, steps, warmup, device) if with_backward else None
     del q, k, v, o, ws
-    return ms, kernel_ms, n_chunks, varlen, backward
+    return ms, kernel_ms, n_chunks, varlen, backward, flush_write
 
 
 def time_backward(q, k, v, dout, slopes, w, steps, warmup, device):
@@ -528,7 +537,7 @@ def main():
               flush=True)
         return
     w = synth.WORKLOADS[args.workload]
-    ms, kernel_ms, n_chunks, varlen, backward = time_prefill(w, args.steps, args.warmup, device,
+    ms, kernel_ms, n_chunks, varlen, backward, _ = time_prefill(w, args.steps, args.warmup, device,
                                                              with_backward=not args.no_backward,
                                                              with_varlen=not args.no_varlen)
     token_heads = w.batch * w.heads * w.n
@@ -572,8 +581,8 @@ def main():
             # the share workload (268 MB moved) is about the size of the Infinity Cache: each of its
             # timed steps starts from a flushed cache
             flush = name == "share"
-            ms_o, kms_o, nch_o, _, _ = time_prefill(wo, steps, 1, device, with_backward=False, with_varlen=False,
-                                                    flush=flush)
+            ms_o, kms_o, nch_o, _, _, ms_wr = time_prefill(wo, steps, 1, device, with_backward=False,
+                                                           with_varlen=False, flush=flush)
             th = wo.batch * wo.heads * wo.n
             log(f"prefill {name}: {ms_o:.3f} ms/step, kernel(s) {kms_o:.3f} ms, {nch_o} chunk(s)"
                 + (" (cache flushed before each step)" if flush else ""))
@@ -582,8 +591,10 @@ def main():
                             "ms_per_step": ms_o, "kernel_ms": kms_o, "tokens_per_s": wo.batch * wo.n / (ms_o * 1e-3),
                             "hbm_frac": 4 * wo.d * 2 * th / (kms_o * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             "mfma_frac": model_flops_per_token_head(wo.d) * th / (ms_o * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                            "cache_flushed_between_steps": flush,
+                            "cache_flushed_between_steps": "by reading 512 MiB" if flush else False,
                             "traffic": measured_traffic(name) if wo.d == 128 else None}
+            if ms_wr is not None:
+                others[name]["ms_per_step_flushed_by_writing_512MiB"] = ms_wr
         result["other_workloads"] = others
     if not args.no_decode:
         result["mixed_batch"] = time_mixed(device)
