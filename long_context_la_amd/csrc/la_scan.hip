@@ -60,16 +60,31 @@ __global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, cons
         float4* P = reinterpret_cast<float4*>(pref + u * n_chunks * (int64_t)d2) + e;
         float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
         P[0] = p;
-        for (int64_t j = 1; j < n_chunks; ++j) {
-#pragma unroll 4
-            for (int64_t f = 0; f < n_sub_per; ++f) {
-                const float4 s = S[((j - 1) * n_sub_per + f + 1) * per];
-                p.x = ls * p.x + s.x;
-                p.y = ls * p.y + s.y;
-                p.z = ls * p.z + s.z;
-                p.w = ls * p.w + s.w;
+        // The sub-chunk states are loaded kGroup at a time before they are folded, so a group costs
+        // one memory round trip instead of one per chunk.  After sub-chunk i (0-based) the fold has
+        // covered (i + 1) / n_sub_per whole chunks; at each chunk boundary that prefix is stored.
+        constexpr int kGroup = 16;
+        int64_t j = 1;     // next chunk prefix to store
+        int64_t f = 0;     // sub-chunks folded into the current chunk
+        for (int64_t base = 0; base < n_sub; base += kGroup) {
+            float4 s[kGroup];
+#pragma unroll
+            for (int q = 0; q < kGroup; ++q)
+                s[q] = base + q < n_sub ? S[(base + q + 1) * per] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int q = 0; q < kGroup; ++q) {
+                if (base + q < n_sub) {
+                    p.x = ls * p.x + s[q].x;
+                    p.y = ls * p.y + s[q].y;
+                    p.z = ls * p.z + s[q].z;
+                    p.w = ls * p.w + s[q].w;
+                    if (++f == n_sub_per) {
+                        P[j * per] = p;
+                        ++j;
+                        f = 0;
+                    }
+                }
             }
-            P[j * per] = p;
         }
     }
 }
