@@ -283,3 +283,32 @@ def test_bf16_products_far_from_unit_scale(device, chunk, scale, kv_scale):
         assert max(float(np.abs(x).max()) for x in scaled) > 2000 and np.abs(kv_ref).max() > 1e6
     assert_close(to_host(o), o_ref, "bf16", "O", stored="bf16")
     assert_close(kv.cpu().numpy(), kv_ref, "bf16", "KV")
+
+
+@pytest.mark.parametrize("n_tiled,n_short", [(52, 4), (55, 0)])
+def test_varlen_tables_at_the_kernel_argument_limit(device, n_tiled, n_short):
+    """Chunk tables of 384 int64 words (5 per tiled chunk, 2 per sequence, 3 more per sequence
+    of at most 8 tokens) travel in kernel arguments, 385 words through page-locked staging; both
+    sides of that boundary against the oracle, sequence by sequence."""
+    import torch
+
+    words = 7 * n_tiled + 5 * n_short
+    assert words in (384, 385)
+    H, d = 2, 128
+    rng = np.random.default_rng(60 + words)
+    lengths = [int(x) for x in rng.integers(9, 200, size=n_tiled)] + [int(x) for x in rng.integers(1, 9, size=n_short)]
+    lengths = [lengths[i] for i in rng.permutation(len(lengths))]
+    cu = [0] + list(np.cumsum(lengths))
+    exact, raw = inputs(61, 1, H, cu[-1], d, "bf16")
+    q, k, v = (to_device(np.ascontiguousarray(x[0].transpose(1, 0, 2)), "bf16", device) for x in raw)
+    kv = torch.zeros(len(lengths), H, d, d, device=device)
+    o = torch.empty_like(q)
+    la.la_prefill_varlen(q, k, v, torch.from_numpy(SL2).to(device), kv, cu, o=o)
+    torch.cuda.synchronize()
+    got_o, got_kv = o.float().cpu().numpy(), kv.cpu().numpy()
+    for s in range(len(lengths)):
+        a, b = cu[s], cu[s + 1]
+        o_ref, kv_ref, _ = oracle.recurrent(*(x[:, :, a:b] for x in exact), SL2)
+        assert_close(got_o[a:b].transpose(1, 0, 2)[None], o_ref, "bf16", f"varlen O, sequence {s} ({b - a} tokens)",
+                     stored="bf16")
+        assert_close(got_kv[s][None], kv_ref, "bf16", f"varlen KV, sequence {s}")
