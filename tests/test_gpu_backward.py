@@ -19,12 +19,16 @@ def _torch():
     return torch
 
 
-def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, layout="bhnd", grad_scale=1.0):
-    """grad_scale (a power of two, so the scaling is exact) multiplies dL/dO and dL/dKV_final."""
+def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, layout="bhnd", grad_scale=1.0,
+                 state_scale=None, zero_grad=False):
+    """grad_scale (a power of two, so the scaling is exact) multiplies dL/dO, and state_scale
+    (grad_scale if None) dL/dKV_final; zero_grad makes dL/dO all zero."""
     torch = _torch()
     exact, raw = inputs(seed, B, H, N, d, dtype)
     dout_raw = synth.generate(synth.V, seed + 500, d, nb=B, nh=H, nt=N, dtype=dtype)
     dout_exact = synth.bf16_bits_to_f32(dout_raw) if dtype == "bf16" else dout_raw
+    if zero_grad:
+        grad_scale = 0.0
     if grad_scale != 1.0:
         dout_exact = (dout_exact * np.float32(grad_scale)).astype(np.float32)
         dout_raw = synth.f32_to_bf16_bits(dout_exact) if dtype == "bf16" else dout_exact
@@ -34,7 +38,8 @@ def run_backward(B, H, N, d, dtype, device, states=True, seed=71, slopes=None, l
         slopes = np.array([2.0 ** (-2 - 3 * h) for h in range(H)], dtype=np.float32)
     rng = np.random.default_rng(seed + 1)
     kv_in = rng.standard_normal((B, H, d, d)).astype(np.float32) if states else None
-    dkv_out = (rng.standard_normal((B, H, d, d)) * grad_scale).astype(np.float32) if states else None
+    dkv_out = (rng.standard_normal((B, H, d, d)) * (grad_scale if state_scale is None else state_scale)
+               ).astype(np.float32) if states else None
 
     def dev(x):
         t = to_device(x, dtype, device)
@@ -67,6 +72,25 @@ def test_backward_tiny_gradients_bf16(device, grad_log2, N, d):
     # gradients of a mean loss over a large tensor sit far below float16's normal range (2^-14):
     # every backward pass runs on full-range (bf16 hi + lo) operands and keeps the bf16 bar
     run_backward(1, 2, N, d, "bf16", device, states=True, seed=95, grad_scale=2.0 ** grad_log2)
+
+
+@pytest.mark.parametrize("grad_log2,state_log2", [(-30, 0), (0, -30), (-40, -26)])
+def test_backward_gradient_and_state_far_apart_bf16(device, grad_log2, state_log2):
+    # dL/dO and dL/dKV_final at scales 2^30 apart either way: the full-range operands keep both
+    run_backward(1, 2, 700, 128, "bf16", device, states=True, seed=98, grad_scale=2.0 ** grad_log2,
+                 state_scale=2.0 ** state_log2)
+
+
+@pytest.mark.parametrize("states", [False, True])
+def test_backward_zero_gradient_bf16(device, states):
+    # an all-zero dL/dO, with and without a dL/dKV_final
+    run_backward(1, 2, 300, 128, "bf16", device, states=states, seed=99, zero_grad=True,
+                 state_scale=1.0 if states else None)
+
+
+def test_backward_tiny_gradients_strided_layout_bf16(device):
+    # tiny gradients in a [B, N, H, d] layout
+    run_backward(2, 2, 200, 128, "bf16", device, states=True, seed=100, layout="bnhd", grad_scale=2.0 ** -30)
 
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 129])
