@@ -495,7 +495,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--settle-s", type=float, default=SETTLE_S,
                     help="seconds of untimed steps before each leg's warm-up (lets the clock settle)")
-    ap.add_argument("--workload", default="full", choices=["full", "share", "long"])
+    ap.add_argument("--workload", default="full", choices=["full", "share", "long", "full_d64"])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -145,8 +145,8 @@ __device__ inline Work decode_work(const FwdArgs& a, int64_t group)
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int mode, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mode, hipStream_t stream);
 // Chunk summaries (kModeLocal semantics) at full width, one workgroup per group of `a` (no value
-// slices); bf16 without the SiLU prologue.
-hipError_t launch_summary_bf16(const FwdArgs& a, hipStream_t stream);
+// slices); bf16 without the SiLU prologue, d = 64 or 128.
+hipError_t launch_summary_bf16(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t bh, int64_t heads,
                        int64_t n_chunks, int64_t chunk, int d, hipStream_t stream);
 // Prefixes from sub-chunk summaries: pref[u][0] = kv[u]; pref[u][j] = the state after chunks

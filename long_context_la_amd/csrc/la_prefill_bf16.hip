@@ -706,14 +706,21 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 // float16 outputs, which bounds the inputs the same way): K and W V as float16, one MFMA per
 // product; W V needs no scale here, as no copy of the state enters a product.  Otherwise (state-only
 // prefills and the backward) bf16 K and W V as a bf16 hi + lo pair, over float32's range.  Eight
-// waves split the 8 x 8 state tiles of 16 x 16 as 2 key-row halves x 4 value-column quarters.  No
-// SiLU prologue (the fused path keeps the sliced summaries).
-struct SumRegs { uint4 k[2]; uint4 v[2]; };  // 16-byte chunks tid and tid + 512 of the K and V tiles
+// waves split the (D/16)^2 state tiles of 16 x 16 into 8 / (D/32) key-row groups x D/32
+// value-column groups: 2 x 4 groups of 4 x 2 tiles at d = 128, 4 x 2 groups of 1 x 2 tiles at
+// d = 64.  No SiLU prologue (the fused path keeps the sliced summaries).
+template <int D> struct SumRegs { uint4 k[D / 64]; uint4 v[D / 64]; };  // 16-byte chunks tid + 512m of K and V
 
-template <bool REV, bool F16>
+template <bool REV, bool F16, int D>
 __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
 {
-    constexpr int D = 128, KS = kKS<D>;  // (d = 128 only: at d = 64 the sliced summaries serve)
+    static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+    constexpr int KS = kKS<D>;
+    constexpr int CPR = D / 8, CPR_LOG = D == 128 ? 4 : 3;    // 16-byte chunks per row of K or V
+    constexpr int M = D / 64;                                  // chunks per thread and tile
+    constexpr int WJ = D / 32, WI = 8 / WJ;                    // wave groups over value, key tiles
+    constexpr int NI = (D / 16) / WI, NJ = (D / 16) / WJ;      // a wave's key-row, value-col tiles
+    using SR = SumRegs<D>;
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sWh[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sWl[F16 ? 1 : 2][F16 ? 8 : BK * KS];
@@ -727,7 +734,8 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, g = l >> 4;
-    const int it0 = 4 * (w >> 2), jt0 = 2 * (w & 3);  // this wave's state tiles: key rows 16(it0..it0+3), value cols 16(jt0..jt0+1)
+    // this wave's state tiles: key rows 16(it0..it0+NI-1), value columns 16(jt0..jt0+NJ-1)
+    const int it0 = NI * (w / WJ), jt0 = NJ * (w % WJ);
     const int tr_row = lr >> 2, tr_col = 4 * (lr & 3);
     const float nsl = neg_slope_log2e(a.slopes, wk.h);
     const u16* Kg = static_cast<const u16*>(a.k) + wk.base;
@@ -756,34 +764,34 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
         if constexpr (!REV) return (uint32_t)r * row_bytes;
         return (uint32_t)(tile_len(tile) - 1 - r) * row_bytes;
     };
-    auto load = [&](SumRegs& R, int tile) __attribute__((always_inline)) {
+    auto load = [&](SR& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_row0(tile);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + t0 * sn, tile_bytes(tile));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + t0 * sn, tile_bytes(tile));
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < M; ++m) {
             const int c = tid + 512 * m;
-            R.k[m] = buf_load16(rk, row_off(tile, c >> 4) + 16u * (c & 15));
-            R.v[m] = buf_load16(rv, row_off(tile, c >> 4) + 16u * (c & 15));
+            R.k[m] = buf_load16(rk, row_off(tile, c >> CPR_LOG) + 16u * (c & (CPR - 1)));
+            R.v[m] = buf_load16(rv, row_off(tile, c >> CPR_LOG) + 16u * (c & (CPR - 1)));
         }
     };
     // decay weights of a full tile and of the last tile (the only one that can be shorter),
-    // computed once: rows tid/16 and 32 + tid/16 of W, and lambda^L
+    // computed once: rows (tid + 512m) / CPR of W, and lambda^L
     const int L_last = tile_len(n_tiles - 1);
-    float wt_full[2], wt_last[2];
+    float wt_full[M], wt_last[M];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int r = (tid >> 4) + 32 * m;
+    for (int m = 0; m < M; ++m) {
+        const int r = (tid + 512 * m) >> CPR_LOG;
         wt_full[m] = decay_pow(nsl, (float)(BK - 1 - r));
         wt_last[m] = (r < L_last) ? decay_pow(nsl, (float)(L_last - 1 - r)) : 0.f;
     }
     const float dl_full = decay_pow(nsl, (float)BK);
     const float dl_last = decay_pow(nsl, (float)L_last);
-    auto stage = [&](const SumRegs& R, int buf, int tile) __attribute__((always_inline)) {
+    auto stage = [&](const SR& R, int buf, int tile) __attribute__((always_inline)) {
         const int L = tile_len(tile);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int c = tid + 512 * m, r = c >> 4, off = r * KS + 8 * (c & 15);
+        for (int m = 0; m < M; ++m) {
+            const int c = tid + 512 * m, r = c >> CPR_LOG, off = r * KS + 8 * (c & (CPR - 1));
             *reinterpret_cast<uint4*>(&sK[buf][off]) = F16 ? bf16x8_to_f16(R.k[m]) : R.k[m];
             const float wt = (L == BK) ? wt_full[m] : wt_last[m];
             const uint32_t in[4] = {R.v[m].x, R.v[m].y, R.v[m].z, R.v[m].w};
@@ -802,51 +810,51 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
             }
         }
     };
-    f32x4 st[8];
+    f32x4 st[NI * NJ];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NI * NJ; ++k) st[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     // S <- lambda^L S + K^T (W V) on this wave's 4 x 2 state tiles (k = token within the tile)
     auto update = [&](int buf, int tile) __attribute__((always_inline)) {
         const float dl = (tile_len(tile) == BK) ? dl_full : dl_last;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) st[k] *= dl;
+        for (int k = 0; k < NI * NJ; ++k) st[k] *= dl;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int k0 = 32 * ks + 8 * g;
-            bf16x8 ka[4], vh[2], vl[2];
+            bf16x8 ka[NI], vh[NJ], vl[NJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NI; ++i) {
                 const int o = (k0 + tr_row) * KS + 16 * (it0 + i) + tr_col;
                 ka[i] = join(lds_tr(&sK[buf][o]), lds_tr(&sK[buf][o + 4 * KS]));
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int o = (k0 + tr_row) * KS + 16 * (jt0 + j) + tr_col;
                 vh[j] = join(lds_tr(&sWh[buf][o]), lds_tr(&sWh[buf][o + 4 * KS]));
                 if constexpr (!F16) vl[j] = join(lds_tr(&sWl[buf][o]), lds_tr(&sWl[buf][o + 4 * KS]));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     if constexpr (F16) {
-                        st[2 * i + j] = mfma_h(ka[i], vh[j], st[2 * i + j]);
+                        st[NJ * i + j] = mfma_h(ka[i], vh[j], st[NJ * i + j]);
                     } else {
-                        st[2 * i + j] = mfma(ka[i], vh[j], st[2 * i + j]);
-                        st[2 * i + j] = mfma(ka[i], vl[j], st[2 * i + j]);
+                        st[NJ * i + j] = mfma(ka[i], vh[j], st[NJ * i + j]);
+                        st[NJ * i + j] = mfma(ka[i], vl[j], st[NJ * i + j]);
                     }
                 }
         }
     };
-    SumRegs RA, RB;
+    SR RA, RB;
     load(RA, 0);
     __builtin_amdgcn_sched_barrier(0);
     load(RB, 1);
     __builtin_amdgcn_sched_barrier(0);
     stage(RA, 0, 0);
     __syncthreads();
-    auto step = [&](SumRegs& R, SumRegs& Rn, int buf, int tile) __attribute__((always_inline)) {
+    auto step = [&](SR& R, SR& Rn, int buf, int tile) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         load(R, tile + 2);
         __builtin_amdgcn_sched_barrier(0);
@@ -864,12 +872,12 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     // C layout: lane (g, lr) holds rows 4g..4g+3 (key) of column lr (value) of each tile
     float* dst = a.ws + wk.slot_out * (int64_t)(D * D);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                dst[(16 * (it0 + i) + 4 * g + t) * D + 16 * (jt0 + j) + lr] = st[2 * i + j][t];
+                dst[(16 * (it0 + i) + 4 * g + t) * D + 16 * (jt0 + j) + lr] = st[NJ * i + j][t];
 }
 
 template <bool GATE, bool REV, bool ACT, int D, bool WIDE>
@@ -905,13 +913,20 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mode, hipStream_t stream
     return hipGetLastError();
 }
 
-hipError_t launch_summary_bf16(const FwdArgs& a, hipStream_t stream)
+template <int D>
+void launch_summary_d(const FwdArgs& a, hipStream_t stream)
 {
     const dim3 grid((unsigned)a.groups), block(512);
     // float16 operands only for a prefill with float16 outputs (whose inputs are bounded alike)
-    if (a.rev) hipLaunchKernelGGL((k_summary_bf16<true, false>), grid, block, 0, stream, a);
-    else if (a.o && !a.wide) hipLaunchKernelGGL((k_summary_bf16<false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_summary_bf16<false, false>), grid, block, 0, stream, a);
+    if (a.rev) hipLaunchKernelGGL((k_summary_bf16<true, false, D>), grid, block, 0, stream, a);
+    else if (a.o && !a.wide) hipLaunchKernelGGL((k_summary_bf16<false, true, D>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_summary_bf16<false, false, D>), grid, block, 0, stream, a);
+}
+
+hipError_t launch_summary_bf16(const FwdArgs& a, int d, hipStream_t stream)
+{
+    if (d == 128) launch_summary_d<128>(a, stream);
+    else launch_summary_d<64>(a, stream);
     return hipGetLastError();
 }
 
