@@ -226,11 +226,12 @@ la_status la_prefill_ex(la_dtype dt, const void* q, const void* k, const void* v
  *   kv         : [n_seq][heads][d][d] float32, read then overwritten.
  *   workspace  : device scratch of at least la_prefill_varlen_workspace_size()
  *                bytes (never 0 bytes: it also receives the chunk tables);
- *                the call copies those tables into it asynchronously on
- *                `stream`, from page-locked staging buffers that the library
- *                reuses only once the copy has completed, so cu_seqlens may be
- *                released as soon as the call returns.  The workspace must not
- *                be in use by other work on other streams.
+ *                the call writes those tables into it asynchronously on
+ *                `stream`: up to 384 words through a kernel's arguments, more
+ *                by a copy from page-locked staging buffers that the library
+ *                reuses only once the copy has completed.  Either way
+ *                cu_seqlens may be released as soon as the call returns.  The
+ *                workspace must not be in use by other work on other streams.
  * No checkpoints.  Supported dtypes and d as for la_prefill; n_seq*heads and
  * (chunks of the sequences longer than 8 tokens)*heads at most 2^20, else
  * LA_ERR_UNSUPPORTED.

@@ -608,7 +608,8 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     s = device_check();
     if (s != LA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // the chunk and sequence tables go to the front of the workspace, through page-locked staging
+    // the chunk and sequence tables go to the front of the workspace (kernel arguments or
+    // page-locked staging, by size)
     s = upload_tables(workspace, p.tab, st);
     if (s != LA_OK) return s;
     const int64_t* ctab = static_cast<const int64_t*>(workspace);

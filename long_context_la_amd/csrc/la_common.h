@@ -19,9 +19,10 @@ constexpr int kShortTokens = 8;  // packed sequences this short run token by tok
 #define LA_LOCAL_TARGET_GROUPS 128
 #endif
 // Chunk summaries are computed per sub-chunk (halving) until the summary pass has at least this
-// many full-width workgroups (one per chunk-head; the sliced summaries of the fused path get four
-// times as many).  Measured on 8 heads: 128 and 256 tie at 1M tokens, and 128 is 7% faster at 32K
-// (fewer summary slots to fold); 512 and above are slower at both.
+// many full-width workgroups at d = 128, twice as many at d = 64 (one per chunk-head; the sliced
+// summaries of the fused path get a workgroup per value slice).  Measured on 8 heads at d = 128:
+// 256 is 1.1% faster at 1M tokens and 5% slower at 32K (more summary slots to fold); 512 is slower
+// at both.
 constexpr int kLocalTargetGroups = LA_LOCAL_TARGET_GROUPS;
 constexpr int kMinSubChunk = 256;  // shortest sub-chunk worth a 64 KiB summary
 

@@ -46,9 +46,10 @@
 // write before the 16-byte global stores.  State waves 4..7: the global
 // loads and LDS staging of K and V, the decay-weighted W V, and the state
 // update, with the state's 16 tiles of 16x16 split 8/5/2/1 (more state work
-// on the SIMDs whose output waves own the earlier, lighter query rows).  The
-// state waves publish the state after tile b (a float16 copy in LDS) for the
-// output waves' inter term of tile b+1.  Without outputs (state-only modes) the
+// on the SIMDs whose output waves own the earlier, lighter query rows; 6/5/3/2
+// with WIDE operands).  The state waves publish the state after tile b (a
+// float16 copy in LDS, or a bf16 hi + lo pair) for the output waves' inter
+// term of tile b+1.  Without outputs (state-only modes) the
 // kernel runs the four state waves alone.
 //
 // MFMA: v_mfma_f32_16x16x32_f16 / _bf16 (A 16x32, B 32x16, C 16x16 fp32; lane l holds
@@ -346,7 +347,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const float wt_last = ((st_id >> 2) < L_last) ? decay_pow(nsl, (float)(L_last - 1 - (st_id >> 2))) * kSc : 0.f;
     const float dl_last = decay_pow(nsl, (float)L_last);
     // K and V rows into LDS buffer `buf` with the decay-weighted V: float16 (and W V scaled by 2^-8)
-    // with outputs, else bf16 with W V as a hi + lo pair.
+    // with float16 outputs, else bf16 with W V as a hi + lo pair (WIDE outputs, state-only and
+    // summary modes).
     auto stage_tile = [&](const KR& R, int buf, int tile) __attribute__((always_inline)) {
         const int L = tile_len(tile);
 #pragma unroll
