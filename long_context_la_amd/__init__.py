@@ -6,11 +6,15 @@ strides and torch's current HIP stream, and raises on a non-OK status.  Every
 step of the computation runs in the library's gfx950 kernels -- there is no
 fallback: if the library is missing, every call raises.
 
-Names follow the C entry points: la_state_init, la_prefill,
-la_prefill_workspace_size, la_prefill_chunk_tokens, la_prefill_varlen,
-la_prefill_varlen_workspace_size, la_prefill_varlen_chunk_tokens, la_decode,
-la_status_string, la_last_error.  mixed_step issues a decode group and a
-varlen prefill group on two streams (two library calls, nothing else);
+Names follow the C entry points: la_state_init, la_prefill (with checkpoints and
+chunk_tokens), la_prefill_noalloc, la_prefill_workspace_size,
+la_prefill_chunk_tokens, la_prefill_varlen, la_prefill_varlen_workspace_size,
+la_prefill_varlen_chunk_tokens, la_decode, la_prefill_fused, la_decode_fused,
+la_backward, la_backward_varlen and their workspace sizes, la_status_string,
+la_last_error.  Every wrapper checks shapes, dtypes, strides and the state,
+checkpoint and slope buffers before anything is launched, since the C ABI sees
+raw pointers only.  mixed_step issues a decode group and a varlen prefill group
+(two library calls, nothing else) on the current stream or on two streams;
 lightning_attention and lightning_attention_varlen wrap the prefill and its
 backward as differentiable ops.
 """
@@ -290,6 +294,27 @@ def la_prefill(q, k, v, slopes, kv, o=None, ckpt=None, ckpt_every: int = 0, work
                              _ptr(slopes), _ptr(kv), _ptr(ckpt), ckpt_every, chunk_tokens,
                              _ptr(workspace), ws_bytes, _stream_ptr(stream, q.device))
     _check(st, "la_prefill")
+
+
+def la_prefill_noalloc(q, k, v, slopes, kv, o=None, ckpt=None, ckpt_every: int = 0, stream=None) -> None:
+    """la_prefill without a workspace argument, for callers that cannot allocate: the chunk
+    states live in the library's per-GPU scratch array (LA_NOALLOC_SCRATCH_BYTES), so calls
+    that overlap on one GPU race.  Allocates nothing."""
+    _check_qkv(q, k, v, 4)
+    dt = _dtype_code(q)
+    B, H, N, d = q.shape
+    _check_out(o, q, "o")
+    _check_slopes(slopes, H)
+    _check_f32(kv, (B, H, d, d), "kv")
+    if ckpt is not None:
+        if ckpt_every <= 0:
+            raise ValueError("ckpt_every must be positive when ckpt is given")
+        _check_f32(ckpt, (B, H, N // ckpt_every, d, d), "ckpt")
+    _require_cuda(q, k, v, slopes, kv, o, ckpt)
+    sb, sh, sn, _ = q.stride()
+    st = lib().la_prefill_noalloc(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, sb, sh, sn,
+                                  _ptr(slopes), _ptr(kv), _ptr(ckpt), ckpt_every, _stream_ptr(stream, q.device))
+    _check(st, "la_prefill_noalloc")
 
 
 def la_decode(q, k, v, slopes, kv, o, stream=None) -> None:

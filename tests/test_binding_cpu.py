@@ -61,6 +61,19 @@ def test_prefill_rejects_bad_states_and_slopes():
         call(ckpt=torch.zeros(B, H, 2, D, D), ckpt_every=100)
 
 
+def test_noalloc_prefill_rejects_bad_states():
+    a = good()
+    call = lambda **kw: la.la_prefill_noalloc(**{**a, **kw})
+    with pytest.raises(ValueError, match="kv"):
+        call(kv=torch.zeros(B, H, D, D + 1))
+    with pytest.raises(ValueError, match="slopes"):
+        call(slopes=torch.ones(H + 1))
+    with pytest.raises(ValueError, match="ckpt"):
+        call(ckpt=torch.zeros(B, H, 1, D, D), ckpt_every=64)
+    with pytest.raises(ValueError, match="GPU"):
+        call()
+
+
 def test_state_init_and_decode_reject_bad_states():
     with pytest.raises(ValueError, match="kv0"):
         la.la_state_init(torch.zeros(B, H, D, D), torch.zeros(B, H, D, D, dtype=torch.float64))

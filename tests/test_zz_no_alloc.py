@@ -82,3 +82,24 @@ def test_noalloc_checkpoints_between_tiles(device):
     assert_close(kv.cpu().numpy(), kv_ref, "bf16", "KV")
     for m in range(N // every):
         assert_close(ck.cpu().numpy()[:, :, m], ck_ref[:, :, m], "bf16", f"checkpoint {m}")
+
+
+def test_noalloc_through_the_binding(device):
+    """The binding's la_prefill_noalloc against la_prefill with a workspace, bit for bit, on a
+    chunked shape with checkpoints."""
+    import torch
+
+    B, H, N, d = 1, 2, 6000, 128
+    exact, raw = inputs(75, B, H, N, d, "bf16")
+    q, k, v = (to_device(x, "bf16", device) for x in raw)
+    sl = torch.from_numpy(SL2).to(device)
+    out = {}
+    for name, fn in (("noalloc", la.la_prefill_noalloc), ("workspace", la.la_prefill)):
+        kv = torch.zeros(B, H, d, d, device=device)
+        o = torch.empty_like(q)
+        ck = torch.zeros(B, H, N // 1024, d, d, device=device)
+        fn(q, k, v, sl, kv, o=o, ckpt=ck, ckpt_every=1024)
+        torch.cuda.synchronize()
+        out[name] = (o.cpu(), kv.cpu(), ck.cpu())
+    for x, y in zip(out["noalloc"], out["workspace"]):
+        assert torch.equal(x, y)
