@@ -39,11 +39,12 @@
 // Wave roles (8 waves, two per SIMD, so one wave's latencies hide behind the
 // other's work).  Output waves 0..3: wave w owns query rows 16w..16w+15 of
 // each 64-token tile -- scores, masking, P V, the inter-tile term and the
-// output store.  Each output wave loads its own 16 rows of Q a whole row per
-// 16 lanes (a load straight into operand layout would touch 16 rows and 16
-// cache lines per instruction; row-wise loads measured 2.5% faster overall),
-// converts them and stages them in its own part of an LDS tile, from which it
-// reads the B operand of S^T and of the transposed inter product.  The outputs
+// output store.  Each output wave loads its own 16 rows of Q as 8 rows x 128
+// bytes per instruction (a load straight into operand layout touches 16 rows
+// and 16 cache lines per instruction; whole 256-byte rows raised the L2 misses
+// of the sibling slices' re-reads), converts them and stages them in its own
+// part of an LDS tile, from which it reads the B operand of S^T and of the
+// transposed inter product.  The outputs
 // are accumulated transposed, O^T = KV^T Q^T + V^T P^T, so a lane holds four
 // consecutive value columns of one row and stages them with one 8-byte LDS
 // write before the 16-byte global stores.  State waves 4..7: the global
@@ -479,26 +480,31 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
         drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
-    // Q rows of this wave: load i covers RPI whole rows, LPR lanes of 16 bytes per row (row blocks in
-    // an order rotated by the slice, so that sibling slices start on different rows).
-    constexpr int LPR = D / 8, RPI = 64 / LPR;
-    auto q_row = [&](int i) __attribute__((always_inline)) { return 16 * w + RPI * ((i + slice) & (NQ - 1)) + l / LPR; };
+    // Q of this wave: load i covers 8 rows x 128 bytes, 8 lanes of 16 bytes per row: row half (b & 1)
+    // of the wave's 16 rows, byte half (b >> 1) of each row (d = 128), with b = i rotated by the
+    // slice so that sibling slices start on different blocks.
+    auto q_row = [&](int i) __attribute__((always_inline)) {
+        return 16 * w + 8 * (((i + slice) & (NQ - 1)) & 1) + (l >> 3);
+    };
+    auto q_piece = [&](int i) __attribute__((always_inline)) {  // 16-byte piece within the row
+        return 8 * (((i + slice) & (NQ - 1)) >> 1) + (l & 7);
+    };
     auto load_q = [&](QR& R, int tile) __attribute__((always_inline)) {
         const int64_t t0 = tile_row0(tile);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + t0 * sn, tile_bytes(tile));
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) R.q[i] = buf_load16(rq, row_off(tile, q_row(i)) + 16u * (l % LPR));
+        for (int i = 0; i < NQ; ++i) R.q[i] = buf_load16(rq, row_off(tile, q_row(i)) + 16u * q_piece(i));
     };
     // loaded rows -> LDS buffer `buf` (float16 with float16 products, else bf16), SiLU first if asked
     auto stage_q = [&](const QR& R, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const uint4 qx = silu_q ? silu8(R.q[i]) : R.q[i];
-            *reinterpret_cast<uint4*>(&sQ[buf][q_row(i) * KS + 8 * (l % LPR)]) = F16 ? bf16x8_to_f16(qx) : qx;
+            *reinterpret_cast<uint4*>(&sQ[buf][q_row(i) * KS + 8 * q_piece(i)]) = F16 ? bf16x8_to_f16(qx) : qx;
         }
     };
     // Outputs of tile `tile` from LDS buffers `buf`.  R holds the loaded rows of tile + 1, which are
-    // staged into the other Q buffer once the products are issued; R then loads tile + 3.
+    // staged into the other Q buffer once the products are issued; R then loads tile + 2.
     auto compute_out = [&](auto wc, QR& R, int buf, int tile) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
         const int64_t t0 = tile_row0(tile);
@@ -570,7 +576,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // tile they delay the products, at its end the next tile's Q)
         __builtin_amdgcn_sched_barrier(0);
         if (tile + 1 < n_tiles) stage_q(R, buf ^ 1);
-        load_q(R, tile + 3);
+        load_q(R, tile + 2);
         __builtin_amdgcn_sched_barrier(0);
         // intra-tile output, transposed like the inter term: (P V)^T = V^T P^T (keys 32k2 +
         // {4g..4g+3, 16+4g..16+4g+3} in each 32-key step; the S^T accumulators are P^T's operand)
@@ -684,25 +690,23 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         else if (j == wk.nck - 1) store_state(swc, st, a.kv + u * d2);
     };
     auto out_loop = [&](auto wc) __attribute__((always_inline)) {
-        // Q of tile t is staged during tile t - 1 from register set t % 2, which was loaded during
-        // tile t - 3 (two tiles of latency, as for K and V); tile 0 is staged here.
-        QR QA, QB;
-        load_q(QA, 0);
+        // Q of tile t is loaded during tile t - 2 and staged during tile t - 1, a tile of latency
+        // (measured as fast as two register sets loaded a tile earlier); tile 0 is staged here.
+        QR Q;
+        load_q(Q, 0);
         __builtin_amdgcn_sched_barrier(0);
-        load_q(QB, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_q(QA, 0);
-        load_q(QA, 2);
+        stage_q(Q, 0);
+        load_q(Q, 1);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         int tile = 0;
         for (; tile + 2 <= n_tiles; tile += 2) {
-            compute_out(wc, QB, 0, tile);
+            compute_out(wc, Q, 0, tile);
             __syncthreads();
-            compute_out(wc, QA, 1, tile + 1);
+            compute_out(wc, Q, 1, tile + 1);
             __syncthreads();
         }
-        if (tile < n_tiles) compute_out(wc, QB, 0, tile);
+        if (tile < n_tiles) compute_out(wc, Q, 0, tile);
     };
     // Each wave runs a loop specialised to its role and index (static work lists, no per-tile
     // branches); all loops pass the same barriers: one after the prologue and one between tiles.
