@@ -39,12 +39,14 @@
 // Wave roles (8 waves, two per SIMD, so one wave's latencies hide behind the
 // other's work).  Output waves 0..3: wave w owns query rows 16w..16w+15 of
 // each 64-token tile -- scores, masking, P V, the inter-tile term and the
-// output store.  Each output wave loads its own 16 rows of Q as 8 rows x 128
-// bytes per instruction (a load straight into operand layout touches 16 rows
-// and 16 cache lines per instruction; whole 256-byte rows raised the L2 misses
-// of the sibling slices' re-reads), converts them and stages them in its own
-// part of an LDS tile, from which it reads the B operand of S^T and of the
-// transposed inter product.  The outputs
+// output store.  Q is the B operand of S^T and of the transposed inter
+// product.  With float16 products each output wave loads its own 16 rows of Q
+// as 8 rows x 128 bytes per instruction (a load straight into operand layout
+// touches 16 rows and 16 cache lines per instruction; whole 256-byte rows
+// raised the L2 misses of the sibling slices' re-reads), converts them and
+// stages them in its own part of an LDS tile, from which it reads the operand.
+// WIDE operands load Q straight into operand layout (the staging's LDS traffic
+// made the backward's passes 7% slower).  The outputs
 // are accumulated transposed, O^T = KV^T Q^T + V^T P^T, so a lane holds four
 // consecutive value columns of one row and stages them with one 8-byte LDS
 // write before the 16-byte global stores.  State waves 4..7: the global
@@ -219,7 +221,7 @@ template <int N> struct IntC { static constexpr int value = N; };
 // The four value slices of a head read the same Q and K rows at nearly the same time; each slice
 // walks the 64-byte column blocks (Q) and 16-row blocks (K) starting at its own index, so that the
 // simultaneous requests of sibling slices fall on different cache lines.
-// Q rows as loaded: piece i of a lane is 16 bytes of one of the wave's 16 rows (see load_q)
+// Q as loaded: 16 bytes per piece of one of the wave's 16 rows (see load_q)
 template <int D> struct QRegs { uint4 q[D / 32]; };
 // K chunks st_id + 256m of the 64 x D tile; V slice row st_id/4
 template <int D> struct KVRegs { uint4 k[D / 32]; uint4 v; };
@@ -253,7 +255,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     __shared__ __attribute__((aligned(16))) u16 sS[2][SW * D];
     __shared__ __attribute__((aligned(16))) u16 sSl[OUT && !F16 ? 2 : 1][OUT && !F16 ? SW * D : 8];
     __shared__ __attribute__((aligned(16))) u16 sO[BK * OS];
-    __shared__ __attribute__((aligned(16))) u16 sQ[OUT ? 2 : 1][OUT ? BK * KS : 8];  // Q tile, K's row stride
+    constexpr bool QLDS = F16;  // Q staged in LDS (see the header comment)
+    __shared__ __attribute__((aligned(16))) u16 sQ[QLDS ? 2 : 1][QLDS ? BK * KS : 8];  // Q tile, K's row stride
 
     int64_t group;
     int slice;
@@ -480,13 +483,16 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
         drow = decay_pow(nsl, (float)(16 * w + lr + 1));
     }
-    // Q of this wave: load i covers 8 rows x 128 bytes, 8 lanes of 16 bytes per row: row half (b & 1)
-    // of the wave's 16 rows, byte half (b >> 1) of each row (d = 128), with b = i rotated by the
-    // slice so that sibling slices start on different blocks.
+    // Q of this wave.  Staged (QLDS): load i covers 8 rows x 128 bytes, 8 lanes of 16 bytes per row:
+    // row half (b & 1) of the wave's 16 rows, byte half (b >> 1) of each row (d = 128).  In operand
+    // layout: piece i is row 16w + lr, features 32b + 8g .. +7.  Either way b is i rotated by the
+    // slice, so that sibling slices start on different blocks.
     auto q_row = [&](int i) __attribute__((always_inline)) {
+        if constexpr (!QLDS) return 16 * w + lr;
         return 16 * w + 8 * (((i + slice) & (NQ - 1)) & 1) + (l >> 3);
     };
     auto q_piece = [&](int i) __attribute__((always_inline)) {  // 16-byte piece within the row
+        if constexpr (!QLDS) return 4 * ((i + slice) & (NQ - 1)) + g;
         return 8 * (((i + slice) & (NQ - 1)) >> 1) + (l & 7);
     };
     auto load_q = [&](QR& R, int tile) __attribute__((always_inline)) {
@@ -503,15 +509,23 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             *reinterpret_cast<uint4*>(&sQ[buf][q_row(i) * KS + 8 * q_piece(i)]) = F16 ? bf16x8_to_f16(qx) : qx;
         }
     };
-    // Outputs of tile `tile` from LDS buffers `buf`.  R holds the loaded rows of tile + 1, which are
-    // staged into the other Q buffer once the products are issued; R then loads tile + 2.
+    // Outputs of tile `tile` from LDS buffers `buf`.  Staged Q: R holds the loaded rows of tile + 1,
+    // which are staged into the other Q buffer once the products are issued.  Otherwise R holds the
+    // operands of this tile.  Either way R then loads tile + 2.
     auto compute_out = [&](auto wc, QR& R, int buf, int tile) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
         const int64_t t0 = tile_row0(tile);
         // Q operand: row 16W + lr, features 32((ks + slice) % NQ) + 8g .. +7 (the order of kop below)
         bf16x8 qf[NQ];
 #pragma unroll
-        for (int ks = 0; ks < NQ; ++ks) qf[ks] = lds8(&sQ[buf][(16 * W + lr) * KS + 32 * ((ks + slice) & (NQ - 1)) + 8 * g]);
+        for (int ks = 0; ks < NQ; ++ks) {
+            if constexpr (QLDS) {
+                qf[ks] = lds8(&sQ[buf][(16 * W + lr) * KS + 32 * ((ks + slice) & (NQ - 1)) + 8 * g]);
+            } else {
+                const uint4 qx = silu_q ? silu8(R.q[ks]) : R.q[ks];
+                qf[ks] = __builtin_bit_cast(bf16x8, F16 ? bf16x8_to_f16(qx) : qx);
+            }
+        }
         // the gate values of this lane's outputs (row 16W + lr, columns 16jt + 4g..+3), read early
         // so the loads are long done when the products are
         uint2 gx[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
@@ -575,7 +589,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // (the fences keep the staging and refill at this point, measured best: at the start of the
         // tile they delay the products, at its end the next tile's Q)
         __builtin_amdgcn_sched_barrier(0);
-        if (tile + 1 < n_tiles) stage_q(R, buf ^ 1);
+        if constexpr (QLDS)
+            if (tile + 1 < n_tiles) stage_q(R, buf ^ 1);
         load_q(R, tile + 2);
         __builtin_amdgcn_sched_barrier(0);
         // intra-tile output, transposed like the inter term: (P V)^T = V^T P^T (keys 32k2 +
@@ -690,23 +705,29 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         else if (j == wk.nck - 1) store_state(swc, st, a.kv + u * d2);
     };
     auto out_loop = [&](auto wc) __attribute__((always_inline)) {
-        // Q of tile t is loaded during tile t - 2 and staged during tile t - 1, a tile of latency
-        // (measured as fast as two register sets loaded a tile earlier); tile 0 is staged here.
-        QR Q;
-        load_q(Q, 0);
+        // Staged Q: Q of tile t is loaded during tile t - 2 and staged during tile t - 1, a tile of
+        // latency in one register set (measured as fast as two sets loaded a tile earlier); tile 0 is
+        // staged here.  Otherwise two register sets alternate, each loaded two tiles ahead.
+        QR QA, QB;
+        load_q(QA, 0);
         __builtin_amdgcn_sched_barrier(0);
-        stage_q(Q, 0);
-        load_q(Q, 1);
+        if constexpr (QLDS) {
+            stage_q(QA, 0);
+            load_q(QA, 1);
+        } else {
+            load_q(QB, 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        QR& Q1 = QLDS ? QA : QB;
         int tile = 0;
         for (; tile + 2 <= n_tiles; tile += 2) {
-            compute_out(wc, Q, 0, tile);
+            compute_out(wc, QA, 0, tile);
             __syncthreads();
-            compute_out(wc, Q, 1, tile + 1);
+            compute_out(wc, Q1, 1, tile + 1);
             __syncthreads();
         }
-        if (tile < n_tiles) compute_out(wc, Q, 0, tile);
+        if (tile < n_tiles) compute_out(wc, QA, 0, tile);
     };
     // Each wave runs a loop specialised to its role and index (static work lists, no per-tile
     // branches); all loops pass the same barriers: one after the prologue and one between tiles.
