@@ -667,9 +667,9 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         __builtin_amdgcn_sched_barrier(0);
         stage_tile(RA, 0, 0);
         if (OUT) write_state_copy(swc, st, 0);
-        // The state waves carry the serial chain (each tile's state copy feeds the next tile's
-        // outputs): they win instruction-issue ties on their SIMD (about 2.5% faster overall).
-        __builtin_amdgcn_s_setprio(1);
+        // (Both roles issue at the same priority: raising the state waves', which carry the chain
+        // from one tile's state to the next tile's inter term, paid before the Q staging and costs
+        // 0.6-2.5% with it.)
         // Checkpoints fall on tile ends (ckpt_every is a multiple of the tile and chunks start on
         // tile boundaries), so a per-tile counter replaces a 64-bit division per tile: ck_phase
         // counts the tiles since the last checkpoint, ck_slot is the next checkpoint's slot.
