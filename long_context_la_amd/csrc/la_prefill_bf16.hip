@@ -51,9 +51,9 @@
 // consecutive value columns of one row and stages them with one 8-byte LDS
 // write before the 16-byte global stores.  State waves 4..7: the global
 // loads and LDS staging of K and V, the decay-weighted W V, and the state
-// update, with the state's 16 tiles of 16x16 split 8/5/2/1 (more state work
-// on the SIMDs whose output waves own the earlier, lighter query rows; 6/5/3/2
-// with WIDE operands).  The state waves publish the state after tile b (a
+// update, with the state's 16 tiles of 16x16 split 6/5/3/2 (more state work
+// on the SIMDs whose output waves own the earlier, lighter query rows, so that
+// each SIMD issues about the same number of MFMAs).  The state waves publish the state after tile b (a
 // float16 copy in LDS, or a bf16 hi + lo pair) for the output waves' inter
 // term of tile b+1.  Without outputs (state-only modes) the
 // kernel runs the four state waves alone.
@@ -320,19 +320,18 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
     // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), D/8 of them, of state
     // wave sw: [first, first + count).  With outputs the split moves state work off the SIMDs whose
-    // output waves own the later query rows (more score blocks): at d = 128, 8/5/2/1 of 16 with
-    // float16 operands (measured 1.2% faster than 6/5/3/2) and 6/5/3/2 with hi + lo pairs (which evens
-    // out their MFMA counts and keeps the registers of a pair within budget); 3/3/1/1 of 8 at d = 64;
-    // equal shares without outputs.
+    // output waves own the later query rows (more score blocks): at d = 128, 6/5/3/2 of 16 (which
+    // evens out the MFMA counts per SIMD; measured against 8/5/2/1, 7/6/2/1, 8/4/3/1, 5/5/3/3,
+    // 6/4/3/3 and 7/5/2/2), 3/3/1/1 of 8 at d = 64; equal shares without outputs.
     auto st_first = [](int sw) constexpr {
         if (!OUT) return (D / 32) * sw;
         if (D == 64) return sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7;
-        return F16 ? (sw == 0 ? 0 : sw == 1 ? 8 : sw == 2 ? 13 : 15) : (sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14);
+        return sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14;
     };
     auto st_count = [](int sw) constexpr {
         if (!OUT) return D / 32;
         if (D == 64) return sw <= 1 ? 3 : 1;
-        return F16 ? (sw == 0 ? 8 : sw == 1 ? 5 : sw == 2 ? 2 : 1) : (sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2);
+        return sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2;
     };
 
     auto load_kv = [&](KR& R, int tile) __attribute__((always_inline)) {
