@@ -53,10 +53,10 @@
 // loads and LDS staging of K and V, the decay-weighted W V, and the state
 // update, with the state's 16 tiles of 16x16 split 6/5/3/2 (more state work
 // on the SIMDs whose output waves own the earlier, lighter query rows, so that
-// each SIMD issues about the same number of MFMAs).  The state waves publish the state after tile b (a
-// float16 copy in LDS, or a bf16 hi + lo pair) for the output waves' inter
-// term of tile b+1.  Without outputs (state-only modes) the
-// kernel runs the four state waves alone.
+// each SIMD issues about the same number of MFMAs).  The state waves publish
+// the state after tile b (a float16 copy in LDS, or a bf16 hi + lo pair) for
+// the output waves' inter term of tile b+1.  Without outputs (state-only
+// modes) the kernel runs the four state waves alone.
 //
 // MFMA: v_mfma_f32_16x16x32_f16 / _bf16 (A 16x32, B 32x16, C 16x16 fp32; lane l holds
 // A row l%16 / B column l%16 and 8 k-values of group g = l/16; C column l%16,
@@ -219,8 +219,9 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
 template <int N> struct IntC { static constexpr int value = N; };
 
 // The four value slices of a head read the same Q and K rows at nearly the same time; each slice
-// walks the 64-byte column blocks (Q) and 16-row blocks (K) starting at its own index, so that the
-// simultaneous requests of sibling slices fall on different cache lines.
+// walks its blocks of Q (8 rows x 128 bytes when staged, 64-byte column blocks in operand layout)
+// and of K (16-row blocks) starting at its own index, so that the simultaneous requests of sibling
+// slices fall on different cache lines.
 // Q as loaded: 16 bytes per piece of one of the wave's 16 rows (see load_q)
 template <int D> struct QRegs { uint4 q[D / 32]; };
 // K chunks st_id + 256m of the 64 x D tile; V slice row st_id/4
@@ -666,9 +667,9 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         __builtin_amdgcn_sched_barrier(0);
         stage_tile(RA, 0, 0);
         if (OUT) write_state_copy(swc, st, 0);
-        // (Both roles issue at the same priority: raising the state waves', which carry the chain
-        // from one tile's state to the next tile's inter term, paid before the Q staging and costs
-        // 0.6-2.5% with it.)
+        // Both roles issue at the same priority.  (Raising the state waves' priority, as they carry
+        // the chain from one tile's state to the next tile's inter term, paid before Q was staged
+        // in LDS and has cost 0.6-2.5% since.)
         // Checkpoints fall on tile ends (ckpt_every is a multiple of the tile and chunks start on
         // tile boundaries), so a per-tile counter replaces a 64-bit division per tile: ck_phase
         // counts the tiles since the last checkpoint, ck_slot is the next checkpoint's slot.

@@ -90,8 +90,17 @@ def cpu_description():
 
 
 def source_digest(path=PREFILL_SOURCE):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code: line comments, trailing blanks and empty lines are
+    dropped first, so that editing a comment does not disown the profiles of unchanged code (the
+    file holds no string literal with a double slash)."""
+    lines = []
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            cut = line.find("//")
+            line = (line if cut < 0 else line[:cut]).rstrip()
+            if line:
+                lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 # ------------------------------------------------------------------ raw CSV access
@@ -283,7 +292,7 @@ def _header(title, names, out_root):
 def summarize_stats(out_root, name, title, last_of=None):
     rows = dispatches(_csv(out_root, name, "kernel_trace"))
     lines = _header(title, [name], out_root)
-    lines.append(f"# kernel source sha256[:16] of la_prefill_bf16.hip: {source_digest()}")
+    lines.append(f"# kernel code digest (sha256[:16] of la_prefill_bf16.hip without comments): {source_digest()}")
     lines.append("# Durations from the kernel trace, all dispatches of the run (settling, warm-up and timed steps).")
     if last_of:
         pattern, wg, n = last_of
