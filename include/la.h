@@ -124,11 +124,14 @@ la_status la_state_init(float* kv, const float* kv0, int64_t batch, int64_t head
  * computed from a zero state, the prefixes are combined, and every chunk then
  * runs from its own prefix, so a long sequence fills all compute units.  The
  * result equals the serial recurrence.  Returns n when one chunk is used, a
- * positive multiple of 64 otherwise, or -1 for invalid shapes.
+ * positive multiple of 64 otherwise, or -1 for invalid shapes.  For LA_BF16 at
+ * d = 128 it describes a prefill with outputs (those may split the value
+ * columns 64 instead of 32 per workgroup, which changes the chunking).
  */
 int64_t la_prefill_chunk_tokens(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d);
 
-/* Bytes of device workspace la_prefill needs for this shape (0 when it needs none). */
+/* Bytes of device workspace la_prefill needs for this shape (0 when it needs none),
+ * with or without outputs. */
 size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d);
 
 /*
@@ -257,7 +260,7 @@ la_status la_prefill_varlen_ex(la_dtype dt, const void* q, const void* k, const 
  * la_prefill without checkpoints).  The SiLU flags act inside the prefill
  * kernels.  LA_GATE alone is applied in the prefill kernel's output store.
  * With LA_NORM, whose mean runs over all d features while each prefill
- * workgroup owns a slice of 32 value columns, the prefill writes o and one
+ * workgroup owns a slice of 32 or 64 value columns, the prefill writes o and one
  * more memory-bound pass normalises (and gates) it in place.  o must not be
  * NULL when LA_NORM or LA_GATE is set; gate must not overlap o.  Workspace as
  * for la_prefill.

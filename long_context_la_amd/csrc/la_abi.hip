@@ -41,16 +41,18 @@ la_status launch_status(hipError_t e, const char* what)
 
 }  // namespace
 
-Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk_override)
+Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk_override, int slice_w)
 {
     Plan p;
-    p.slices = (int)(d / kSliceW);
+    p.slices = (int)(d / slice_w);
     const int64_t units = batch * heads * p.slices;
     int64_t chunk = n;
     if (chunk_override > 0) {
         chunk = chunk_override;
-    } else if (units < kTargetGroups && n > kMinChunk) {
-        const int64_t want = (kTargetGroups + units - 1) / units;  // chunks per sequence
+    } else if (2 * units <= kTargetGroups && n > kMinChunk) {
+        // chunks per sequence: as many as keep the workgroups within one round (rounded up, more
+        // than half a round of unchunked workgroups would turn into two rounds plus a summary pass)
+        const int64_t want = kTargetGroups / units;
         int64_t c = (n + want - 1) / want;
         c = ((c + kBlock - 1) / kBlock) * kBlock;
         if (c < kMinChunk) c = kMinChunk;
@@ -132,6 +134,17 @@ size_t workspace_bytes_for(const Plan& p, int64_t batch, int64_t heads, int64_t 
     return (size_t)batch * (size_t)heads * (size_t)slots * (size_t)d * (size_t)d * sizeof(float);
 }
 
+// Workspace of a prefill of this shape whatever it computes: the plans of both slice widths (the
+// size queries do not know whether outputs are asked for).
+size_t prefill_workspace_any(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk_tokens)
+{
+    const size_t a = workspace_bytes_for(make_plan(batch, heads, n, d, chunk_tokens), batch, heads, d);
+    const size_t b = workspace_bytes_for(
+        make_plan(batch, heads, n, d, chunk_tokens, fwd_slice_w(dt, batch, heads, n, d, true, false, 0)), batch, heads,
+        d);
+    return a > b ? a : b;
+}
+
 la_status check_fusion(const la_fusion* fu, const void* o)
 {
     if (!fu) return LA_OK;
@@ -187,6 +200,8 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
     la_status s = prefill_checks(dt, q, k, v, o, batch, heads, n, d, sb, sh, sn, slopes, kv, ckpt, ckpt_every,
                                  chunk_tokens, fu);
     if (s != LA_OK || n == 0) return s;
+    const int slice_w = fwd_slice_w(dt, batch, heads, n, d, o != nullptr, rev || wide,
+                                    (fu ? fu->flags : 0u) & (LA_SILU_Q | LA_SILU_K | LA_SILU_V));
 
     if (ckpt && ckpt_every % kBlock != 0) {
         // Checkpoints inside a tile: the sequence runs as one prefill per checkpoint segment of
@@ -203,7 +218,9 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
             const int64_t len = m < n_ck ? ckpt_every : n - t0;
             // a segment is chunked only when its own chunk workspace fits in the caller's
             int64_t ct = chunk_tokens;
-            if (ct == 0 && workspace_bytes_for(make_plan(batch, heads, len, d, 0), batch, heads, d) >
+            const int seg_w = fwd_slice_w(dt, batch, heads, len, d, o != nullptr, rev || wide,
+                                          (fu ? fu->flags : 0u) & (LA_SILU_Q | LA_SILU_K | LA_SILU_V));
+            if (ct == 0 && workspace_bytes_for(make_plan(batch, heads, len, d, 0, seg_w), batch, heads, d) >
                                (workspace ? workspace_bytes : 0))
                 ct = ((len + kBlock - 1) / kBlock) * kBlock;
             s = prefill_impl(dt, at(q, t0), at(k, t0), at(v, t0), o ? (void*)at(o, t0) : nullptr, batch, heads, len, d,
@@ -219,7 +236,7 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
         }
         return LA_OK;
     }
-    const Plan p = make_plan(batch, heads, n, d, chunk_tokens);
+    const Plan p = make_plan(batch, heads, n, d, chunk_tokens, slice_w);
     const int64_t n_sub = p.n_chunks > 1 ? (p.n_chunks - 1) * p.sub : 0;
     if (batch * heads * (p.n_chunks > n_sub ? p.n_chunks : n_sub) > kMaxUnits)
         return fail(LA_ERR_UNSUPPORTED, "more than 2^20 (batch, head, chunk) work items: use a larger chunk_tokens");
@@ -343,7 +360,7 @@ la_status prefill_noalloc_impl(la_dtype dt, const void* q, const void* k, const 
     la_status s = prefill_checks(dt, q, k, v, o, batch, heads, n, d, sb, sh, sn, slopes, kv, ckpt, ckpt_every, 0,
                                  nullptr);
     if (s != LA_OK || n == 0) return s;
-    const size_t need = workspace_bytes_for(make_plan(batch, heads, n, d, 0), batch, heads, d);
+    const size_t need = prefill_workspace_any(dt, batch, heads, n, d, 0);
     if (need > kScratchBytes)
         return fail(LA_ERR_UNSUPPORTED, "this shape needs " + std::to_string(need) +
                                             " bytes of chunk states; la_prefill_noalloc holds " +
@@ -783,7 +800,7 @@ la_status la_state_init(float* kv, const float* kv0, int64_t batch, int64_t head
 int64_t la_prefill_chunk_tokens(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)
 {
     if (check_shape(dt, batch, heads, n, d) != LA_OK) return -1;
-    const Plan p = make_plan(batch, heads, n, d, 0);
+    const Plan p = make_plan(batch, heads, n, d, 0, fwd_slice_w(dt, batch, heads, n, d, true, false, 0));
     return p.n_chunks > 1 ? p.chunk : n;
 }
 
@@ -792,7 +809,7 @@ size_t la_prefill_workspace_size_ex(la_dtype dt, int64_t batch, int64_t heads, i
 {
     if (check_shape(dt, batch, heads, n, d) != LA_OK) return 0;
     if (chunk_tokens < 0 || (chunk_tokens > 0 && chunk_tokens % kBlock != 0)) return 0;
-    return workspace_bytes_for(make_plan(batch, heads, n, d, chunk_tokens), batch, heads, d);
+    return prefill_workspace_any(dt, batch, heads, n, d, chunk_tokens);
 }
 
 size_t la_prefill_workspace_size(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d)

@@ -28,13 +28,19 @@
 // Without outputs (state-only and chunk-summary modes) the state update keeps
 // bfloat16 operands, with W V as a hi + lo pair.
 //
-// Decomposition.  A workgroup owns one (batch, head, chunk, slice of 32 value
-// columns): both the state's columns and the outputs' columns split by value
-// column with no communication, which gives 4 workgroups per head without a
-// second pass over K and V.  Q and K rows are read by the four slices of a
-// head; their workgroups sit on one XCD so the re-reads hit L2.  Sequences
+// Decomposition.  A workgroup owns one (batch, head, chunk, slice of 32 or 64
+// value columns): both the state's columns and the outputs' columns split by
+// value column with no communication, which gives 4 (or 2) workgroups per head
+// without a second pass over K and V.  Q and K rows are read by every slice of
+// a head; their workgroups sit on one XCD so the re-reads hit L2.  Sequences
 // with too few heads to fill the GPU are also cut into chunks (la_scan.hip
-// combines the chunk summaries).
+// combines the chunk summaries).  The 64-column instantiation (float16
+// outputs at d = 128) does the score products and the Q and K conversions
+// once for twice the columns: a tile takes about 1.55x as long, so a head
+// costs ~23% less GPU time.  The host uses it where the work is split
+// anyway (chunked sequences, or more (batch, head) pairs than one round of
+// 32-column workgroups holds); 64 heads of one sequence keep 32 columns,
+// which fill the GPU without the summary pass that two chunks would need.
 //
 // Wave roles (8 waves, two per SIMD, so one wave's latencies hide behind the
 // other's work).  Output waves 0..3: wave w owns query rows 16w..16w+15 of
@@ -51,9 +57,10 @@
 // consecutive value columns of one row and stages them with one 8-byte LDS
 // write before the 16-byte global stores.  State waves 4..7: the global
 // loads and LDS staging of K and V, the decay-weighted W V, and the state
-// update, with the state's 16 tiles of 16x16 split 6/5/3/2 (more state work
-// on the SIMDs whose output waves own the earlier, lighter query rows, so that
-// each SIMD issues about the same number of MFMAs).  The state waves publish
+// update, with the state's 16 tiles of 16x16 split 6/5/3/2 (32 tiles split
+// 12/10/6/4 with 64 columns: more state work on the SIMDs whose output waves
+// own the earlier, lighter query rows, so that each SIMD issues about the same
+// number of MFMAs).  The state waves publish
 // the state after tile b (a float16 copy in LDS, or a bf16 hi + lo pair) for
 // the output waves' inter term of tile b+1.  Without outputs (state-only
 // modes) the kernel runs the four state waves alone.
@@ -225,15 +232,24 @@ template <int N> struct IntC { static constexpr int value = N; };
 // Q as loaded: 16 bytes per piece of one of the wave's 16 rows (see load_q)
 template <int D> struct QRegs { uint4 q[D / 32]; };
 // K chunks st_id + 256m of the 64 x D tile; V slice row st_id/4
-template <int D> struct KVRegs { uint4 k[D / 32]; uint4 v; };
+template <int D, int NV> struct KVRegs { uint4 k[D / 32]; uint4 v[NV]; };
 
 // REV walks each sequence from its last token to its first (token index t of the recurrence is
 // memory row n-1-t), the order of the reverse state recurrence of the backward pass.  ACT enables
 // the SiLU prologue (which of q, k, v is chosen at run time); without it no activation code is
 // compiled in, since untaken branches inside the tile loops still cost about 10% here.
-template <int MODE, bool GATE, bool REV, bool ACT, int D, bool WIDE>
+template <int MODE, bool GATE, bool REV, bool ACT, int D, bool WIDE, int SWT>
 __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(FwdArgs a)
 {
+    static_assert(SWT == 32 || (SWT == 64 && D == 128 && MODE == kModeOut && !WIDE),
+                  "64-column slices only for float16 outputs at d = 128");
+    // value columns of this workgroup's slice, and the row strides that depend on it: V and W V
+    // rows of 96 B (32 columns) or 160 B (64 columns), so the 4 rows of a transposing read fall in
+    // disjoint banks; output staging rows likewise
+    constexpr int SW = SWT, VS = SWT + 16, OS = SWT + 16;
+    constexpr int NJ = SW / 16;         // 16-column tiles of the slice
+    constexpr int PPR = SW / 8;         // 16-byte pieces of a slice row
+    constexpr int NV = SW / 32;         // V pieces per state lane (64 rows x PPR pieces over 256 lanes)
     static_assert(!(GATE && REV), "the reverse walk has no epilogue");
     static_assert(D == 64 || D == 128, "head dimension 64 or 128");
     static_assert(!WIDE || MODE == kModeOut, "full-range operands matter only with outputs");
@@ -247,7 +263,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
     constexpr int NQ = D / 32;   // 32-feature steps of a score or inter product; also Q, K loads per lane
     constexpr int CPR = D / 8, CPR_LOG = D == 128 ? 4 : 3;  // 16-byte chunks per row of Q or K
     using QR = QRegs<D>;
-    using KR = KVRegs<D>;
+    using KR = KVRegs<D, NV>;
     constexpr int SW0 = OUT ? 4 : 0;  // first state wave
     __shared__ __attribute__((aligned(16))) u16 sK[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sV[2][BK * VS];
@@ -319,19 +335,22 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 
     // ------------------------------------------------------------------ state waves
     const int st_id = tid - SW0 * 64;  // 0..255 within the state waves
-    // State tiles q = 2*it + jt (it: key rows 16it.., jt: value columns 16jt..), D/8 of them, of state
-    // wave sw: [first, first + count).  With outputs the split moves state work off the SIMDs whose
-    // output waves own the later query rows (more score blocks): at d = 128, 6/5/3/2 of 16 (which
+    // State tiles q = NJ*it + jt (it: key rows 16it.., jt: value columns 16jt..), D*SW/256 of them, of
+    // state wave sw: [first, first + count).  With outputs the split moves state work off the SIMDs
+    // whose output waves own the later query rows (more score blocks): at d = 128, 6/5/3/2 of 16 (which
     // evens out the MFMA counts per SIMD; measured against 8/5/2/1, 7/6/2/1, 8/4/3/1, 5/5/3/3,
-    // 6/4/3/3 and 7/5/2/2), 3/3/1/1 of 8 at d = 64; equal shares without outputs.
+    // 6/4/3/3 and 7/5/2/2), 12/10/6/4 of 32 with 64 columns (48 MFMAs per SIMD and tile on each),
+    // 3/3/1/1 of 8 at d = 64; equal shares without outputs.
     auto st_first = [](int sw) constexpr {
-        if (!OUT) return (D / 32) * sw;
+        if (!OUT) return (D * SW / 1024) * sw;
         if (D == 64) return sw == 0 ? 0 : sw == 1 ? 3 : sw == 2 ? 6 : 7;
+        if (SW == 64) return sw == 0 ? 0 : sw == 1 ? 12 : sw == 2 ? 22 : 28;
         return sw == 0 ? 0 : sw == 1 ? 6 : sw == 2 ? 11 : 14;
     };
     auto st_count = [](int sw) constexpr {
-        if (!OUT) return D / 32;
+        if (!OUT) return D * SW / 1024;
         if (D == 64) return sw <= 1 ? 3 : 1;
+        if (SW == 64) return sw == 0 ? 12 : sw == 1 ? 10 : sw == 2 ? 6 : 4;
         return sw == 0 ? 6 : sw == 1 ? 5 : sw == 2 ? 3 : 2;
     };
 
@@ -344,15 +363,24 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const int c = st_id + 256 * ((m + slice) & (NQ - 1));
             R.k[m] = buf_load16(rk, row_off(tile, c >> CPR_LOG) + 16u * (c & (CPR - 1)));
         }
-        R.v = buf_load16(rv, row_off(tile, st_id >> 2) + 16u * (st_id & 3));
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int c = st_id + 256 * m;
+            R.v[m] = buf_load16(rv, row_off(tile, c / PPR) + 16u * (c % PPR));
+        }
     };
     // Decay weights, computed once: lambda^(L-1-r) for the V row r this lane stages (0 past the
     // tile's end) and lambda^L for the state, for a full tile and for the last tile, the only one
     // that can be shorter.
     const int L_last = tile_len(n_tiles - 1);
-    const float wt_full = decay_pow(nsl, (float)(BK - 1 - (st_id >> 2))) * kSc;
+    float wt_full[NV], wt_last[NV];
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+        const int r = (st_id + 256 * m) / PPR;
+        wt_full[m] = decay_pow(nsl, (float)(BK - 1 - r)) * kSc;
+        wt_last[m] = (r < L_last) ? decay_pow(nsl, (float)(L_last - 1 - r)) * kSc : 0.f;
+    }
     const float dl_full = decay_pow(nsl, (float)BK);
-    const float wt_last = ((st_id >> 2) < L_last) ? decay_pow(nsl, (float)(L_last - 1 - (st_id >> 2))) * kSc : 0.f;
     const float dl_last = decay_pow(nsl, (float)L_last);
     // K and V rows into LDS buffer `buf` with the decay-weighted V: float16 (and W V scaled by 2^-8)
     // with float16 outputs, else bf16 with W V as a hi + lo pair (WIDE outputs, state-only and
@@ -365,9 +393,12 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const uint4 kx = silu_k ? silu8(R.k[m]) : R.k[m];
             *reinterpret_cast<uint4*>(&sK[buf][(c >> CPR_LOG) * KS + 8 * (c & (CPR - 1))]) = F16 ? bf16x8_to_f16(kx) : kx;
         }
-        const int r = st_id >> 2, off = r * VS + 8 * (st_id & 3);
-        const uint4 vx = silu_v ? silu8(R.v) : R.v;
-        const float wt = (L == BK) ? wt_full : wt_last;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+        const int c = st_id + 256 * m;
+        const int off = (c / PPR) * VS + 8 * (c % PPR);
+        const uint4 vx = silu_v ? silu8(R.v[m]) : R.v[m];
+        const float wt = (L == BK) ? wt_full[m] : wt_last[m];
         const uint32_t in[4] = {vx.x, vx.y, vx.z, vx.w};
         if constexpr (F16) {
             uint32_t hv[4], hw[4];
@@ -387,6 +418,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             *reinterpret_cast<uint4*>(&sVWh[buf][off]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
             *reinterpret_cast<uint4*>(&sVWl[buf][off]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
+        }
     };
     // state copy for the inter term, KV^T[value col][key row], 4 consecutive key rows per lane:
     // float16 (the accumulators hold the state scaled by 2^-8), or a bf16 hi + lo pair when WIDE
@@ -395,7 +427,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 #pragma unroll
         for (int k = 0; k < C; ++k) {
             const int q = F + k;
-            const int off = ss_off<D>(16 * (q & 1) + lr, 16 * (q >> 1) + 4 * g);
+            const int off = ss_off<D>(16 * (q % NJ) + lr, 16 * (q / NJ) + 4 * g);
             if constexpr (F16) {
                 *reinterpret_cast<uint2*>(&sS[buf][off]) = make_uint2(cvt2h(st[k][0], st[k][1]), cvt2h(st[k][2], st[k][3]));
             } else {
@@ -414,7 +446,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const int q = F + k;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                dst[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] = st[k][t] * kScInv;
+                dst[(16 * (q / NJ) + 4 * g + t) * D + slice * SW + 16 * (q % NJ) + lr] = st[k][t] * kScInv;
         }
     };
     auto load_state = [&](auto swc, f32x4* st, const float* src) __attribute__((always_inline)) {
@@ -424,7 +456,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             const int q = F + k;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                st[k][t] = src ? src[(16 * (q >> 1) + 4 * g + t) * D + slice * SW + 16 * (q & 1) + lr] * kSc : 0.f;
+                st[k][t] = src ? src[(16 * (q / NJ) + 4 * g + t) * D + slice * SW + 16 * (q % NJ) + lr] * kSc : 0.f;
         }
     };
     // KV <- lambda^L KV + K^T (W V) on this wave's state tiles
@@ -435,13 +467,13 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         for (int k = 0; k < C; ++k) st[k] *= dl;
         // key-row tiles it0..it1 cover this wave's state tiles; the two value-column tiles of one
         // key-row tile share its K^T operand
-        constexpr int IT0 = F >> 1, NIT = ((F + C - 1) >> 1) - IT0 + 1;
-        bf16x8 vh[2][2], vl[2][2], ka[2][NIT];
+        constexpr int IT0 = F / NJ, NIT = (F + C - 1) / NJ - IT0 + 1;
+        bf16x8 vh[2][NJ], vl[2][NJ], ka[2][NIT];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int k0 = 32 * ks + 8 * g;
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
+            for (int jt = 0; jt < NJ; ++jt) {
                 const int o = (k0 + tr_row) * VS + 16 * jt + tr_col;
                 vh[ks][jt] = join(lds_tr(&sVWh[buf][o]), lds_tr(&sVWh[buf][o + 4 * VS]));
                 if constexpr (!F16) vl[ks][jt] = join(lds_tr(&sVWl[buf][o]), lds_tr(&sVWl[buf][o + 4 * VS]));
@@ -459,10 +491,10 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             for (int k = 0; k < C; ++k) {
                 const int q = F + k;
                 if constexpr (F16) {
-                    st[k] = mfma_h(ka[ks][(q >> 1) - IT0], vh[ks][q & 1], st[k]);
+                    st[k] = mfma_h(ka[ks][q / NJ - IT0], vh[ks][q % NJ], st[k]);
                 } else {
-                    st[k] = mfma(ka[ks][(q >> 1) - IT0], vh[ks][q & 1], st[k]);
-                    st[k] = mfma(ka[ks][(q >> 1) - IT0], vl[ks][q & 1], st[k]);
+                    st[k] = mfma(ka[ks][q / NJ - IT0], vh[ks][q % NJ], st[k]);
+                    st[k] = mfma(ka[ks][q / NJ - IT0], vl[ks][q % NJ], st[k]);
                 }
             }
     };
@@ -528,19 +560,21 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         }
         // the gate values of this lane's outputs (row 16W + lr, columns 16jt + 4g..+3), read early
         // so the loads are long done when the products are
-        uint2 gx[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+        uint2 gx[NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) gx[jt] = make_uint2(0u, 0u);
         if constexpr (GATE) {
             const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gg + t0 * sn, tile_bytes(tile));
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
+            for (int jt = 0; jt < NJ; ++jt)
                 gx[jt] = buf_load8(rg, (uint32_t)(16 * W + lr) * row_bytes + 2u * (16 * jt + 4 * g));
         }
         // Issue every LDS operand read of the inter and score products up front (the fence keeps
         // the scheduler from sinking them next to their MFMAs, which would expose each read's
         // latency in turn).
-        bf16x8 sh[2][NQ], sl[2][NQ], kop[W + 1][NQ];
+        bf16x8 sh[NJ][NQ], sl[NJ][NQ], kop[W + 1][NQ];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
             for (int ks = 0; ks < NQ; ++ks) {
                 const int off = ss_off<D>(16 * jt + lr, 32 * ((ks + slice) & (NQ - 1)) + 8 * g);
@@ -555,9 +589,9 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         __builtin_amdgcn_sched_barrier(0);
         // inter-tile term, transposed: (Q KV)^T = KV^T Q^T, so a lane's accumulators hold one output
         // row (query lr) and four consecutive value columns 16jt + 4g..+3; rows scaled by lambda^(r+1)
-        f32x4 acc[2];
+        f32x4 acc[NJ];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
+        for (int jt = 0; jt < NJ; ++jt) {
             acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NQ; ++ks) {
@@ -585,7 +619,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
             }
         }
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) acc[jt] *= drow;
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] *= drow;
         // (the fences keep the staging and refill at this point, measured best: at the start of the
         // tile they delay the products, at its end the next tile's Q)
         __builtin_amdgcn_sched_barrier(0);
@@ -596,11 +630,11 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // intra-tile output, transposed like the inter term: (P V)^T = V^T P^T (keys 32k2 +
         // {4g..4g+3, 16+4g..16+4g+3} in each 32-key step; the S^T accumulators are P^T's operand)
         constexpr int NK2 = W / 2 + 1;
-        bf16x8 vop[NK2][2];
+        bf16x8 vop[NK2][NJ];
 #pragma unroll
         for (int k2 = 0; k2 < NK2; ++k2)
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
+            for (int jt = 0; jt < NJ; ++jt) {
                 const u16* vb = &sV[buf][tr_row * VS + 16 * jt + tr_col];
                 vop[k2][jt] = join(lds_tr(vb + (32 * k2 + 4 * g) * VS), lds_tr(vb + (32 * k2 + 16 + 4 * g) * VS));
             }
@@ -612,7 +646,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
                                        cvt2h(p[2 * k2 + 1][0], p[2 * k2 + 1][1]),
                                        cvt2h(p[2 * k2 + 1][2], p[2 * k2 + 1][3])));
 #pragma unroll
-                for (int jt = 0; jt < 2; ++jt) acc[jt] = mfma_h(vop[k2][jt], ph, acc[jt]);
+                for (int jt = 0; jt < NJ; ++jt) acc[jt] = mfma_h(vop[k2][jt], ph, acc[jt]);
             } else {
                 uint32_t hh[4], ll[4];
                 split2(p[2 * k2][0], p[2 * k2][1], hh[0], ll[0]);
@@ -622,7 +656,7 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
                 const bf16x8 ph = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
                 const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
 #pragma unroll
-                for (int jt = 0; jt < 2; ++jt) {
+                for (int jt = 0; jt < NJ; ++jt) {
                     acc[jt] = mfma(vop[k2][jt], ph, acc[jt]);
                     acc[jt] = mfma(vop[k2][jt], pl, acc[jt]);
                 }
@@ -631,23 +665,26 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
         // undo the 2^-8 of P and of the state copy
         if constexpr (F16)
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) acc[jt] *= 1.f / kHalfScale;
+            for (int jt = 0; jt < NJ; ++jt) acc[jt] *= 1.f / kHalfScale;
         // gate in float32, so the output is rounded to bf16 once
         if constexpr (GATE)
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) gate4(acc[jt], gx[jt]);
+            for (int jt = 0; jt < NJ; ++jt) gate4(acc[jt], gx[jt]);
         // output tile: stage this wave's 16 rows (8-byte runs of 4 columns), then 16-byte stores
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < NJ; ++jt)
             *reinterpret_cast<uint2*>(&sO[(16 * W + lr) * OS + 16 * jt + 4 * g]) =
                 make_uint2(cvt2(acc[jt][0], acc[jt][1]), cvt2(acc[jt][2], acc[jt][3]));
         wave_lds_sync();
         {
-            const int rr = 16 * W + (l >> 2), cc = 8 * (l & 3);
-            const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + t0 * sn, tile_bytes(tile));
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
-                                                   (int)(row_off(tile, rr) + 2u * cc), 0, 0);
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const int c = l + 64 * m, rr = 16 * W + c / PPR, cc = 8 * (c % PPR);
+                const uint4 x = *reinterpret_cast<const uint4*>(&sO[rr * OS + cc]);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
+                                                       (int)(row_off(tile, rr) + 2u * cc), 0, 0);
+            }
         }
     };
 
@@ -931,10 +968,10 @@ template <bool GATE, bool REV, bool ACT, int D, bool WIDE>
 void launch_mode(const FwdArgs& a, int mode, dim3 grid, hipStream_t stream)
 {
     if (mode == kModeOut)
-        hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT, D, WIDE>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((k_fwd_bf16<kModeOut, GATE, REV, ACT, D, WIDE, 32>), grid, dim3(512), 0, stream, a);
     else if (mode == kModeState)
-        hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT, D, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT, D, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_fwd_bf16<kModeState, false, REV, ACT, D, false, 32>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd_bf16<kModeLocal, false, REV, ACT, D, false, 32>), grid, dim3(256), 0, stream, a);
 }
 
 template <int D>
@@ -942,6 +979,14 @@ void launch_d(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
     const bool gate = a.gate && mode == kModeOut, act = a.act != 0;
+    if constexpr (D == 128) {
+        // 64-column slices (two per head): the plan chose them for float16 outputs without a prologue
+        if (a.slices * 64 == D) {
+            if (gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true, false, false, D, false, 64>), grid, dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, false, false, D, false, 64>), grid, dim3(512), 0, stream, a);
+            return;
+        }
+    }
     // the backward's passes: plain inputs, full-range operands
     if (a.rev) launch_mode<false, true, false, D, true>(a, mode, grid, stream);
     else if (a.wide) launch_mode<false, false, false, D, true>(a, mode, grid, stream);

@@ -237,9 +237,12 @@ def mfma_utilisation(pmc_csv, pattern, simds, xcds, tiles_per_simd=None, workgro
 # ------------------------------------------------------------------ the profiling runs
 BENCH = "python3 {root}/bench.py"
 ONLY_FULL = "--no-cpu-baseline --no-decode --no-backward --no-varlen --no-other-workloads"
-# The full-layer prefill kernel: outputs, no gate, forward walk, no SiLU prologue, d = 128, float16
-# operands (k_fwd_bf16<MODE, GATE, REV, ACT, D, WIDE>).
-MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false>"
+# The prefill kernel with outputs, no gate, forward walk, no SiLU prologue, d = 128, float16
+# operands (k_fwd_bf16<MODE, GATE, REV, ACT, D, WIDE, value columns per workgroup>): 32-column
+# slices for the full layer (64 heads fill the GPU unchunked), 64-column slices for the chunked
+# share and long-context prefills.
+MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false, 32>"
+WIDE_MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false, 64>"
 
 RUNS = {
     # name: (rocprofv3 arguments, bench arguments)
@@ -403,11 +406,11 @@ def summarize_all(out_root, profiles_dir=PROFILES):
         "prefill_full_hbm_traffic.txt": lambda: summarize_traffic(
             out_root, "full", MAIN_KERNEL, full_bytes, 256),
         "prefill_share_hbm_traffic.txt": lambda: summarize_traffic(
-            out_root, "share", MAIN_KERNEL, eight_heads(32768), 256,
+            out_root, "share", WIDE_MAIN_KERNEL, eight_heads(32768), 256,
             extra_kernels=(("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
                            ("prefix combine (k_scan_sub)", r"k_scan_sub", None))),
         "prefill_long_hbm_traffic.txt": lambda: summarize_traffic(
-            out_root, "long", MAIN_KERNEL, eight_heads(1 << 20), 256,
+            out_root, "long", WIDE_MAIN_KERNEL, eight_heads(1 << 20), 256,
             extra_kernels=(("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
                            ("prefix combine (k_scan_sub)", r"k_scan_sub", None))),
         "decode_128x64_hbm_traffic.txt": lambda: summarize_traffic(

@@ -102,18 +102,26 @@ def test_decode_and_state_init_validation():
 
 
 def test_plan_and_workspace_sizes():
-    # 64 heads x 4 value slices fill the GPU: one chunk, no workspace
+    # 64 heads x 4 value slices of 32 columns fill the GPU: one chunk, no workspace
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 64, 131072, 128) == 131072
     assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 0
-    # 8 heads: 8 chunks per sequence
+    # 2 x 64 heads: one round of 256 workgroups of 64 columns, no chunks
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 2, 64, 131072, 128) == 131072
+    assert la.la_prefill_workspace_size(la.LA_BF16, 2, 64, 131072, 128) == 0
+    # 8 heads: the 32-column plan would cut 8 chunks, so the 64-column plan runs: 16 chunks per
+    # sequence (8 x 2 slices x 16 = 256 workgroups)
     c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 32768, 128)
-    assert c == 4096
-    # prefix slots (8 per head) + summary slots: 7 chunks x 4 sub-chunks + 1, so that the summary
-    # pass has 8 x 28 = 224 >= 128 full-width workgroups
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * (8 + 1 + 7 * 4) * 128 * 128 * 4
+    assert c == 2048
+    # the size query covers both widths' plans (it does not know whether outputs are asked for):
+    # 64 columns: prefix slots (16 per head) + summary slots: 15 chunks x 2 sub-chunks + 1, so that the
+    # summary pass has 8 x 30 = 240 >= 128 full-width workgroups; 32 columns: 8 + 1 + 7 x 4
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * (16 + 1 + 15 * 2) * 128 * 128 * 4
     c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 1048576, 128)
-    assert c == 131072
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (8 + 1 + 7 * 4) * 128 * 128 * 4
+    assert c == 65536
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (16 + 1 + 15 * 2) * 128 * 128 * 4
+    # float32 keeps 32-column slices (4 per head at d = 128), and so does d = 64 (2 per head)
+    assert la.la_prefill_chunk_tokens(la.LA_F32, 1, 8, 32768, 128) == 4096
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 32768, 64) == 2048
     # sub-chunks stay >= 256 tokens and multiples of 64: a 1024-token chunk splits at most 4 ways
     assert la.la_prefill_workspace_size(la.LA_BF16, 1, 1, 4096, 128, chunk_tokens=1024) == (4 + 1 + 3 * 4) * 128 * 128 * 4
     # short sequences are not chunked

@@ -1,0 +1,105 @@
+"""GPU parity of the plans that give each bf16 workgroup 64 value columns (d = 128, float16
+products, no SiLU prologue), against the fp64 oracle, with the bars of tests/common.py:
+
+* one unchunked round of 64-column slices, where 32-column slices would need more than one
+  round of workgroups (more than 64 (batch, head) pairs): incoming states, checkpoints inside
+  and at the end of the tiles, the gate epilogue, determinism;
+* chunked plans with summaries (few heads, where the 32-column plan would cut 4 or more chunks).
+Other bf16 d = 128 tests with outputs, few (batch, head) pairs and sequences long enough for four
+or more chunks of at least 1024 tokens run these slices too.
+"""
+import numpy as np
+import pytest
+
+import long_context_la_amd as la
+import oracle
+from common import TOL, assert_close, half_ulp, inputs, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def layer_slopes(H):
+    # the 64-head layer's decay rates 2^(-8(h+1)/H)
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
+
+
+def run(B, H, N, seed, device, kv_in=None, ckpt_every=0, gate=None):
+    import torch
+
+    exact, raw = inputs(seed, B, H, N, 128, "bf16")
+    q, k, v = (to_device(x, "bf16", device) for x in raw)
+    slopes = layer_slopes(H)
+    ts = torch.from_numpy(slopes).to(device)
+    kv = (torch.zeros(B, H, 128, 128, dtype=torch.float32, device=device) if kv_in is None
+          else torch.from_numpy(np.ascontiguousarray(kv_in, np.float32)).to(device))
+    o = torch.empty_like(q)
+    ck = (torch.full((B, H, N // ckpt_every, 128, 128), float("nan"), dtype=torch.float32, device=device)
+          if ckpt_every else None)
+    if gate is None:
+        la.la_prefill(q, k, v, ts, kv, o=o, ckpt=ck, ckpt_every=ckpt_every)
+    else:
+        import synth
+
+        g = to_device(synth.f32_to_bf16_bits(gate), "bf16", device)
+        la.la_prefill_fused(q, k, v, ts, kv, o, gate=g)
+    torch.cuda.synchronize()
+    return exact, slopes, to_host(o), kv.cpu().numpy(), (ck.cpu().numpy() if ck is not None else None)
+
+
+@pytest.mark.parametrize("every", [256, 1000])
+def test_one_round_checkpoints(device, every):
+    B, H, N = 2, 64, 2000
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, B, H, N, 128) == N
+    rng = np.random.default_rng(5)
+    kv_in = (rng.standard_normal((B, H, 128, 128)) * 0.5).astype(np.float32)
+    exact, slopes, o, kv, ck = run(B, H, N, 62, device, kv_in=kv_in, ckpt_every=every)
+    o_ref, kv_ref, ck_ref = oracle.recurrent(*exact, slopes, kv_in=kv_in, ckpt_every=every)
+    assert_close(o, o_ref, "bf16", "O with checkpoints", stored="bf16")
+    assert_close(kv, kv_ref, "bf16", "KV with checkpoints")
+    assert not np.isnan(ck).any(), "a checkpoint slot was left unwritten"
+    assert_close(ck.reshape(-1, *ck.shape[2:])[:, None], ck_ref.reshape(-1, *ck_ref.shape[2:])[:, None], "bf16",
+                 "checkpoints")
+
+
+def test_one_round_gate(device):
+    B, H, N = 2, 64, 700
+    rng = np.random.default_rng(7)
+    import synth
+
+    g = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((rng.standard_normal((B, H, N, 128)) * 2.0).astype(np.float32)))
+    exact, slopes, o, kv, _ = run(B, H, N, 63, device, gate=g)
+    o_pre, kv_ref, _ = oracle.recurrent(*exact, slopes)
+    sg = oracle.sigmoid(g.astype(np.float64))
+    want = o_pre * sg
+    # measured in the pre-gate domain: the gate multiplies the float32 result before the one rounding
+    excess = np.maximum(np.abs(o - want) - half_ulp(o, "bf16"), 0.0) / sg
+    worst = max(float(excess[b, h].max()) / float(np.sqrt(np.mean(o_pre[b, h] ** 2)))
+                for b in range(B) for h in range(H))
+    assert worst <= TOL["bf16"], f"gated: {worst:.3e}"
+    assert_close(kv, kv_ref, "bf16", "KV gated")
+
+
+def test_one_round_deterministic(device):
+    a = run(2, 64, 1000, 64, device)
+    b = run(2, 64, 1000, 64, device)
+    assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+
+
+def test_one_round_of_wide_slices(device):
+    B, H, N = 3, 32, 1500  # 96 pairs: 192 workgroups of 64 columns, no chunks
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, B, H, N, 128) == N
+    exact, slopes, o, kv, _ = run(B, H, N, 65, device)
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes)
+    assert_close(o, o_ref, "bf16", "O one round", stored="bf16")
+    assert_close(kv, kv_ref, "bf16", "KV one round")
+
+
+@pytest.mark.parametrize("H,N", [(8, 5000), (16, 4097)])
+def test_wide_slices_with_summaries(device, H, N):
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, H, N, 128) < N
+    rng = np.random.default_rng(9)
+    kv_in = (rng.standard_normal((1, H, 128, 128)) * 0.5).astype(np.float32)
+    exact, slopes, o, kv, _ = run(1, H, N, 66, device, kv_in=kv_in)
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes, kv_in=kv_in)
+    assert_close(o, o_ref, "bf16", f"O summaries ({H}x{N})", stored="bf16")
+    assert_close(kv, kv_ref, "bf16", f"KV summaries ({H}x{N})")
