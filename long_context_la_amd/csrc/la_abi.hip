@@ -464,7 +464,7 @@ size_t varlen_workspace_bytes(const VarPlan& p, int64_t heads, int64_t d)
 }
 
 la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
-                           int64_t chunk_override, VarPlan& p)
+                           int64_t chunk_override, VarPlan& p, int slice_w = kSliceW)
 {
     if (n_seq < 1 || n_seq > (int64_t(1) << 24)) return fail(LA_ERR_INVALID_ARGUMENT, "n_seq must be in [1, 2^24]");
     if (!cu) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens must not be NULL");
@@ -480,7 +480,7 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
     if (st != LA_OK) return st;
     if (chunk_override < 0 || (chunk_override > 0 && chunk_override % kBlock != 0))
         return fail(LA_ERR_INVALID_ARGUMENT, "chunk_tokens must be 0 or a positive multiple of 64");
-    p.slices = (int)(d / kSliceW);
+    p.slices = (int)(d / slice_w);
     const int64_t total = cu[n_seq];
     int64_t chunk = longest;
     if (chunk_override > 0) {
@@ -525,6 +525,30 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
     p.tab.insert(p.tab.end(), stab.begin(), stab.end());
     p.tab.insert(p.tab.end(), rtab.begin(), rtab.end());
     return LA_OK;
+}
+
+// Value columns per workgroup of a packed prefill (see fwd_slice_w): 64 when the 32-column plan
+// chunks, or when the 32-column work spread over the GPU (the tiles of every (chunk, head,
+// slice) over kTargetGroups workgroup slots) exceeds 1.55x the longest sequence's tile chain --
+// 1.55 being the measured time per tile of a 64-column workgroup against a 32-column one, so
+// that the longer chains of the 64-column plan stay off the critical path.  Arguments as for
+// make_varlen_plan; an invalid batch gets kSliceW (make_varlen_plan then reports it).
+int varlen_slice_w(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d, bool out, bool wide)
+{
+    if (!(dt == LA_BF16 && d == 128 && out && !wide) || !cu || n_seq < 1) return kSliceW;
+    VarPlan p32;
+    if (make_varlen_plan(dt, n_seq, cu, heads, d, 0, p32) != LA_OK) return kSliceW;
+    if (p32.chunked) return kWideSliceW;
+    int64_t tiles = 0, longest = 0;
+    for (int64_t s = 0; s < n_seq; ++s) {
+        const int64_t n = cu[s + 1] - cu[s];
+        if (n <= kShortTokens) continue;  // token by token, no tile kernel
+        const int64_t t = (n + kBlock - 1) / kBlock;
+        tiles += t;
+        longest = t > longest ? t : longest;
+    }
+    const int64_t spread = tiles * heads * (d / kSliceW);  // 32-column tiles over all workgroups
+    return 100 * spread > 155 * longest * kTargetGroups ? kWideSliceW : kSliceW;
 }
 
 // Small tables travel by value in the arguments of a one-block kernel that writes them to the
@@ -605,7 +629,8 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
                               bool wide = false)
 {
     VarPlan p;
-    la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, chunk_tokens, p);
+    la_status s = make_varlen_plan(dt, n_seq, cu, heads, d, chunk_tokens, p,
+                                   varlen_slice_w(dt, n_seq, cu, heads, d, o != nullptr, rev || wide));
     if (s != LA_OK) return s;
     if (!kv || !slopes) return fail(LA_ERR_INVALID_ARGUMENT, "kv and slopes must not be NULL");
     if (p.total_chunks == 0 && p.n_short == 0) return LA_OK;  // every sequence empty
@@ -660,7 +685,13 @@ la_status prefill_varlen_impl(la_dtype dt, const void* q, const void* k, const v
     }
     if (p.total_chunks == 0) return LA_OK;
     if (p.chunked) {
-        s = launch_status(run(kModeLocal), "chunk-summary launch");
+        // local summaries on 32-column slices whatever the main pass uses (each slice writes its
+        // columns of the d x d slots)
+        FwdArgs b = a;
+        b.slices = (int)(d / kSliceW);
+        s = launch_status(dt == LA_BF16 ? launch_fwd_bf16(b, (int)d, kModeLocal, st)
+                                        : launch_fwd_f32(b, (int)d, kModeLocal, st),
+                          "chunk-summary launch");
         if (s != LA_OK) return s;
         s = launch_status(launch_scan_varlen(a.ws, kv, slopes, a.stab, n_seq, heads, p.chunk, (int)d, st),
                           "prefix-combine launch");
@@ -727,9 +758,14 @@ size_t la_prefill_varlen_workspace_size_ex(la_dtype dt, int64_t n_seq, const int
                                            int64_t d, int64_t chunk_tokens)
 {
     try {
-        VarPlan p;
+        // the plans of both slice widths (the query does not know whether outputs are asked for)
+        VarPlan p, p64;
         if (make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, chunk_tokens, p) != LA_OK) return 0;
-        return varlen_workspace_bytes(p, heads, d);
+        const size_t a = varlen_workspace_bytes(p, heads, d);
+        const int w = varlen_slice_w(dt, n_seq, cu_seqlens, heads, d, true, false);
+        if (w == kSliceW || make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, chunk_tokens, p64, w) != LA_OK) return a;
+        const size_t b = varlen_workspace_bytes(p64, heads, d);
+        return a > b ? a : b;
     } catch (...) {
         return 0;
     }
@@ -746,7 +782,9 @@ int64_t la_prefill_varlen_chunk_tokens(la_dtype dt, int64_t n_seq, const int64_t
 {
     try {
         VarPlan p;
-        if (make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, 0, p) != LA_OK) return -1;
+        if (make_varlen_plan(dt, n_seq, cu_seqlens, heads, d, 0, p,
+                             varlen_slice_w(dt, n_seq, cu_seqlens, heads, d, true, false)) != LA_OK)
+            return -1;
         return p.chunk;
     } catch (...) {
         return -1;

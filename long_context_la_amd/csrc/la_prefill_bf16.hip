@@ -975,17 +975,17 @@ void launch_mode(const FwdArgs& a, int mode, dim3 grid, hipStream_t stream)
 }
 
 template <int D>
-void launch_d(const FwdArgs& a, int mode, hipStream_t stream)
+bool launch_d(const FwdArgs& a, int mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)xcd_grid_size(a.groups, a.slices));
     const bool gate = a.gate && mode == kModeOut, act = a.act != 0;
-    if constexpr (D == 128) {
-        // 64-column slices (two per head): the plan chose them for float16 outputs without a prologue
-        if (a.slices * 64 == D) {
-            if (gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true, false, false, D, false, 64>), grid, dim3(512), 0, stream, a);
-            else hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, false, false, D, false, 64>), grid, dim3(512), 0, stream, a);
-            return;
-        }
+    if (a.slices * 64 == D) {
+        // 64-column slices (two per head): plans choose them only for float16 outputs at d = 128
+        // without a prologue; anything else is refused rather than run on the wrong columns
+        if (D != 128 || mode != kModeOut || a.wide || a.rev || act) return false;
+        if (gate) hipLaunchKernelGGL((k_fwd_bf16<kModeOut, true, false, false, 128, false, 64>), grid, dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((k_fwd_bf16<kModeOut, false, false, false, 128, false, 64>), grid, dim3(512), 0, stream, a);
+        return true;
     }
     // the backward's passes: plain inputs, full-range operands
     if (a.rev) launch_mode<false, true, false, D, true>(a, mode, grid, stream);
@@ -994,14 +994,14 @@ void launch_d(const FwdArgs& a, int mode, hipStream_t stream)
     else if (gate) launch_mode<true, false, false, D, false>(a, mode, grid, stream);
     else if (act) launch_mode<false, false, true, D, false>(a, mode, grid, stream);
     else launch_mode<false, false, false, D, false>(a, mode, grid, stream);
+    return true;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int mode, hipStream_t stream)
 {
-    if (d == 128) launch_d<128>(a, mode, stream);
-    else launch_d<64>(a, mode, stream);
+    if (!(d == 128 ? launch_d<128>(a, mode, stream) : launch_d<64>(a, mode, stream))) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

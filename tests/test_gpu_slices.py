@@ -4,9 +4,10 @@ products, no SiLU prologue), against the fp64 oracle, with the bars of tests/com
 * one unchunked round of 64-column slices, where 32-column slices would need more than one
   round of workgroups (more than 64 (batch, head) pairs): incoming states, checkpoints inside
   and at the end of the tiles, the gate epilogue, determinism;
-* chunked plans with summaries (few heads, where the 32-column plan would cut 4 or more chunks).
-Other bf16 d = 128 tests with outputs, few (batch, head) pairs and sequences long enough for four
-or more chunks of at least 1024 tokens run these slices too.
+* chunked plans with summaries (few heads, where the 32-column plan would chunk the sequence);
+* packed batches whose work spreads well beyond one round (and chunked packed batches).
+Other bf16 d = 128 tests with outputs, few (batch, head) pairs and sequences long enough to be
+chunked (over 1024 tokens) run these slices too.
 """
 import numpy as np
 import pytest
@@ -103,3 +104,21 @@ def test_wide_slices_with_summaries(device, H, N):
     o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes, kv_in=kv_in)
     assert_close(o, o_ref, "bf16", f"O summaries ({H}x{N})", stored="bf16")
     assert_close(kv, kv_ref, "bf16", f"KV summaries ({H}x{N})")
+
+
+@pytest.mark.parametrize("head_major", [False, True])
+def test_packed_batch_on_wide_slices(device, head_major):
+    # 64 heads over many tiles: the packed plan takes 64-column slices (its 32-column work spread
+    # over the GPU exceeds 1.55x the longest tile chain), next to token-by-token and empty sequences
+    from test_gpu_varlen import run_varlen
+
+    run_varlen([1500, 700, 300, 65, 64, 9, 8, 1, 0, 2000], 64, 128, "bf16", device, head_major=head_major, seed=71)
+
+
+def test_packed_chunked_on_wide_slices(device):
+    # few heads, one long sequence: chunked (summaries on 32-column slices, main pass on 64)
+    from test_gpu_varlen import run_varlen
+
+    lengths = [6000, 2500, 40]
+    assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16, [0] + list(np.cumsum(lengths)), 3, 128) < 6000
+    run_varlen(lengths, 3, 128, "bf16", device, seed=72)
