@@ -301,7 +301,7 @@ def test_n_zero_is_noop(device):
 
 
 def test_bf16_d64_chunked_with_states(device):
-    # chunks and sub-chunk summaries through the MFMA tile kernel's sliced summary mode (d = 64)
+    # chunks and sub-chunk summaries through the full-width summary kernel at d = 64
     kv0 = np.random.default_rng(10).standard_normal((1, 2, 64, 64)).astype(np.float32)
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 2, 9000, 64) < 9000
     check_prefill(36, 1, 2, 9000, 64, "bf16", SL2, device, kv_in=kv0)
@@ -309,7 +309,7 @@ def test_bf16_d64_chunked_with_states(device):
 
 def test_bf16_chunked_batch_with_states(device):
     # two sequences of the batch, both cut into chunks and sub-chunk summaries (full-width
-    # summary kernel), each from its own incoming state
+    # summary kernel; main pass on 64-column slices), each from its own incoming state
     kv0 = np.random.default_rng(9).standard_normal((2, 2, 128, 128)).astype(np.float32)
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 2, 2, 5000, 128) < 5000
     check_prefill(28, 2, 2, 5000, 128, "bf16", SL2, device, kv_in=kv0)
