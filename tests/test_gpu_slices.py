@@ -5,7 +5,8 @@ products, no SiLU prologue), against the fp64 oracle, with the bars of tests/com
   round of workgroups (more than 64 (batch, head) pairs): incoming states, checkpoints inside
   and at the end of the tiles, the gate epilogue, determinism;
 * chunked plans with summaries (few heads, where the 32-column plan would chunk the sequence);
-* packed batches whose work spreads well beyond one round (and chunked packed batches).
+* packed batches whose work spreads well beyond one round (and chunked packed batches);
+* the same plan shapes at d = 64, which keeps 32-column slices.
 Other bf16 d = 128 tests with outputs, few (batch, head) pairs and sequences long enough to be
 chunked (over 1024 tokens) run these slices too.
 """
@@ -24,17 +25,17 @@ def layer_slopes(H):
     return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
 
 
-def run(B, H, N, seed, device, kv_in=None, ckpt_every=0, gate=None):
+def run(B, H, N, seed, device, kv_in=None, ckpt_every=0, gate=None, d=128):
     import torch
 
-    exact, raw = inputs(seed, B, H, N, 128, "bf16")
+    exact, raw = inputs(seed, B, H, N, d, "bf16")
     q, k, v = (to_device(x, "bf16", device) for x in raw)
     slopes = layer_slopes(H)
     ts = torch.from_numpy(slopes).to(device)
-    kv = (torch.zeros(B, H, 128, 128, dtype=torch.float32, device=device) if kv_in is None
+    kv = (torch.zeros(B, H, d, d, dtype=torch.float32, device=device) if kv_in is None
           else torch.from_numpy(np.ascontiguousarray(kv_in, np.float32)).to(device))
     o = torch.empty_like(q)
-    ck = (torch.full((B, H, N // ckpt_every, 128, 128), float("nan"), dtype=torch.float32, device=device)
+    ck = (torch.full((B, H, N // ckpt_every, d, d), float("nan"), dtype=torch.float32, device=device)
           if ckpt_every else None)
     if gate is None:
         la.la_prefill(q, k, v, ts, kv, o=o, ckpt=ck, ckpt_every=ckpt_every)
@@ -122,3 +123,42 @@ def test_packed_chunked_on_wide_slices(device):
     lengths = [6000, 2500, 40]
     assert la.la_prefill_varlen_chunk_tokens(la.LA_BF16, [0] + list(np.cumsum(lengths)), 3, 128) < 6000
     run_varlen(lengths, 3, 128, "bf16", device, seed=72)
+
+
+# d = 64 keeps 32-column slices (two per head) in every plan; the same shapes as above
+
+
+def test_d64_two_rounds_checkpoints_and_gate(device):
+    B, H, N, d = 3, 48, 700, 64  # 144 pairs: 288 workgroups of 32 columns, more than one round
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, B, H, N, d) == N
+    rng = np.random.default_rng(11)
+    kv_in = (rng.standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    exact, slopes, o, kv, ck = run(B, H, N, 81, device, kv_in=kv_in, ckpt_every=128, d=d)
+    o_ref, kv_ref, ck_ref = oracle.recurrent(*exact, slopes, kv_in=kv_in, ckpt_every=128)
+    assert_close(o, o_ref, "bf16", "O d=64 one round", stored="bf16")
+    assert_close(kv, kv_ref, "bf16", "KV d=64 one round")
+    assert not np.isnan(ck).any()
+    assert_close(ck.reshape(-1, *ck.shape[2:])[:, None], ck_ref.reshape(-1, *ck_ref.shape[2:])[:, None], "bf16",
+                 "checkpoints d=64")
+    import synth
+
+    g = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((rng.standard_normal((B, H, N, d)) * 2.0).astype(np.float32)))
+    exact, slopes, o, kv, _ = run(B, H, N, 82, device, gate=g, d=d)
+    o_pre, kv_ref, _ = oracle.recurrent(*exact, slopes)
+    sg = oracle.sigmoid(g.astype(np.float64))
+    excess = np.maximum(np.abs(o - o_pre * sg) - half_ulp(o, "bf16"), 0.0) / sg
+    worst = max(float(excess[b, h].max()) / float(np.sqrt(np.mean(o_pre[b, h] ** 2)))
+                for b in range(B) for h in range(H))
+    assert worst <= TOL["bf16"], f"gated d=64: {worst:.3e}"
+    assert_close(kv, kv_ref, "bf16", "KV gated d=64")
+
+
+@pytest.mark.parametrize("H,N", [(64, 3000), (2, 9000)])
+def test_d64_chunked(device, H, N):
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, H, N, 64) < N
+    rng = np.random.default_rng(12)
+    kv_in = (rng.standard_normal((1, H, 64, 64)) * 0.5).astype(np.float32)
+    exact, slopes, o, kv, _ = run(1, H, N, 83, device, kv_in=kv_in, d=64)
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes, kv_in=kv_in)
+    assert_close(o, o_ref, "bf16", f"O d=64 chunked ({H}x{N})", stored="bf16")
+    assert_close(kv, kv_ref, "bf16", f"KV d=64 chunked ({H}x{N})")
