@@ -464,7 +464,7 @@ size_t varlen_workspace_bytes(const VarPlan& p, int64_t heads, int64_t d)
 }
 
 la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_t heads, int64_t d,
-                           int64_t chunk_override, VarPlan& p, int slice_w = kSliceW)
+                           int64_t chunk_override, VarPlan& p, int slice_w = kSliceW, bool tables = true)
 {
     if (n_seq < 1 || n_seq > (int64_t(1) << 24)) return fail(LA_ERR_INVALID_ARGUMENT, "n_seq must be in [1, 2^24]");
     if (!cu) return fail(LA_ERR_INVALID_ARGUMENT, "cu_seqlens must not be NULL");
@@ -501,6 +501,19 @@ la_status make_varlen_plan(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_
     if (n_tiled_chunks * heads > kMaxUnits)
         return fail(LA_ERR_UNSUPPORTED, "more than 2^20 (chunk, head) work items: use a larger chunk_tokens");
     p.tab.clear();
+    if (!tables) {  // the plan's shape only: chunk counts, no tables
+        for (int64_t s = 0; s < n_seq; ++s) {
+            const int64_t n = cu[s + 1] - cu[s];
+            if (n >= 1 && n <= kShortTokens) {
+                ++p.n_short;
+                continue;
+            }
+            const int64_t nc = n == 0 ? 0 : (n <= p.chunk ? 1 : (n + p.chunk - 1) / p.chunk);
+            p.total_chunks += nc;
+            if (nc > 1) p.chunked = true;
+        }
+        return LA_OK;
+    }
     std::vector<int64_t> stab((size_t)(2 * n_seq)), rtab;
     for (int64_t s = 0; s < n_seq; ++s) {
         const int64_t n = cu[s + 1] - cu[s];
@@ -537,7 +550,7 @@ int varlen_slice_w(la_dtype dt, int64_t n_seq, const int64_t* cu, int64_t heads,
 {
     if (!(dt == LA_BF16 && d == 128 && out && !wide) || !cu || n_seq < 1) return kSliceW;
     VarPlan p32;
-    if (make_varlen_plan(dt, n_seq, cu, heads, d, 0, p32) != LA_OK) return kSliceW;
+    if (make_varlen_plan(dt, n_seq, cu, heads, d, 0, p32, kSliceW, false) != LA_OK) return kSliceW;
     if (p32.chunked) return kWideSliceW;
     int64_t tiles = 0, longest = 0;
     for (int64_t s = 0; s < n_seq; ++s) {
