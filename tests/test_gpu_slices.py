@@ -162,4 +162,3 @@ def test_d64_chunked(device, H, N):
     o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes, kv_in=kv_in)
     assert_close(o, o_ref, "bf16", f"O d=64 chunked ({H}x{N})", stored="bf16")
     assert_close(kv, kv_ref, "bf16", f"KV d=64 chunked ({H}x{N})")
-
