@@ -25,6 +25,7 @@ constexpr int kShortTokens = 8;  // packed sequences this short run token by tok
 // at both.
 constexpr int kLocalTargetGroups = LA_LOCAL_TARGET_GROUPS;
 constexpr int kMinSubChunk = 256;  // shortest sub-chunk worth a 64 KiB summary
+constexpr int kLongSubChunk = 8192;  // sub-chunks this long may be split up to twice the target
 
 // How a prefill is split: value-column slices x sequence chunks per (batch, head).
 struct Plan {
@@ -96,6 +97,9 @@ struct FwdArgs {
     // Full-range products for the outputs (bf16 hi + lo operands instead of float16): the
     // backward's passes, whose gradient inputs can lie far below float16's normal range.
     int wide;
+    // Full-width chunk summaries of sub-chunks: tokens per chunk of the plan (the fold weighs a
+    // sub-chunk's state by the decay to its chunk's end), or 0 when the launch's chunks are whole.
+    int64_t span;
 };
 
 // SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), in float32.

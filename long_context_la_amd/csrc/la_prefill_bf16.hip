@@ -792,7 +792,8 @@ __global__ __launch_bounds__(MODE == kModeOut ? 512 : 256, 1) void k_fwd_bf16(Fw
 // prefills and the backward) bf16 K and W V as a bf16 hi + lo pair, over float32's range.  Eight
 // waves split the (D/16)^2 state tiles of 16 x 16 into 8 / (D/32) key-row groups x D/32
 // value-column groups: 2 x 4 groups of 4 x 2 tiles at d = 128, 4 x 2 groups of 1 x 2 tiles at
-// d = 64.  No SiLU prologue (the fused path keeps the sliced summaries).
+// d = 64.  No SiLU prologue (the fused path keeps the sliced summaries).  Forward summaries skip
+// the tokens whose weight at their chunk's end is too small to reach float32 (see tile0 below).
 template <int D> struct SumRegs { uint4 k[D / 64]; uint4 v[D / 64]; };  // 16-byte chunks tid + 512m of K and V
 
 template <bool REV, bool F16, int D>
@@ -815,6 +816,25 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     if (wk.j == wk.nck - 1) return;  // a sequence's last (sub-)chunk needs no summary
     const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int n_tiles = (int)((t_end - t_begin + BK - 1) / BK);
+    // Tokens too far before their chunk's end to matter.  A token t of a chunk ending at e enters
+    // the chunk's state with weight lambda^(e-1-t), and every element of a local state is bounded
+    // by M = max|k v| / (1 - lambda) <= max|k v| (1 + 1/s).  So the tokens before e - W with
+    // lambda^W M < 2^-150, i.e. s W >= ln(max|k v|) + 150 ln 2 + ln(1 + 1/s), change the chunk's
+    // state by less than the smallest float32 denormal, and a float32 result cannot depend on them:
+    // the sub-chunk starts its tiles at the first one that holds a token from e - W on (all of
+    // them with no decay).  max|k v| < 65504^2 with float16 operands (the range their prefill
+    // requires), else bf16's largest value squared; ln 2 of margin each.
+    int tile0 = 0;
+    if (!REV && a.span > 0) {
+        const double sl = (double)a.slopes[wk.h];
+        const double c = F16 ? 2.0 * 11.09 + 151.0 * 0.6931471805599453 : 2.0 * 88.72 + 151.0 * 0.6931471805599453;
+        if (sl > 0.0 && sl < 1e30) {
+            const double win = (c + log1p(1.0 / sl)) / sl;
+            const int64_t e = ((t_begin / a.span) + 1) * a.span;
+            const double first = (double)(e - t_begin) - win;  // tokens of the sub-chunk before e - W
+            if (first > 0.0) tile0 = first >= (double)n_tiles * BK ? n_tiles : (int)(first / BK);
+        }
+    }
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, g = l >> 4;
@@ -932,11 +952,11 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
         }
     };
     SR RA, RB;
-    load(RA, 0);
+    load(RA, tile0);
     __builtin_amdgcn_sched_barrier(0);
-    load(RB, 1);
+    load(RB, tile0 + 1);
     __builtin_amdgcn_sched_barrier(0);
-    stage(RA, 0, 0);
+    if (tile0 < n_tiles) stage(RA, 0, tile0);
     __syncthreads();
     auto step = [&](SR& R, SR& Rn, int buf, int tile) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
@@ -945,7 +965,7 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
         update(buf, tile);
         if (tile + 1 < n_tiles) stage(Rn, buf ^ 1, tile + 1);
     };
-    int tile = 0;
+    int tile = tile0;
     for (; tile + 2 <= n_tiles; tile += 2) {
         step(RA, RB, 0, tile);
         __syncthreads();

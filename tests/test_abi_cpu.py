@@ -116,9 +116,11 @@ def test_plan_and_workspace_sizes():
     # 64 columns: prefix slots (16 per head) + summary slots: 15 chunks x 2 sub-chunks + 1, so that the
     # summary pass has 8 x 30 = 240 >= 128 full-width workgroups; 32 columns: 8 + 1 + 7 x 4
     assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * (16 + 1 + 15 * 2) * 128 * 128 * 4
+    # 1M tokens: 16 chunks of 65536; their sub-chunks go finer (the summaries skip decayed tokens):
+    # 15 x 4 sub-chunks of 16384, 8 x 60 = 480 summary workgroups
     c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 1048576, 128)
     assert c == 65536
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (16 + 1 + 15 * 2) * 128 * 128 * 4
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (16 + 1 + 15 * 4) * 128 * 128 * 4
     # float32 keeps 32-column slices (4 per head at d = 128), and so does d = 64 (2 per head)
     assert la.la_prefill_chunk_tokens(la.LA_F32, 1, 8, 32768, 128) == 4096
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 32768, 64) == 2048

@@ -162,3 +162,35 @@ def test_d64_chunked(device, H, N):
     o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes, kv_in=kv_in)
     assert_close(o, o_ref, "bf16", f"O d=64 chunked ({H}x{N})", stored="bf16")
     assert_close(kv, kv_ref, "bf16", f"KV d=64 chunked ({H}x{N})")
+
+
+# Chunk summaries skip the tokens whose weight at their chunk's end, times the largest state the
+# float16 input range allows, is below the smallest float32 denormal (fast-decaying heads skip most
+# of every chunk).  The results must not change; the second case puts large values only in the
+# skipped tokens and small ones after them.
+
+
+@pytest.mark.parametrize("boost", [False, True])
+def test_summaries_skip_decayed_tokens(device, boost):
+    import torch
+
+    B, H, N, d = 1, 4, 40000, 128
+    slopes = np.array([0.5, 0.05, 2.0 ** -6, 2.0 ** -9], dtype=np.float32)
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, B, H, N, d) < N
+    exact, raw = inputs(67, B, H, N, d, "bf16")
+    if boost:
+        # the first half of each 1024-token block scaled by 8, the rest by 1/8 (exact in bf16, and
+        # within the float16 products' range)
+        scale = np.where((np.arange(N) % 1024) < 512, 8.0, 1.0 / 8.0).astype(np.float32)[None, None, :, None]
+        exact = [x * scale for x in exact]
+        import synth
+
+        raw = [synth.f32_to_bf16_bits(x) for x in exact]
+    q, k, v = (to_device(x, "bf16", device) for x in raw)
+    kv = torch.zeros(B, H, d, d, device=device)
+    o = torch.empty_like(q)
+    la.la_prefill(q, k, v, torch.from_numpy(slopes).to(device), kv, o=o)
+    torch.cuda.synchronize()
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes)
+    assert_close(to_host(o), o_ref, "bf16", f"O skipped summaries (boost={boost})", stored="bf16")
+    assert_close(kv.cpu().numpy(), kv_ref, "bf16", f"KV skipped summaries (boost={boost})")
