@@ -179,9 +179,9 @@ la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, v
  * graph capture, tight serving loops, harnesses that forbid allocation): no
  * workspace argument.  The chunk states live in a device array inside the
  * library of LA_NOALLOC_SCRATCH_BYTES (48 MiB), one per GPU, held until the
- * process ends; every shape the default plan chunks fits (its chunk and
- * sub-chunk counts keep the states under 48 MiB; one (batch, head) pair of
- * 4M tokens at d = 128 needs 41.7 MB), and a shape needing more returns
+ * process ends; every shape the default plan chunks fits (the plan keeps its
+ * chunk and sub-chunk states within 48 MiB; 26 heads of 262144 tokens at
+ * d = 128 need 47.1 MiB), and a shape needing more returns
  * LA_ERR_UNSUPPORTED.  The call allocates nothing and frees nothing.
  * All calls on one GPU share that array: calls that overlap on one GPU (on
  * different streams, or from different threads without ordering) race and

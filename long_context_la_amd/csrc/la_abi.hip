@@ -72,12 +72,18 @@ Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk
         while (local_groups * p.sub < target && p.chunk % (2 * p.sub * kBlock) == 0 &&
                p.chunk / (2 * p.sub) >= kMinSubChunk)
             p.sub *= 2;
-        // Long sub-chunks go finer, up to twice the target: the summary kernel skips the tokens too
-        // far before their chunk's end to matter, so the pass takes as long as the longest window a
-        // sub-chunk must still cover (measured on 8 heads x 1M tokens: 2.23 -> 2.01 ms; the 64-head
-        // d = 64 layer: 1.094 -> 1.028 ms; short sub-chunks, as at 8 heads x 32K, lose by it).
-        while (local_groups * p.sub < 2 * target && p.chunk % (2 * p.sub * kBlock) == 0 &&
-               p.chunk / (2 * p.sub) >= kLongSubChunk)
+        // Long sub-chunks go finer, up to four times the target (two summary workgroups fit one CU)
+        // while the chunk states stay within the allocation-free entry point's array: the summary
+        // kernel skips the tokens too far before their chunk's end to matter, so the pass takes as
+        // long as the longest window a sub-chunk must still cover (measured on 8 heads x 1M tokens:
+        // 2.23 -> 2.01 ms; the 64-head d = 64 layer: 1.094 -> 1.028 ms; short sub-chunks, as at 8
+        // heads x 32K, lose by it).
+        auto state_bytes_at = [&](int64_t sub) {
+            return (size_t)(batch * heads * (p.n_chunks + 1 + (p.n_chunks - 1) * sub)) * (size_t)(d * d) *
+                   sizeof(float);
+        };
+        while (local_groups * p.sub < 4 * target && p.chunk % (2 * p.sub * kBlock) == 0 &&
+               p.chunk / (2 * p.sub) >= kLongSubChunk && state_bytes_at(2 * p.sub) <= LA_NOALLOC_SCRATCH_BYTES)
             p.sub *= 2;
     }
     return p;

@@ -38,19 +38,22 @@ struct Plan {
 Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk_override,
                int slice_w = kSliceW);
 constexpr int kWideSliceW = 64;  // value columns per workgroup of the wide-slice plans
+constexpr int64_t kWideMinTokens = 65536;  // sequences this long take the wide slices in any case
 // Value columns per workgroup of a forward prefill.  bf16 at d = 128 with float16 outputs and no
 // SiLU prologue has a 64-column instantiation, whose workgroups take 1.55x the time per tile of
 // the 32-column ones for twice the columns (the score products and the Q and K conversions serve
 // twice the columns).  It pays where the work is split anyway: when the 32-column plan chunks the
 // sequence (the wide plan's summaries then cover a few more tokens: 3/4 instead of 1/2 of them,
 // 15/16 instead of 7/8), or needs more than one round of workgroups.  Where 32-column slices fill
-// the GPU once without chunks (64 (batch, head) pairs), the wide plan would add a summary pass
-// over half the tokens, and short sequences are latency-bound tile chains.
+// the GPU once without chunks (33 to 64 (batch, head) pairs), the wide plan adds a summary pass
+// over about half the tokens; from kWideMinTokens on it still pays (64 heads x 131072 tokens:
+// 2.19 -> 2.00 ms; the summaries skip the tokens whose decay cannot reach float32, and with no
+// decay to skip it measured 2.145 ms), while shorter sequences keep the 32-column tile chains.
 inline int fwd_slice_w(la_dtype dt, int64_t batch, int64_t heads, int64_t n, int64_t d, bool out, bool wide,
                        uint32_t act)
 {
     if (!(dt == LA_BF16 && d == 128 && out && !wide && act == 0)) return kSliceW;
-    if (batch * heads * (d / kSliceW) > kTargetGroups) return kWideSliceW;
+    if (batch * heads * (d / kSliceW) > kTargetGroups || n >= kWideMinTokens) return kWideSliceW;
     return make_plan(batch, heads, n, d, 0, kSliceW).n_chunks > 1 ? kWideSliceW : kSliceW;
 }
 

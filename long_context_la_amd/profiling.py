@@ -238,11 +238,13 @@ def mfma_utilisation(pmc_csv, pattern, simds, xcds, tiles_per_simd=None, workgro
 BENCH = "python3 {root}/bench.py"
 ONLY_FULL = "--no-cpu-baseline --no-decode --no-backward --no-varlen --no-other-workloads"
 # The prefill kernel with outputs, no gate, forward walk, no SiLU prologue, d = 128, float16
-# operands (k_fwd_bf16<MODE, GATE, REV, ACT, D, WIDE, value columns per workgroup>): 32-column
-# slices for the full layer (64 heads fill the GPU unchunked), 64-column slices for the chunked
-# share and long-context prefills.
-MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false, 32>"
-WIDE_MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false, 64>"
+# operands (k_fwd_bf16<MODE, GATE, REV, ACT, D, WIDE, value columns per workgroup>): every profiled
+# prefill (full layer, share, long context) runs 64-column slices in chunks, after the chunk
+# summaries and their prefix combine.
+MAIN_KERNEL = r"k_fwd_bf16<0, false, false, false, 128, false, 64>"
+WIDE_MAIN_KERNEL = MAIN_KERNEL
+CHUNK_KERNELS = (("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
+                 ("prefix combine (k_scan_sub)", r"k_scan_sub", None))
 
 RUNS = {
     # name: (rocprofv3 arguments, bench arguments)
@@ -292,7 +294,10 @@ def _header(title, names, out_root):
     return lines
 
 
-def summarize_stats(out_root, name, title, last_of=None):
+def summarize_stats(out_root, name, title, last_of=None, also=()):
+    """Kernel table of a trace.  last_of = (pattern, workgroups, n): the average of the last n
+    dispatches of that kernel (the timed steps); also = ((label, pattern), ...): the prefill's other
+    launches, whose last-n averages are added into a per-step total."""
     rows = dispatches(_csv(out_root, name, "kernel_trace"))
     lines = _header(title, [name], out_root)
     lines.append(f"# kernel code digest (sha256[:16] of la_prefill_bf16.hip without comments): {source_digest()}")
@@ -301,8 +306,19 @@ def summarize_stats(out_root, name, title, last_of=None):
         pattern, wg, n = last_of
         sel = select(rows, pattern, wg)[-n:]
         if sel:
+            main = statistics.fmean(d['us'] for d in sel)
             lines.append(f"# Last {len(sel)} dispatches of {sel[0]['short']} with {wg} workgroups (the timed steps): "
-                         f"average {statistics.fmean(d['us'] for d in sel):.1f} us")
+                         f"average {main:.1f} us")
+            parts, total = [], main
+            for label, pat in also:
+                other = select(rows, pat, None)[-n:]
+                if other:
+                    avg = statistics.fmean(d['us'] for d in other)
+                    parts.append(f"{label} {avg:.1f} us")
+                    total += avg
+            if parts:
+                lines.append(f"# The prefill's launches per timed step (last {n} of each): main {main:.1f} us + "
+                             + " + ".join(parts) + f" = {total:.1f} us")
     lines.append(format_table(kernel_table(rows)))
     return "\n".join(lines) + "\n"
 
@@ -394,7 +410,7 @@ def summarize_all(out_root, profiles_dir=PROFILES):
         "kernel_stats_prefill_full_64x131072.txt": lambda: summarize_stats(
             out_root, "stats_full", "kernel statistics of the full-layer prefill (1 x 64 heads x 131072 tokens, d=128, "
             "bf16): settling, 1 warm-up, 5 timed steps and 5 per-kernel timings",
-            (MAIN_KERNEL, 256, 5)),
+            (MAIN_KERNEL, 256, 5), also=tuple((label.split(" (")[0], pat) for label, pat, _ in CHUNK_KERNELS)),
         "kernel_stats_bench_all_legs.txt": lambda: summarize_stats(
             out_root, "stats_all", "kernel statistics of bench.py: full-layer prefill (1 x 64 heads x 131072 tokens, "
             "d=128, bf16), backward, packed and mixed legs, decode (128 x 64 units, 100 steps)"),
@@ -404,18 +420,16 @@ def summarize_all(out_root, profiles_dir=PROFILES):
             out_root, "stats_long", "kernel statistics of the chunked long-context prefill (1 x 8 heads x 1048576, "
             "d=128, checkpoints every 65536)"),
         "prefill_full_hbm_traffic.txt": lambda: summarize_traffic(
-            out_root, "full", MAIN_KERNEL, full_bytes, 256),
+            out_root, "full", MAIN_KERNEL, full_bytes, 256, extra_kernels=CHUNK_KERNELS),
         "prefill_share_hbm_traffic.txt": lambda: summarize_traffic(
             out_root, "share", WIDE_MAIN_KERNEL, eight_heads(32768), 256,
-            extra_kernels=(("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
-                           ("prefix combine (k_scan_sub)", r"k_scan_sub", None))),
+            extra_kernels=CHUNK_KERNELS),
         "prefill_long_hbm_traffic.txt": lambda: summarize_traffic(
             out_root, "long", WIDE_MAIN_KERNEL, eight_heads(1 << 20), 256,
-            extra_kernels=(("chunk summaries (k_summary_bf16)", r"k_summary_bf16", None),
-                           ("prefix combine (k_scan_sub)", r"k_scan_sub", None))),
+            extra_kernels=CHUNK_KERNELS),
         "decode_128x64_hbm_traffic.txt": lambda: summarize_traffic(
             out_root, "decode", r"k_decode", 8192 * (2 * 128 * 128 * 4 + 4 * 128 * 2), 8192),
-        "prefill_full_mfma_util.txt": lambda: summarize_mfma(out_root, 2048, MAIN_KERNEL,
+        "prefill_full_mfma_util.txt": lambda: summarize_mfma(out_root, 1024, MAIN_KERNEL,
                                                              256),
     }
     written = []

@@ -102,9 +102,16 @@ def test_decode_and_state_init_validation():
 
 
 def test_plan_and_workspace_sizes():
-    # 64 heads x 4 value slices of 32 columns fill the GPU: one chunk, no workspace
-    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 64, 131072, 128) == 131072
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 0
+    # 64 heads x 131072 tokens: 64-column slices in two chunks (64 x 2 x 2 = 256 workgroups); the
+    # summaries of chunk 0 in 8 sub-chunks of 8192 tokens: 2 prefix + 1 + 8 summary slots per head
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 64, 131072, 128) == 65536
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 64 * (2 + 1 + 8) * 128 * 128 * 4
+    # every default plan's chunk states fit the allocation-free entry point's array
+    assert max(la.la_prefill_workspace_size(la.LA_BF16, 1, h, n, 128) for h in (1, 8, 26, 64)
+               for n in (65536, 262144, 1 << 20, 1 << 22)) <= la.LA_NOALLOC_SCRATCH_BYTES
+    # shorter: 32-column slices fill the GPU once, unchunked
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 64, 32768, 128) == 32768
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 32768, 128) == 0
     # 2 x 64 heads: one round of 256 workgroups of 64 columns, no chunks
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 2, 64, 131072, 128) == 131072
     assert la.la_prefill_workspace_size(la.LA_BF16, 2, 64, 131072, 128) == 0
@@ -287,3 +294,12 @@ def test_binding_stride_match_ignores_size_one_dims():
     assert q.stride() != o.stride()
     assert la._same_strides(o, q) and la._same_strides(q, o)
     assert not la._same_strides(torch.empty(3, 2, 128).permute(1, 0, 2), torch.empty(2, 3, 128))
+
+
+def test_noalloc_array_size_matches_the_header():
+    import os
+    import re
+
+    h = open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "..", "include", "la.h")).read()
+    m = re.search(r"#define LA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", h)
+    assert m and int(m.group(1)) << 20 == la.LA_NOALLOC_SCRATCH_BYTES

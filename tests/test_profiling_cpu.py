@@ -9,12 +9,12 @@ import pytest
 from long_context_la_amd import profiling
 
 FIX = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rocprof")
-FWD = r"k_fwd_bf16<0, false, false, false, 128, false, 32>"
+FWD = r"k_fwd_bf16<0, false, false, false, 128, false, 64>"
 
 
 def test_short_names():
-    assert profiling.short_name("void la::(anonymous namespace)::k_fwd_bf16<0, false, false, false, 128, false, 32>"
-                                "(la::FwdArgs)") == "k_fwd_bf16<0, false, false, false, 128, false, 32>"
+    assert profiling.short_name("void la::(anonymous namespace)::k_fwd_bf16<0, false, false, false, 128, false, 64>"
+                                "(la::FwdArgs)") == "k_fwd_bf16<0, false, false, false, 128, false, 64>"
     assert profiling.short_name("la::(anonymous namespace)::k_state_init(float*, float const*, long)") == \
         "k_state_init"
     assert profiling.short_name("_ZN2la12_GLOBAL__N_18k_decodeIDF16bLi128ELb0EEEvPKT_S4_S4_PS2_PKfPflNS0_2FuE") == \
@@ -27,7 +27,7 @@ def test_kernel_trace_table():
     fwd = profiling.select(rows, FWD, 256)
     assert [round(d["us"]) for d in fwd] == [2000 + 50 * j for j in range(12)]
     table = {(t["kernel"], t["workgroups"]): t for t in profiling.kernel_table(rows)}
-    t = table[("k_fwd_bf16<0, false, false, false, 128, false, 32>", 256)]
+    t = table[("k_fwd_bf16<0, false, false, false, 128, false, 64>", 256)]
     assert t["calls"] == 12 and t["min_us"] == pytest.approx(2000) and t["max_us"] == pytest.approx(2550)
     assert t["avg_us"] == pytest.approx(2275) and t["median_us"] == pytest.approx(2275)
     assert table[("k_state_init", 256)]["calls"] == 12
