@@ -303,3 +303,21 @@ def test_noalloc_array_size_matches_the_header():
     h = open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "..", "include", "la.h")).read()
     m = re.search(r"#define LA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", h)
     assert m and int(m.group(1)) << 20 == la.LA_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.skipif(gpu_available(), reason="relies on the device check coming after the workspace check")
+def test_workspace_query_covers_every_plan():
+    # with exactly the queried bytes no prefill fails its workspace check, with or without outputs,
+    # whichever slice width and chunking the call takes; one byte less fails for plans that chunk
+    for dt, d in ((la.LA_BF16, 128), (la.LA_BF16, 64), (la.LA_F32, 128)):
+        for B, H in ((1, 1), (1, 8), (1, 26), (2, 32), (1, 48), (1, 64), (2, 64), (3, 48)):
+            for N in (1000, 1025, 5000, 40000, 65536, 131072, 1 << 20):
+                need = la.la_prefill_workspace_size(dt, B, H, N, d)
+                sh, sb = N * d, H * N * d
+                for o in (FAKE, None):
+                    r = _prefill(dt=dt, B=B, H=H, N=N, d=d, sh=sh, sb=sb, sn=d, o=o,
+                                 ws=FAKE if need else None, ws_bytes=need)
+                    assert r == la.LA_ERR_DEVICE, (dt, B, H, N, d, o is None, need, la.la_status_string(r))
+                if need and la.la_prefill_chunk_tokens(dt, B, H, N, d) < N:
+                    r = _prefill(dt=dt, B=B, H=H, N=N, d=d, sh=sh, sb=sb, sn=d, ws=FAKE, ws_bytes=need - 1)
+                    assert r == la.LA_ERR_WORKSPACE, (dt, B, H, N, d)
