@@ -103,3 +103,42 @@ def test_noalloc_through_the_binding(device):
         out[name] = (o.cpu(), kv.cpu(), ck.cpu())
     for x, y in zip(out["noalloc"], out["workspace"]):
         assert torch.equal(x, y)
+
+
+def test_noalloc_at_the_layer_shape(device):
+    """The 64-head layer (1 x 64 x 131072, d = 128), whose plan fills most of the array (two chunks
+    of 64-column slices, eight summary sub-chunks: 44 MiB), against la_prefill with a caller
+    workspace bit for bit, then a smaller call through the same array; the oracle checks windows of
+    the layer in tests/test_gpu_workloads.py."""
+    import torch
+
+    import bench
+    import synth
+
+    w = synth.WORKLOADS["full"]
+    need = la.la_prefill_workspace_size(la.LA_BF16, w.batch, w.heads, w.n, w.d)
+    assert 32 << 20 < need <= la.LA_NOALLOC_SCRATCH_BYTES
+    q, k, v = bench.make_prefill_inputs(w, device)
+    sl = torch.from_numpy(w.slopes()).to(device)
+    out = {}
+    for entry in ("noalloc", "workspace"):
+        kv = torch.zeros(w.batch, w.heads, w.d, w.d, device=device)
+        o = torch.empty_like(q)
+        ws = torch.empty(need, dtype=torch.uint8, device=device) if entry == "workspace" else None
+        _call(entry, q, k, v, o, sl, kv, ws=ws)
+        torch.cuda.synchronize()
+        out[entry] = (o, kv)
+    assert torch.equal(out["noalloc"][0], out["workspace"][0]) and torch.equal(out["noalloc"][1], out["workspace"][1])
+    del out, q, k, v
+    torch.cuda.empty_cache()
+    # a smaller chunked call after it, through the same array
+    B, H, N, d = 1, 2, 9000, 128
+    exact, raw = inputs(76, B, H, N, d, "bf16")
+    q, k, v = (to_device(x, "bf16", device) for x in raw)
+    kv = torch.zeros(B, H, d, d, device=device)
+    o = torch.empty_like(q)
+    _call("noalloc", q, k, v, o, torch.from_numpy(SL2).to(device), kv)
+    torch.cuda.synchronize()
+    o_ref, kv_ref, _ = oracle.recurrent(*exact, SL2)
+    assert_close(to_host(o), o_ref, "bf16", "O after the layer", stored="bf16")
+    assert_close(kv.cpu().numpy(), kv_ref, "bf16", "KV after the layer")
