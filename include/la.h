@@ -178,17 +178,16 @@ la_status la_prefill(la_dtype dt, const void* q, const void* k, const void* v, v
  * la_prefill for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation): no
  * workspace argument.  The chunk states live in a device array inside the
- * library of LA_NOALLOC_SCRATCH_BYTES (48 MiB), one per GPU, held until the
+ * library of LA_NOALLOC_SCRATCH_BYTES (96 MiB), one per GPU, held until the
  * process ends; every shape the default plan chunks fits (the plan keeps its
- * chunk and sub-chunk states within 48 MiB; 26 heads of 262144 tokens at
- * d = 128 need 47.1 MiB), and a shape needing more returns
- * LA_ERR_UNSUPPORTED.  The call allocates nothing and frees nothing.
+ * chunk and sub-chunk states within 96 MiB; 15 heads of 1M tokens at d = 128
+ * need 94.7 MiB), and a shape needing more returns LA_ERR_UNSUPPORTED.  The call allocates nothing and frees nothing.
  * All calls on one GPU share that array: calls that overlap on one GPU (on
  * different streams, or from different threads without ordering) race and
  * give wrong results; calls ordered on one stream are safe.  Arguments,
  * results and errors otherwise as la_prefill.
  */
-#define LA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 la_status la_prefill_noalloc(la_dtype dt, const void* q, const void* k, const void* v, void* o,
                              int64_t batch, int64_t heads, int64_t n, int64_t d,
                              int64_t stride_b, int64_t stride_h, int64_t stride_n,

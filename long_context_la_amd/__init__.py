@@ -34,7 +34,7 @@ LA_ERR_DEVICE = 4
 LA_ERR_INTERNAL = 5
 LA_F32 = 0
 LA_BF16 = 1
-LA_NOALLOC_SCRATCH_BYTES = 48 << 20  # include/la.h: the allocation-free prefill's per-GPU array
+LA_NOALLOC_SCRATCH_BYTES = 96 << 20  # include/la.h: the allocation-free prefill's per-GPU array
 
 EXPORTED = ["la_state_init", "la_prefill_chunk_tokens", "la_prefill_workspace_size",
             "la_prefill_workspace_size_ex", "la_prefill", "la_prefill_ex",

@@ -82,7 +82,7 @@ Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk
             return (size_t)(batch * heads * (p.n_chunks + 1 + (p.n_chunks - 1) * sub)) * (size_t)(d * d) *
                    sizeof(float);
         };
-        while (local_groups * p.sub < 4 * target && p.chunk % (2 * p.sub * kBlock) == 0 &&
+        while (local_groups * p.sub < 8 * target && p.chunk % (2 * p.sub * kBlock) == 0 &&
                p.chunk / (2 * p.sub) >= kLongSubChunk && state_bytes_at(2 * p.sub) <= LA_NOALLOC_SCRATCH_BYTES)
             p.sub *= 2;
     }

@@ -25,7 +25,7 @@ constexpr int kShortTokens = 8;  // packed sequences this short run token by tok
 // at both.
 constexpr int kLocalTargetGroups = LA_LOCAL_TARGET_GROUPS;
 constexpr int kMinSubChunk = 256;  // shortest sub-chunk worth a 64 KiB summary
-constexpr int kLongSubChunk = 8192;  // sub-chunks this long may be split up to twice the target
+constexpr int kLongSubChunk = 4096;  // sub-chunks this long may be split further (la_abi.hip, make_plan)
 
 // How a prefill is split: value-column slices x sequence chunks per (batch, head).
 struct Plan {

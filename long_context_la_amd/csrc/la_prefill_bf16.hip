@@ -810,8 +810,18 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     __shared__ __attribute__((aligned(16))) u16 sWh[2][BK * KS];
     __shared__ __attribute__((aligned(16))) u16 sWl[F16 ? 1 : 2][F16 ? 8 : BK * KS];
 
-    const int64_t group = blockIdx.x;
-    if (group >= a.groups) return;
+    if ((int64_t)blockIdx.x >= a.groups) return;
+    // Workgroup order (fixed-length batches): by a sub-chunk's position from its chunk's end
+    // first, then (sequence, head), then chunk.  The sub-chunks nearest their chunk's end are the
+    // ones that keep the most tiles once the decayed tokens are skipped, so they are dispatched
+    // first, ahead of the ones that finish at once; consecutive ids (which go round-robin over the
+    // XCDs) keep walking a head's chunks, as in the plain order.
+    int64_t group = blockIdx.x;
+    if (!a.ctab && a.span > 0) {
+        const int64_t ns = a.chunks_launched, per = a.span / a.chunk, nc = ns / per, bh = a.groups / ns;
+        const int64_t rank = group / (bh * nc), rem = group % (bh * nc);
+        group = (rem / nc) * ns + (rem % nc) * per + (per - 1 - rank);
+    }
     const Work wk = decode_work(a, group);
     if (wk.j == wk.nck - 1) return;  // a sequence's last (sub-)chunk needs no summary
     const int64_t t_begin = wk.t_begin, t_end = wk.t_end;

@@ -103,9 +103,9 @@ def test_decode_and_state_init_validation():
 
 def test_plan_and_workspace_sizes():
     # 64 heads x 131072 tokens: 64-column slices in two chunks (64 x 2 x 2 = 256 workgroups); the
-    # summaries of chunk 0 in 8 sub-chunks of 8192 tokens: 2 prefix + 1 + 8 summary slots per head
+    # summaries of chunk 0 in 16 sub-chunks of 4096 tokens: 2 prefix + 1 + 16 summary slots per head
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 64, 131072, 128) == 65536
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 64 * (2 + 1 + 8) * 128 * 128 * 4
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 64, 131072, 128) == 64 * (2 + 1 + 16) * 128 * 128 * 4
     # every default plan's chunk states fit the allocation-free entry point's array
     assert max(la.la_prefill_workspace_size(la.LA_BF16, 1, h, n, 128) for h in (1, 8, 26, 64)
                for n in (65536, 262144, 1 << 20, 1 << 22)) <= la.LA_NOALLOC_SCRATCH_BYTES
@@ -124,10 +124,10 @@ def test_plan_and_workspace_sizes():
     # summary pass has 8 x 30 = 240 >= 128 full-width workgroups; 32 columns: 8 + 1 + 7 x 4
     assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 32768, 128) == 8 * (16 + 1 + 15 * 2) * 128 * 128 * 4
     # 1M tokens: 16 chunks of 65536; their sub-chunks go finer (the summaries skip decayed tokens):
-    # 15 x 4 sub-chunks of 16384, 8 x 60 = 480 summary workgroups
+    # 15 x 8 sub-chunks of 8192, 8 x 120 = 960 summary workgroups
     c = la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 1048576, 128)
     assert c == 65536
-    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (16 + 1 + 15 * 4) * 128 * 128 * 4
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, 8, 1048576, 128) == 8 * (16 + 1 + 15 * 8) * 128 * 128 * 4
     # float32 keeps 32-column slices (4 per head at d = 128), and so does d = 64 (2 per head)
     assert la.la_prefill_chunk_tokens(la.LA_F32, 1, 8, 32768, 128) == 4096
     assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, 8, 32768, 64) == 2048

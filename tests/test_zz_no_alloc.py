@@ -107,7 +107,7 @@ def test_noalloc_through_the_binding(device):
 
 def test_noalloc_at_the_layer_shape(device):
     """The 64-head layer (1 x 64 x 131072, d = 128), whose plan fills most of the array (two chunks
-    of 64-column slices, eight summary sub-chunks: 44 MiB), against la_prefill with a caller
+    of 64-column slices, sixteen summary sub-chunks: 76 MiB), against la_prefill with a caller
     workspace bit for bit, then a smaller call through the same array; the oracle checks windows of
     the layer in tests/test_gpu_workloads.py."""
     import torch
