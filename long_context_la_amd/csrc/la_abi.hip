@@ -72,7 +72,7 @@ Plan make_plan(int64_t batch, int64_t heads, int64_t n, int64_t d, int64_t chunk
         while (local_groups * p.sub < target && p.chunk % (2 * p.sub * kBlock) == 0 &&
                p.chunk / (2 * p.sub) >= kMinSubChunk)
             p.sub *= 2;
-        // Long sub-chunks go finer, up to four times the target (two summary workgroups fit one CU)
+        // Long sub-chunks go finer, up to eight times the target (two summary workgroups fit one CU)
         // while the chunk states stay within the allocation-free entry point's array: the summary
         // kernel skips the tokens too far before their chunk's end to matter, so the pass takes as
         // long as the longest window a sub-chunk must still cover (measured on 8 heads x 1M tokens:
