@@ -326,7 +326,10 @@ la_status prefill_impl(la_dtype dt, const void* q, const void* k, const void* v,
                                             : launch_fwd_f32(b, (int)d, kModeLocal, st),
                           "chunk-summary launch");
         if (s != LA_OK) return s;
-        s = launch_status(launch_scan_sub(a.ws, b.ws, kv, slopes, bh, heads, p.n_chunks, p.sub, b.chunk, (int)d, st),
+        // the full-width forward summaries place their sub-chunks over each head's window
+        const int window = full_width && !a.rev && summary_windowed(b.chunk) ? (a.o && !a.wide ? 1 : 2) : 0;
+        s = launch_status(launch_scan_sub(a.ws, b.ws, kv, slopes, bh, heads, p.n_chunks, p.sub, b.chunk, window,
+                                          (int)d, st),
                           "prefix-combine launch");
         if (s != LA_OK) return s;
     }

@@ -176,9 +176,12 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
                        int64_t n_chunks, int64_t chunk, int d, hipStream_t stream);
 // Prefixes from sub-chunk summaries: pref[u][0] = kv[u]; pref[u][j] = the state after chunks
 // 0..j-1, folding sub[u][1 + (j-1)*n_sub_per + f] (sub-chunks of sub_len tokens) in order.
+// window 0: the sub-chunks split each chunk evenly; 1 (float16 summaries) or 2 (bf16): they sit
+// over each head's window before the chunk's end (summary_sub_len), as the summary kernel places
+// them, and the tokens before it only decay the incoming prefix.
 hipError_t launch_scan_sub(float* pref, const float* sub, const float* kv, const float* slopes, int64_t bh,
-                           int64_t heads, int64_t n_chunks, int64_t n_sub_per, int64_t sub_len, int d,
-                           hipStream_t stream);
+                           int64_t heads, int64_t n_chunks, int64_t n_sub_per, int64_t sub_len, int window,
+                           int d, hipStream_t stream);
 hipError_t launch_scan_varlen(float* ws, const float* kv, const float* slopes, const int64_t* stab,
                               int64_t n_seq, int64_t heads, int64_t chunk, int d, hipStream_t stream);
 hipError_t launch_state_init(float* kv, const float* kv0, int64_t count, hipStream_t stream);
@@ -229,6 +232,41 @@ __device__ inline float decay_pow(float nsl, float k)
 __device__ inline float neg_slope_log2e(const float* slopes, int64_t h)
 {
     return (float)(-(double)slopes[h] * 1.4426950408889634);
+}
+
+// Tokens before a chunk's end that can still reach its float32 state, for decay rate s: a token t
+// of a chunk ending at e enters the state with weight lambda^(e-1-t), and every element of a local
+// state is bounded by max|k v| / (1 - lambda) <= max|k v| (1 + 1/s), so the tokens before e - W with
+// s W >= ln(max|k v|) + 150 ln 2 + ln(1 + 1/s) change it by less than the smallest float32 denormal.
+// max|k v| < 65504^2 with float16 operands (f16: the range their prefill requires), else bf16's
+// largest value squared; ln 2 of margin each.  No decay (or a rate that is not a positive finite
+// number) returns a window longer than any sequence.
+__device__ inline double summary_window(float slope, bool f16)
+{
+    const double sl = (double)slope;
+    if (!(sl > 0.0 && sl < 1e30)) return 1e300;
+    const double c = f16 ? 2.0 * 11.09 + 151.0 * 0.6931471805599453 : 2.0 * 88.72 + 151.0 * 0.6931471805599453;
+    return (c + log1p(1.0 / sl)) / sl;
+}
+
+// Forward sub-chunks of at least kLongSubChunk tokens (even split) are placed over their head's
+// window; shorter ones split their chunk evenly (at 1024-token sub-chunks the window placement
+// measured 2-4% slower: the sub-chunks it fills had ended at once).
+__host__ __device__ inline bool summary_windowed(int64_t even_sub_len)
+{
+    return even_sub_len >= kLongSubChunk;
+}
+
+// Sub-chunk length when the `per` sub-chunks of a chunk of `span` tokens sit end to end over the
+// last tokens of the chunk only: the shortest tile multiple whose `per` copies cover the window,
+// and at most span / per (the even split, whenever the window spans the chunk).  The summary
+// kernel and the prefix combine both take it from here, so they place the sub-chunks alike.
+__device__ inline int64_t summary_sub_len(double win, int64_t span, int64_t per)
+{
+    const int64_t even = span / per;
+    const double tiles = ceil(win / (double)(per * kBlock));
+    if (!(tiles * kBlock < (double)even)) return even;
+    return (tiles >= 1.0 ? (int64_t)tiles : 1) * kBlock;
 }
 
 }  // namespace la

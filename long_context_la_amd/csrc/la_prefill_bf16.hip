@@ -824,26 +824,31 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     }
     const Work wk = decode_work(a, group);
     if (wk.j == wk.nck - 1) return;  // a sequence's last (sub-)chunk needs no summary
-    const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
+    // Tokens too far before their chunk's end to matter (summary_window: the tokens before e - W
+    // change a chunk ending at e by less than the smallest float32 denormal).  Forward summaries
+    // start their tiles at the first one that holds a token from e - W on, all of them with no
+    // decay; long fixed-length sub-chunks are moreover placed end to end over the window alone
+    // (summary_sub_len, as the prefix combine expects), so a head whose window is shorter than its
+    // chunk splits the window, not the chunk, over its workgroups.
+    int64_t t_begin = wk.t_begin, t_end = wk.t_end;
+    double win = 0.0;
+    int64_t e = 0;
+    if (!REV && a.span > 0) {
+        win = summary_window(a.slopes[wk.h], F16);
+        e = ((t_begin / a.span) + 1) * a.span;
+        const int64_t per = a.span / a.chunk;
+        if (!a.ctab && per > 1 && summary_windowed(a.chunk)) {
+            const int64_t len = summary_sub_len(win, a.span, per);
+            const int64_t i = (t_begin % a.span) / a.chunk;  // position within the chunk
+            t_begin = e - (per - i) * len;
+            t_end = t_begin + len;
+        }
+    }
     const int n_tiles = (int)((t_end - t_begin + BK - 1) / BK);
-    // Tokens too far before their chunk's end to matter.  A token t of a chunk ending at e enters
-    // the chunk's state with weight lambda^(e-1-t), and every element of a local state is bounded
-    // by M = max|k v| / (1 - lambda) <= max|k v| (1 + 1/s).  So the tokens before e - W with
-    // lambda^W M < 2^-150, i.e. s W >= ln(max|k v|) + 150 ln 2 + ln(1 + 1/s), change the chunk's
-    // state by less than the smallest float32 denormal, and a float32 result cannot depend on them:
-    // the sub-chunk starts its tiles at the first one that holds a token from e - W on (all of
-    // them with no decay).  max|k v| < 65504^2 with float16 operands (the range their prefill
-    // requires), else bf16's largest value squared; ln 2 of margin each.
     int tile0 = 0;
     if (!REV && a.span > 0) {
-        const double sl = (double)a.slopes[wk.h];
-        const double c = F16 ? 2.0 * 11.09 + 151.0 * 0.6931471805599453 : 2.0 * 88.72 + 151.0 * 0.6931471805599453;
-        if (sl > 0.0 && sl < 1e30) {
-            const double win = (c + log1p(1.0 / sl)) / sl;
-            const int64_t e = ((t_begin / a.span) + 1) * a.span;
-            const double first = (double)(e - t_begin) - win;  // tokens of the sub-chunk before e - W
-            if (first > 0.0) tile0 = first >= (double)n_tiles * BK ? n_tiles : (int)(first / BK);
-        }
+        const double first = (double)(e - t_begin) - win;  // tokens of the sub-chunk before e - W
+        if (first > 0.0) tile0 = first >= (double)n_tiles * BK ? n_tiles : (int)(first / BK);
     }
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

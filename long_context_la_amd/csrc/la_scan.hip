@@ -44,10 +44,11 @@ __global__ __launch_bounds__(256) void k_scan(float* __restrict__ ws, const floa
 // Chunk prefixes from sub-chunk summaries (the summary pass runs on sub-chunks to fill the GPU):
 // the recurrence P <- lambda^sub_len P + S runs over the sub-chunks in order and P is stored at
 // every chunk boundary.
+template <bool WIN>
 __global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, const float* __restrict__ sub,
                                                   const float* __restrict__ kv, const float* __restrict__ slopes,
                                                   int64_t bh, int64_t heads, int64_t n_chunks, int64_t n_sub_per,
-                                                  int64_t sub_len, int d2)
+                                                  int64_t sub_len, bool f16, int d2)
 {
     const int64_t per = d2 / 4;
     const int64_t n_sub = (n_chunks - 1) * n_sub_per;
@@ -55,7 +56,18 @@ __global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, cons
         const int64_t u = idx / per;
         const int64_t e = idx % per;
         const float nsl = neg_slope_log2e(slopes, u % heads);
-        const float ls = decay_pow(nsl, (float)sub_len);
+        // WIN: sub-chunks over the head's window, whose chunk's first `gap` tokens are in none of
+        // them; the prefix entering the chunk decays across those in two factors (each underflows
+        // only where the product is below float32's range anyway)
+        int64_t len = sub_len, gap = 0;
+        float g1 = 1.f, g2 = 1.f;
+        if constexpr (WIN) {
+            len = summary_sub_len(summary_window(slopes[u % heads], f16), n_sub_per * sub_len, n_sub_per);
+            gap = n_sub_per * (sub_len - len);
+            g1 = decay_pow(nsl, (float)(gap / 2));
+            g2 = decay_pow(nsl, (float)(gap - gap / 2));
+        }
+        const float ls = decay_pow(nsl, (float)len);
         const float4* S = reinterpret_cast<const float4*>(sub + u * (n_sub + 1) * (int64_t)d2) + e;
         float4* P = reinterpret_cast<float4*>(pref + u * n_chunks * (int64_t)d2) + e;
         float4 p = reinterpret_cast<const float4*>(kv + u * (int64_t)d2)[e];
@@ -74,6 +86,12 @@ __global__ __launch_bounds__(256) void k_scan_sub(float* __restrict__ pref, cons
 #pragma unroll
             for (int q = 0; q < kGroup; ++q) {
                 if (base + q < n_sub) {
+                    if (WIN && gap > 0 && f == 0) {
+                        p.x = p.x * g1 * g2;
+                        p.y = p.y * g1 * g2;
+                        p.z = p.z * g1 * g2;
+                        p.w = p.w * g1 * g2;
+                    }
                     p.x = ls * p.x + s[q].x;
                     p.y = ls * p.y + s[q].y;
                     p.z = ls * p.z + s[q].z;
@@ -191,14 +209,18 @@ hipError_t launch_scan(float* ws, const float* kv, const float* slopes, int64_t 
 }
 
 hipError_t launch_scan_sub(float* pref, const float* sub, const float* kv, const float* slopes, int64_t bh,
-                           int64_t heads, int64_t n_chunks, int64_t n_sub_per, int64_t sub_len, int d,
-                           hipStream_t stream)
+                           int64_t heads, int64_t n_chunks, int64_t n_sub_per, int64_t sub_len, int window,
+                           int d, hipStream_t stream)
 {
     const int d2 = d * d;
     const int64_t threads = bh * (d2 / 4);
     const dim3 grid = stride_grid(threads), block(256);
-    hipLaunchKernelGGL(k_scan_sub, grid, block, 0, stream, pref, sub, kv, slopes, bh, heads, n_chunks, n_sub_per,
-                       sub_len, d2);
+    if (window)
+        hipLaunchKernelGGL(k_scan_sub<true>, grid, block, 0, stream, pref, sub, kv, slopes, bh, heads, n_chunks,
+                           n_sub_per, sub_len, window == 1, d2);
+    else
+        hipLaunchKernelGGL(k_scan_sub<false>, grid, block, 0, stream, pref, sub, kv, slopes, bh, heads, n_chunks,
+                           n_sub_per, sub_len, false, d2);
     return hipGetLastError();
 }
 

@@ -166,18 +166,17 @@ def test_d64_chunked(device, H, N):
 
 # Chunk summaries skip the tokens whose weight at their chunk's end, times the largest state the
 # float16 input range allows, is below the smallest float32 denormal (fast-decaying heads skip most
-# of every chunk).  The results must not change; the second case puts large values only in the
-# skipped tokens and small ones after them.
+# of every chunk); sub-chunks of 4096 tokens or more sit end to end over each head's window before
+# its chunk's end, where the summary kernel and the prefix combine must agree.  The results must not
+# change; the boosted cases put large values in the first half of every 1024-token block (the
+# skipped tokens, for the fast heads) and small ones after them.
 
 
-@pytest.mark.parametrize("boost", [False, True])
-def test_summaries_skip_decayed_tokens(device, boost):
+def _skip_case(device, H, N, slopes, boost, seed, what):
     import torch
 
-    B, H, N, d = 1, 4, 40000, 128
-    slopes = np.array([0.5, 0.05, 2.0 ** -6, 2.0 ** -9], dtype=np.float32)
-    assert la.la_prefill_chunk_tokens(la.LA_BF16, B, H, N, d) < N
-    exact, raw = inputs(67, B, H, N, d, "bf16")
+    B, d = 1, 128
+    exact, raw = inputs(seed, B, H, N, d, "bf16")
     if boost:
         # the first half of each 1024-token block scaled by 8, the rest by 1/8 (exact in bf16, and
         # within the float16 products' range)
@@ -192,5 +191,26 @@ def test_summaries_skip_decayed_tokens(device, boost):
     la.la_prefill(q, k, v, torch.from_numpy(slopes).to(device), kv, o=o)
     torch.cuda.synchronize()
     o_ref, kv_ref, _ = oracle.recurrent(*exact, slopes)
-    assert_close(to_host(o), o_ref, "bf16", f"O skipped summaries (boost={boost})", stored="bf16")
-    assert_close(kv.cpu().numpy(), kv_ref, "bf16", f"KV skipped summaries (boost={boost})")
+    assert_close(to_host(o), o_ref, "bf16", f"O {what} (boost={boost})", stored="bf16")
+    assert_close(kv.cpu().numpy(), kv_ref, "bf16", f"KV {what} (boost={boost})")
+
+
+@pytest.mark.parametrize("boost", [False, True])
+def test_summaries_skip_decayed_tokens(device, boost):
+    # 1280-token chunks in two sub-chunks each, split evenly
+    H, N = 4, 40000
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, H, N, 128) < N
+    _skip_case(device, H, N, np.array([0.5, 0.05, 2.0 ** -6, 2.0 ** -9], dtype=np.float32), boost, 67,
+               "skipped summaries")
+
+
+@pytest.mark.parametrize("boost", [False, True])
+def test_summaries_over_decay_windows(device, boost):
+    # 8192-token chunks in two 4096-token sub-chunks: long enough that each head's two sub-chunks
+    # sit over its window before the chunk's end (for the 0.5 and 0.05 heads a few hundred and
+    # ~2600 tokens, for 2^-6 and 2^-9 the whole chunk), and the prefix combine places them alike
+    H, N = 16, 65536
+    assert la.la_prefill_chunk_tokens(la.LA_BF16, 1, H, N, 128) == 8192
+    assert la.la_prefill_workspace_size(la.LA_BF16, 1, H, N, 128) == H * (8 + 1 + 7 * 2) * 128 * 128 * 4
+    slopes = np.tile(np.array([0.5, 0.05, 2.0 ** -6, 2.0 ** -9], dtype=np.float32), 4)
+    _skip_case(device, H, N, slopes, boost, 68, "summaries over windows")
