@@ -118,7 +118,7 @@ def short_name(name):
     n = re.sub(r"^void ", "", n)
     n = n.replace("la::(anonymous namespace)::", "")
     n = re.sub(r"\(la::FwdArgs\)$", "", n)
-    n = re.sub(r"\((float|long|int|char|const|\*|,|\s)*\)$", "", n)
+    n = re.sub(r"\((float|long|int|char|bool|unsigned|const|\*|,|\s)*\)$", "", n)
     if n.startswith("at::native::") or n.startswith("void at::native::"):
         return "torch elementwise (bench set-up)"
     return n
