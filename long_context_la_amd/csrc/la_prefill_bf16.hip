@@ -811,16 +811,24 @@ __global__ __launch_bounds__(512, 1) void k_summary_bf16(FwdArgs a)
     __shared__ __attribute__((aligned(16))) u16 sWl[F16 ? 1 : 2][F16 ? 8 : BK * KS];
 
     if ((int64_t)blockIdx.x >= a.groups) return;
-    // Workgroup order (fixed-length batches): by a sub-chunk's position from its chunk's end
-    // first, then (sequence, head), then chunk.  The sub-chunks nearest their chunk's end are the
-    // ones that keep the most tiles once the decayed tokens are skipped, so they are dispatched
-    // first, ahead of the ones that finish at once; consecutive ids (which go round-robin over the
-    // XCDs) keep walking a head's chunks, as in the plain order.
+    // Workgroup order (fixed-length batches, evenly split sub-chunks): by a sub-chunk's position
+    // from its chunk's end first, then (sequence, head), then chunk.  The sub-chunks nearest their
+    // chunk's end are the ones that keep the most tiles once the decayed tokens are skipped, so
+    // they are dispatched first, ahead of the ones that finish at once; consecutive ids (which go
+    // round-robin over the XCDs) keep walking a head's chunks, as in the plain order.
     int64_t group = blockIdx.x;
     if (!a.ctab && a.span > 0) {
         const int64_t ns = a.chunks_launched, per = a.span / a.chunk, nc = ns / per, bh = a.groups / ns;
-        const int64_t rank = group / (bh * nc), rem = group % (bh * nc);
-        group = (rem / nc) * ns + (rem % nc) * per + (per - 1 - rank);
+        if (per > 1 && summary_windowed(a.chunk)) {
+            // sub-chunks over the decay windows: all of a head's sub-chunks keep the same number of
+            // tiles, which grows with the head's window; the model's decay rates fall with the head
+            // index, so the last (sequence, head) comes first and the longest windows start on
+            // CUs of their own
+            group = (bh - 1 - group / ns) * ns + group % ns;
+        } else {
+            const int64_t rank = group / (bh * nc), rem = group % (bh * nc);
+            group = (rem / nc) * ns + (rem % nc) * per + (per - 1 - rank);
+        }
     }
     const Work wk = decode_work(a, group);
     if (wk.j == wk.nck - 1) return;  // a sequence's last (sub-)chunk needs no summary
